@@ -1,0 +1,16 @@
+"""Block-quantized (GGUF Q4_0 / Q4_K / Q6_K, BF16, F16) matrix-vector product
+y = x @ W on AMD Instinct MI355X (gfx950), through a C-ABI library.
+
+The HIP library ``libqmv.so`` is loaded lazily on first use; there is no CPU
+fallback: if the library is missing, every compute call raises.
+"""
+from .synth import FORMAT_IDS, FORMAT_NAMES, F16, BF16, Q4_0, Q4_K, Q6_K  # noqa: F401
+
+
+def __getattr__(name):
+    # The binding is imported on first attribute access so that input
+    # generation works without the HIP library being present.
+    from . import binding
+    if hasattr(binding, name):
+        return getattr(binding, name)
+    raise AttributeError(name)

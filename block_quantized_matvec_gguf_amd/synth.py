@@ -1,0 +1,141 @@
+"""Seeded synthetic inputs for the block-quantized matvec.
+
+This module only draws random numbers and lays them out as stored blocks; it
+holds none of the product's arithmetic (no decoding, no dot products). Both the
+GPU path's tests/benchmark and the CPU oracle consume what it produces.
+
+Value distributions follow the five workloads the method is measured on:
+
+* Q4_0: per 32-weight block an f16 scale d ~ U[0.001, 0.02] and 16 uniform
+  random code bytes (so every 4-bit code is uniform on 0..15).
+* Q4_K: per 256-weight super-block f16 d ~ U[0.001, 0.02], f16 dmin ~
+  U[0, 0.01], 12 uniform random bytes of packed scales/mins (every packed
+  6-bit scale and min is then uniform on 0..63) and 128 uniform code bytes.
+* Q6_K: 128 uniform ql bytes, 64 uniform qh bytes, 16 signed 8-bit scales
+  uniform on -32..31 and f16 d ~ U[0.0005, 0.01].
+* F16 / BF16: weights ~ N(0, 0.02), rounded to nearest-even in the storage
+  type (f64 draw -> f32 -> storage type).
+* x: f32 ~ U[-1, 1].
+
+All generators take a numpy Generator; the named workloads use fixed seeds.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+F16, BF16, Q4_0, Q4_K, Q6_K = 1, 2, 3, 4, 5
+FORMAT_IDS = {"f16": F16, "bf16": BF16, "q4_0": Q4_0, "q4_k": Q4_K, "q6_k": Q6_K}
+FORMAT_NAMES = {v: k for k, v in FORMAT_IDS.items()}
+
+# weights per block, bytes per block (GGUF block sizes)
+BLOCK = {F16: (1, 2), BF16: (1, 2), Q4_0: (32, 18), Q4_K: (256, 144), Q6_K: (256, 210)}
+
+
+def fmt_id(fmt) -> int:
+    if isinstance(fmt, str):
+        return FORMAT_IDS[fmt.lower()]
+    return int(fmt)
+
+
+def row_bytes(fmt, k: int) -> int:
+    qk, bb = BLOCK[fmt_id(fmt)]
+    if k % qk:
+        raise ValueError("k=%d is not a multiple of the block size %d" % (k, qk))
+    return (k // qk) * bb
+
+
+def weight_bytes(fmt, k: int, n: int) -> int:
+    return row_bytes(fmt, k) * n
+
+
+def _f16_bytes(values: np.ndarray) -> np.ndarray:
+    """Little-endian f16 (round to nearest even) as a (..., 2) uint8 array."""
+    h = np.asarray(values, dtype=np.float64).astype("<f2")
+    return h.view(np.uint8).reshape(h.shape + (2,))
+
+
+def bf16_bits(values: np.ndarray) -> np.ndarray:
+    """Round f32 values to bfloat16 (nearest, ties to even) and return the
+    16-bit patterns. Inputs must be finite."""
+    f = np.ascontiguousarray(values, dtype=np.float32)
+    u = f.view(np.uint32).astype(np.uint64)
+    rounded = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    return rounded.astype(np.uint16)
+
+
+def gen_x(rng: np.random.Generator, m: int, k: int) -> np.ndarray:
+    return rng.uniform(-1.0, 1.0, size=(m, k)).astype(np.float32)
+
+
+def gen_f16(rng, n, k, std=0.02) -> np.ndarray:
+    w = rng.normal(0.0, std, size=(n, k)).astype(np.float32)
+    return np.ascontiguousarray(w.astype("<f2")).view(np.uint8).reshape(-1)
+
+
+def gen_bf16(rng, n, k, std=0.02) -> np.ndarray:
+    w = rng.normal(0.0, std, size=(n, k)).astype(np.float32)
+    return bf16_bits(w).astype("<u2").view(np.uint8).reshape(-1)
+
+
+def gen_q4_0(rng, n, k, d_range=(0.001, 0.02)) -> np.ndarray:
+    nb = n * (k // 32)
+    if k % 32:
+        raise ValueError("Q4_0 needs k % 32 == 0")
+    blk = np.empty((nb, 18), dtype=np.uint8)
+    blk[:, 0:2] = _f16_bytes(rng.uniform(d_range[0], d_range[1], size=nb))
+    blk[:, 2:18] = rng.integers(0, 256, size=(nb, 16), dtype=np.uint8)
+    return blk.reshape(-1)
+
+
+def gen_q4_k(rng, n, k, d_range=(0.001, 0.02), dmin_range=(0.0, 0.01)) -> np.ndarray:
+    if k % 256:
+        raise ValueError("Q4_K needs k % 256 == 0")
+    nb = n * (k // 256)
+    blk = np.empty((nb, 144), dtype=np.uint8)
+    blk[:, 0:2] = _f16_bytes(rng.uniform(d_range[0], d_range[1], size=nb))
+    blk[:, 2:4] = _f16_bytes(rng.uniform(dmin_range[0], dmin_range[1], size=nb))
+    blk[:, 4:144] = rng.integers(0, 256, size=(nb, 140), dtype=np.uint8)
+    return blk.reshape(-1)
+
+
+def gen_q6_k(rng, n, k, d_range=(0.0005, 0.01)) -> np.ndarray:
+    if k % 256:
+        raise ValueError("Q6_K needs k % 256 == 0")
+    nb = n * (k // 256)
+    blk = np.empty((nb, 210), dtype=np.uint8)
+    blk[:, 0:192] = rng.integers(0, 256, size=(nb, 192), dtype=np.uint8)
+    blk[:, 192:208] = rng.integers(-32, 32, size=(nb, 16), dtype=np.int8).view(np.uint8)
+    blk[:, 208:210] = _f16_bytes(rng.uniform(d_range[0], d_range[1], size=nb))
+    return blk.reshape(-1)
+
+
+def gen_weights(fmt, rng, n, k) -> np.ndarray:
+    f = fmt_id(fmt)
+    return {F16: gen_f16, BF16: gen_bf16, Q4_0: gen_q4_0, Q4_K: gen_q4_k,
+            Q6_K: gen_q6_k}[f](rng, n, k)
+
+
+# The measured workloads. Seeds: W stream 0x51A70000 + id, x stream 0x51A71000 + id.
+WORKLOADS = {
+    "q4_0_small": dict(id=1, fmt="q4_0", k=256, n=512, m=1),
+    "bf16_ffn_up": dict(id=2, fmt="bf16", k=2560, n=10240, m=1),
+    "f16_ffn_up": dict(id=2, fmt="f16", k=2560, n=10240, m=1),
+    "q4_k_ffn_up": dict(id=3, fmt="q4_k", k=2560, n=10240, m=1),
+    "q6_k_vocab_outproj": dict(id=4, fmt="q6_k", k=2560, n=262144, m=1, tiles=8),
+    "q4_k_prefill": dict(id=5, fmt="q4_k", k=4096, n=14336, m=64),
+}
+
+
+def workload(name: str, n: int | None = None):
+    """(fmt_id, W bytes, x (m,k) f32, spec) for a named workload. n may cap
+    the row count (the first n rows of the full matrix are then generated by
+    the same draws only when n is the full size; a capped n is its own draw)."""
+    spec = dict(WORKLOADS[name])
+    if n is not None:
+        spec["n"] = n
+    f = fmt_id(spec["fmt"])
+    rw = np.random.default_rng(0x51A70000 + spec["id"] + (0 if n is None else 7919 * n))
+    rx = np.random.default_rng(0x51A71000 + spec["id"])
+    W = gen_weights(f, rw, spec["n"], spec["k"])
+    x = gen_x(rx, spec["m"], spec["k"])
+    return f, W, x, spec

@@ -1,0 +1,434 @@
+"""Pins of the CPU oracle to things other than itself.
+
+Each ``pin_*`` function raises AssertionError when the oracle disagrees with
+what the pages or the mathematics fix: library conversions of every f16/bf16
+bit pattern, hand-built blocks from ``tests/golden/`` (values derived by hand),
+invariants (blocks that must decode to zero, scales that must silence exactly
+their own elements), packer/unpacker round trips (the packers here are written
+from the layout description, independently of the oracle's decoders), one-hot
+brute force, exact small-integer products, and a factored per-block evaluation
+of the same sums written with numpy.
+
+The functions are plain so that ``test_oracle_mutants.py`` can run all of them
+against deliberately broken copies of the oracle and show that each plausible
+mistake is caught.
+"""
+from __future__ import annotations
+
+import os
+import sys
+from fractions import Fraction
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import oracle  # noqa: E402
+from block_quantized_matvec_gguf_amd import synth  # noqa: E402
+
+from conftest import read_golden  # noqa: E402
+
+F16, BF16, Q4_0, Q4_K, Q6_K = oracle.F16, oracle.BF16, oracle.Q4_0, oracle.Q4_K, oracle.Q6_K
+
+
+# ------------------------------------------------------------ test packers
+# Written from the layout description (value -> bytes), the inverse direction
+# of the oracle's decoders.
+
+def f16_le(v: float) -> list:
+    return list(np.array([v], dtype="<f2").view(np.uint8))
+
+
+def pack_q4_0(codes, d: float) -> np.ndarray:
+    """codes: 32 ints 0..15 in element order."""
+    codes = list(codes)
+    out = f16_le(d)
+    for b in range(16):
+        out.append(codes[b] | (codes[16 + b] << 4))
+    return np.array(out, dtype=np.uint8)
+
+
+def pack_q4_k_scales(scales, mins) -> list:
+    out = [0] * 12
+    for j in range(4):
+        out[j] = scales[j] | ((scales[j + 4] >> 4) << 6)
+        out[j + 4] = mins[j] | ((mins[j + 4] >> 4) << 6)
+        out[j + 8] = (scales[j + 4] & 15) | ((mins[j + 4] & 15) << 4)
+    return out
+
+
+def pack_q4_k(codes, scales, mins, d: float, dmin: float) -> np.ndarray:
+    """codes: 256 ints 0..15 in element order."""
+    out = f16_le(d) + f16_le(dmin) + pack_q4_k_scales(scales, mins)
+    qs = [0] * 128
+    for chunk in range(4):
+        for l in range(32):
+            qs[32 * chunk + l] = codes[64 * chunk + l] | (codes[64 * chunk + 32 + l] << 4)
+    return np.array(out + qs, dtype=np.uint8)
+
+
+def q6_k_position(e: int):
+    """(half, quarter, lane) of element e of a Q6_K super-block."""
+    return e // 128, (e % 128) // 32, e % 32
+
+
+def q6_k_scale_slot(e: int) -> int:
+    h, g, l = q6_k_position(e)
+    return 8 * h + 2 * g + l // 16
+
+
+def pack_q6_k(codes, scales, d: float) -> np.ndarray:
+    """codes: 256 ints 0..63 in element order; scales: 16 ints -128..127."""
+    ql = [0] * 128
+    qh = [0] * 64
+    for e in range(256):
+        h, g, l = q6_k_position(e)
+        lo, hi = codes[e] & 15, codes[e] >> 4
+        p = 64 * h + 32 * (g % 2) + l
+        ql[p] |= lo << (4 * (g // 2))
+        qh[32 * h + l] |= hi << (2 * g)
+    sc = [s & 0xFF for s in scales]
+    return np.array(ql + qh + sc + f16_le(d), dtype=np.uint8)
+
+
+def hexbytes(s: str) -> np.ndarray:
+    return np.array([int(t, 16) for t in s.split()], dtype=np.uint8)
+
+
+# --------------------------------------------------------------- the pins
+
+def pin_f16_every_pattern():
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ref = bits.view(np.float16).astype(np.float64)
+    got = np.array([oracle.f16_to_f32(int(b)) for b in bits], dtype=np.float64)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan), "f16 NaN patterns differ"
+    assert np.array_equal(got[~nan], ref[~nan]), "f16 decode differs from numpy float16"
+
+
+def pin_bf16_every_pattern():
+    import torch
+    bits = np.arange(65536, dtype=np.int64)
+    ref = torch.tensor(bits.astype(np.uint16).view(np.int16)).view(torch.bfloat16) \
+        .to(torch.float64).numpy()
+    got = np.array([oracle.bf16_to_f32(int(b)) for b in bits], dtype=np.float64)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan]), "bf16 decode differs from torch bfloat16"
+
+
+def pin_q4_0_golden():
+    g = read_golden("q4_0_hand_block.txt")
+    for b, v in zip(g["bytes"], g["values"]):
+        blk = hexbytes(b)
+        want = np.array([float(t) for t in v.split()], dtype=np.float64)
+        got = oracle.dequant_row(Q4_0, blk, 32).astype(np.float64)
+        assert np.array_equal(got, want), (got, want)
+    # the packer reproduces the hand-built bytes
+    codes = [l for l in range(16)] + [15 - l for l in range(16)]
+    assert np.array_equal(pack_q4_0(codes, 1.0), hexbytes(g["bytes"][0]))
+
+
+def pin_q4_0_zero_blocks():
+    rng = np.random.default_rng(11)
+    # every code 8 -> all zero whatever d is
+    for d in (0.0123, -3.5, 65504.0):
+        blk = pack_q4_0([8] * 32, d)
+        assert not np.any(oracle.dequant_row(Q4_0, blk, 32))
+    # d = 0 -> all zero whatever the codes are
+    blk = pack_q4_0(list(rng.integers(0, 16, 32)), 0.0)
+    assert not np.any(oracle.dequant_row(Q4_0, blk, 32))
+
+
+def pin_q4_0_roundtrip():
+    rng = np.random.default_rng(12)
+    for _ in range(50):
+        codes = [int(c) for c in rng.integers(0, 16, 32)]
+        d = float(np.float16(rng.uniform(-0.1, 0.1)))
+        got = oracle.dequant_row(Q4_0, pack_q4_0(codes, d), 32)
+        want = np.float32(d) * (np.array(codes, dtype=np.float32) - np.float32(8))
+        assert np.array_equal(got, want)
+
+
+def pin_q4_k_golden_scales():
+    g = read_golden("q4_k_hand_scales.txt")
+    scales = [int(t) for t in g["scales"][0].split()]
+    mins = [int(t) for t in g["mins"][0].split()]
+    packed = hexbytes(g["bytes"][0])
+    assert list(packed) == pack_q4_k_scales(scales, mins), "test packer vs hand bytes"
+    # d=1, dmin=0, every code 1: element of sub-block s decodes to scale_s.
+    blk = np.concatenate([np.array(f16_le(1.0) + f16_le(0.0), np.uint8), packed,
+                          np.full(128, 0x11, np.uint8)])
+    w = oracle.dequant_row(Q4_K, blk, 256)
+    for e in range(256):
+        s = 2 * (e // 64) + (e % 64) // 32
+        assert w[e] == scales[s], (e, w[e], scales[s])
+    # d=0, dmin=1: element of sub-block s decodes to -min_s.
+    blk[0:4] = f16_le(0.0) + f16_le(1.0)
+    w = oracle.dequant_row(Q4_K, blk, 256)
+    for e in range(256):
+        s = 2 * (e // 64) + (e % 64) // 32
+        assert w[e] == -mins[s], (e, w[e], mins[s])
+
+
+def pin_q4_k_scale_roundtrip():
+    """Every (scale, min) pair in every slot survives pack -> oracle decode.
+    Codes are all 1, d = 1, dmin = 1/64, so element value = scale - min/64,
+    which identifies the pair uniquely."""
+    rng = np.random.default_rng(13)
+    pairs = [(a, b) for a in range(64) for b in range(64)]
+    blocks = []
+    expect = []
+    for slot in range(8):
+        for a, b in pairs[slot::8] + pairs[(slot + 3) % 8::8]:
+            sc = [int(v) for v in rng.integers(0, 64, 8)]
+            mn = [int(v) for v in rng.integers(0, 64, 8)]
+            sc[slot], mn[slot] = a, b
+            blocks.append(pack_q4_k([1] * 256, sc, mn, 1.0, 1.0 / 64))
+            expect.append((sc, mn))
+    W = np.concatenate(blocks)
+    w = oracle.dequant(Q4_K, W, 256, len(blocks))
+    for r, (sc, mn) in enumerate(expect):
+        for s in range(8):
+            e0 = 64 * (s // 2) + 32 * (s % 2)
+            want = np.float32(sc[s]) - np.float32(mn[s]) / np.float32(64)
+            assert np.all(w[r, e0:e0 + 32] == want), (r, s)
+
+
+def pin_q4_k_element_ownership():
+    """Only sub-block s has a non-zero scale: exactly its 32 elements are
+    non-zero and they carry their own codes."""
+    rng = np.random.default_rng(14)
+    codes = [int(c) for c in rng.integers(1, 16, 256)]
+    for s in range(8):
+        sc = [0] * 8
+        sc[s] = 1
+        w = oracle.dequant_row(Q4_K, pack_q4_k(codes, sc, [0] * 8, 1.0, 0.0), 256)
+        owned = [e for e in range(256) if 2 * (e // 64) + (e % 64) // 32 == s]
+        assert set(np.nonzero(w)[0].tolist()) == set(owned), s
+        for e in owned:
+            assert w[e] == codes[e]
+
+
+def pin_q4_k_zero_blocks():
+    rng = np.random.default_rng(15)
+    codes = [int(c) for c in rng.integers(0, 16, 256)]
+    sc = [int(c) for c in rng.integers(0, 64, 8)]
+    mn = [int(c) for c in rng.integers(0, 64, 8)]
+    assert not np.any(oracle.dequant_row(Q4_K, pack_q4_k(codes, sc, mn, 0.0, 0.0), 256))
+    assert not np.any(oracle.dequant_row(Q4_K, pack_q4_k(codes, [0] * 8, [0] * 8, 0.7, 0.3), 256))
+    assert not np.any(oracle.dequant_row(Q4_K, pack_q4_k([0] * 256, sc, [0] * 8, 0.7, 0.3), 256))
+
+
+def pin_q6_k_golden():
+    g = read_golden("q6_k_hand_block.txt")
+    ql = [(p % 16) * 0x11 for p in range(128)]
+    qh = [0x88 if p % 32 < 16 else 0xDD for p in range(64)]
+    sc = list(hexbytes(g["scales"][0]))
+    d = list(hexbytes(g["d"][0]))
+    blk = np.array(ql + qh + sc + d, dtype=np.uint8)
+    w = oracle.dequant_row(Q6_K, blk, 256)
+    for item in g["spot"][0].split():
+        e, v = item.split(":")
+        assert w[int(e)] == float(v), (e, w[int(e)], v)
+    for e in range(256):
+        assert w[e] == (q6_k_scale_slot(e) - 8) * (e % 64 - 32), e
+    # the test packer reproduces the hand-built bytes
+    assert np.array_equal(pack_q6_k([e % 64 for e in range(256)], [s - 8 for s in range(16)],
+                                    1.0), blk)
+
+
+def pin_q6_k_zero_blocks():
+    rng = np.random.default_rng(16)
+    sc = [int(v) for v in rng.integers(-32, 32, 16)]
+    assert not np.any(oracle.dequant_row(Q6_K, pack_q6_k([32] * 256, sc, 0.01), 256))
+    codes = [int(v) for v in rng.integers(0, 64, 256)]
+    assert not np.any(oracle.dequant_row(Q6_K, pack_q6_k(codes, sc, 0.0), 256))
+
+
+def pin_q6_k_scale_ownership():
+    """Zeroing scale slot s zeroes exactly its 16 elements."""
+    rng = np.random.default_rng(17)
+    codes = [int(v) for v in rng.integers(0, 64, 256)]
+    codes = [c if c != 32 else 33 for c in codes]  # no code that is zero anyway
+    for s in range(16):
+        sc = [int(v) for v in rng.integers(1, 32, 16)]
+        sc[s] = 0
+        w = oracle.dequant_row(Q6_K, pack_q6_k(codes, sc, 0.25), 256)
+        zeros = set(np.nonzero(w == 0)[0].tolist())
+        assert zeros == {e for e in range(256) if q6_k_scale_slot(e) == s}, s
+
+
+def pin_q6_k_roundtrip():
+    rng = np.random.default_rng(18)
+    for _ in range(40):
+        codes = [int(v) for v in rng.integers(0, 64, 256)]
+        sc = [int(v) for v in rng.integers(-128, 128, 16)]
+        d = float(np.float16(rng.uniform(-0.02, 0.02)))
+        w = oracle.dequant_row(Q6_K, pack_q6_k(codes, sc, d), 256)
+        for e in range(256):
+            want = (np.float32(d) * np.float32(sc[q6_k_scale_slot(e)])) * np.float32(codes[e] - 32)
+            assert w[e] == want, e
+
+
+def _random_matrix(fmt, n, k, seed):
+    rng = np.random.default_rng(seed)
+    return synth.gen_weights(fmt, rng, n, k)
+
+
+def pin_onehot_bruteforce():
+    """x = e_i picks column i: y_j must equal the decoded weight w_j[i]."""
+    for fmt, k in ((Q4_0, 32), (Q4_0, 64), (Q4_K, 256), (Q6_K, 256), (F16, 24), (BF16, 24)):
+        n = 6
+        W = _random_matrix(fmt, n, k, 100 + fmt)
+        dense = oracle.dequant(fmt, W, k, n)
+        X = np.eye(k, dtype=np.float32)
+        y, s = oracle.gemv(fmt, W, X, k, n)
+        assert np.array_equal(y, dense.T.astype(np.float64)), fmt
+        assert np.array_equal(s, np.abs(dense.T.astype(np.float64))), fmt
+
+
+def pin_dense_route_matches_gemv():
+    """Decode everything, then a library f64 matmul: same sums as the oracle's
+    gemv to f64 rounding."""
+    for fmt, k, n in ((Q4_0, 128, 16), (Q4_K, 512, 9), (Q6_K, 512, 7), (F16, 40, 5),
+                      (BF16, 64, 11)):
+        W = _random_matrix(fmt, n, k, 200 + fmt)
+        x = synth.gen_x(np.random.default_rng(300 + fmt), 3, k)
+        dense = oracle.dequant(fmt, W, k, n).astype(np.float64)
+        want = x.astype(np.float64) @ dense.T
+        y, s = oracle.gemv(fmt, W, x, k, n)
+        assert np.all(np.abs(y - want) <= 1e-12 * s + 1e-300), fmt
+
+
+def _factored_q4_0(W, x, k, n):
+    blk = W.reshape(n, k // 32, 18)
+    d = blk[:, :, 0:2].copy().view("<f2")[..., 0].astype(np.float64)
+    qs = blk[:, :, 2:18].astype(np.int64)
+    codes = np.concatenate([qs & 15, qs >> 4], axis=2) - 8  # (n, nb, 32)
+    xb = x.astype(np.float64).reshape(-1, k // 32, 32)
+    return np.einsum("jb,tbe,jbe->tj", d, xb, codes.astype(np.float64))
+
+
+def _factored_q4_k(W, x, k, n):
+    nb = k // 256
+    blk = W.reshape(n, nb, 144)
+    d = blk[:, :, 0:2].copy().view("<f2")[..., 0].astype(np.float64)
+    dmin = blk[:, :, 2:4].copy().view("<f2")[..., 0].astype(np.float64)
+    sc = blk[:, :, 4:16].astype(np.int64)
+    lo6 = sc & 63
+    scale = np.concatenate([lo6[..., 0:4], (sc[..., 8:12] & 15) | ((sc[..., 0:4] >> 6) << 4)], -1)
+    mins = np.concatenate([lo6[..., 4:8], (sc[..., 8:12] >> 4) | ((sc[..., 4:8] >> 6) << 4)], -1)
+    qs = blk[:, :, 16:144].astype(np.int64).reshape(n, nb, 4, 32)
+    codes = np.stack([qs & 15, qs >> 4], axis=3).reshape(n, nb, 8, 32)  # sub-block major
+    xb = x.astype(np.float64).reshape(-1, nb, 8, 32)
+    qx = np.einsum("tbse,jbse->tjbs", xb, codes.astype(np.float64))
+    sx = xb.sum(-1)  # (t, nb, 8)
+    return (np.einsum("jb,jbs,tjbs->tj", d, scale.astype(np.float64), qx)
+            - np.einsum("jb,jbs,tbs->tj", dmin, mins.astype(np.float64), sx))
+
+
+def _factored_q6_k(W, x, k, n):
+    nb = k // 256
+    blk = W.reshape(n, nb, 210)
+    ql = blk[:, :, 0:128].astype(np.int64).reshape(n, nb, 2, 2, 32)   # h, g%2, l
+    qh = blk[:, :, 128:192].astype(np.int64).reshape(n, nb, 2, 32)    # h, l
+    sc = blk[:, :, 192:208].view(np.int8).astype(np.float64).reshape(n, nb, 2, 4, 2)  # h, g, l//16
+    d = blk[:, :, 208:210].copy().view("<f2")[..., 0].astype(np.float64)
+    lo = np.stack([ql[:, :, :, 0] & 15, ql[:, :, :, 1] & 15, ql[:, :, :, 0] >> 4,
+                   ql[:, :, :, 1] >> 4], axis=3)                      # n, nb, h, g, l
+    hi = np.stack([(qh >> (2 * g)) & 3 for g in range(4)], axis=3)
+    codes = (lo | (hi << 4)) - 32
+    xb = x.astype(np.float64).reshape(-1, nb, 2, 4, 2, 16)            # t, b, h, g, l//16, l%16
+    cq = codes.reshape(n, nb, 2, 4, 2, 16).astype(np.float64)
+    part = np.einsum("tbhgce,jbhgce->tjbhgc", xb, cq)
+    return np.einsum("jb,jbhgc,tjbhgc->tj", d, sc, part)
+
+
+def pin_factored_route_matches_gemv():
+    """Per-block factored sums (scale * sum(q*x) - min * sum(x)) in f64 agree
+    with the oracle's decode-then-sum to within the f32 rounding of the decoded
+    weights."""
+    for fmt, k, n, fn in ((Q4_0, 256, 13, _factored_q4_0), (Q4_K, 768, 7, _factored_q4_k),
+                          (Q6_K, 512, 9, _factored_q6_k)):
+        W = _random_matrix(fmt, n, k, 400 + fmt)
+        x = synth.gen_x(np.random.default_rng(500 + fmt), 2, k)
+        want = fn(W, x, k, n)
+        y, s = oracle.gemv(fmt, W, x, k, n)
+        assert np.all(np.abs(y - want) <= 2.0 ** -22 * s + 1e-300), fmt
+
+
+def pin_exact_small_integers():
+    """Small-integer f16/bf16 weights and dyadic x: every partial sum is exact,
+    so the result equals the rational sum exactly."""
+    rng = np.random.default_rng(19)
+    k, n = 48, 5
+    wi = rng.integers(-9, 10, size=(n, k))
+    xi = rng.integers(-8, 9, size=(2, k))
+    x = (xi / 8.0).astype(np.float32)
+    for fmt in (F16, BF16):
+        if fmt == F16:
+            W = wi.astype("<f2").view(np.uint8).reshape(-1)
+        else:
+            W = synth.bf16_bits(wi.astype(np.float32)).astype("<u2").view(np.uint8).reshape(-1)
+        y, _ = oracle.gemv(fmt, W, x, k, n)
+        for t in range(2):
+            for j in range(n):
+                want = sum(Fraction(int(wi[j, i])) * Fraction(int(xi[t, i]), 8) for i in range(k))
+                assert Fraction(y[t, j]) == want, (fmt, t, j)
+
+
+def pin_identity_f16():
+    """The pages' identity check (matmul.rs, test f16_matmul_3x4_eye): W = I
+    (n = k = 4), x = (i+1)/4, y = x."""
+    k = n = 4
+    W = np.eye(n, k).astype("<f2").view(np.uint8).reshape(-1)
+    x = ((np.arange(k) + 1) * 0.25).astype(np.float32)
+    y, _ = oracle.gemv(F16, W, x, k, n)
+    assert np.array_equal(y[0], x.astype(np.float64))
+
+
+def pin_linearity():
+    rng = np.random.default_rng(20)
+    for fmt, k, n in ((Q4_K, 256, 6), (Q6_K, 256, 6), (Q4_0, 64, 6)):
+        W = _random_matrix(fmt, n, k, 600 + fmt)
+        # dyadic x so that 2*x1 + x2 is exact in f32
+        x1 = (rng.integers(-64, 65, size=(1, k)) / 64.0).astype(np.float32)
+        x2 = (rng.integers(-64, 65, size=(1, k)) / 64.0).astype(np.float32)
+        y1, s1 = oracle.gemv(fmt, W, x1, k, n)
+        y2, s2 = oracle.gemv(fmt, W, x2, k, n)
+        y3, _ = oracle.gemv(fmt, W, 2 * x1 + x2, k, n)
+        assert np.all(np.abs(y3 - (2 * y1 + y2)) <= 1e-12 * (2 * s1 + s2) + 1e-300)
+
+
+def pin_ranges_and_threads():
+    """Row ranges, row lists, tiling and thread count give identical bits."""
+    fmt, k, n = Q6_K, 512, 37
+    W = _random_matrix(fmt, n, k, 700)
+    x = synth.gen_x(np.random.default_rng(701), 2, k)
+    y_all, s_all = oracle.gemv(fmt, W, x, k, n, threads=1)
+    y_mt, _ = oracle.gemv(fmt, W, x, k, n, threads=8)
+    assert np.array_equal(y_all, y_mt)
+    tiles = [oracle.gemv(fmt, W, x, k, n, a, b)[0] for a, b in ((0, 5), (5, 6), (6, 30), (30, 37))]
+    assert np.array_equal(np.concatenate(tiles, axis=1), y_all)
+    rows = [36, 0, 17, 17]
+    y_r, s_r = oracle.gemv_rows(fmt, W, x, k, n, rows)
+    assert np.array_equal(y_r, y_all[:, rows]) and np.array_equal(s_r, s_all[:, rows])
+
+
+def pin_pages_q4_0_case():
+    """The pages' Q4_0 parity case shape (matmul.rs, test
+    q4_0_matmul_gpu_vs_cpu_oracle: k=128, n=16, d in [-0.1, 0.1), random code
+    bytes, x in [-0.5, 0.5)) against the factored evaluation, with that test's
+    own bar max_abs < 1e-4."""
+    rng = np.random.default_rng(21)
+    k, n = 128, 16
+    W = synth.gen_q4_0(rng, n, k, d_range=(-0.1, 0.1))
+    x = (rng.uniform(-0.5, 0.5, size=(1, k))).astype(np.float32)
+    y, _ = oracle.gemv(Q4_0, W, x, k, n)
+    assert np.max(np.abs(y - _factored_q4_0(W, x, k, n))) < 1e-4
+
+
+ALL_PINS = [v for name, v in sorted(globals().items()) if name.startswith("pin_")]
