@@ -1,0 +1,265 @@
+// C ABI of the block-quantized matvec library (declared in include/qmv.h):
+// argument validation (rullama 0.5.0, src/backend/matmul.rs, the checks at the
+// top of each matmul_* function: block-multiple k, even k for the 16-bit
+// formats, the expected weight byte count), kernel selection and launch on the
+// caller's stream. Nothing here synchronises or allocates device memory.
+#include "qmv.h"
+#include "qmv_internal.h"
+
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+namespace {
+
+struct DevInfo {
+    bool gfx950;
+    int num_cu;
+};
+
+std::mutex g_mu;
+std::atomic<int> g_refs{0};
+std::vector<DevInfo> g_dev;
+thread_local std::string t_err;
+
+int fail(int code, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    t_err = buf;
+    return code;
+}
+
+int64_t block_elems(int fmt) {
+    switch (fmt) {
+    case QMV_FMT_F16:
+    case QMV_FMT_BF16: return 2; // the pages require even k for 16-bit weights
+    case QMV_FMT_Q4_0: return 32;
+    case QMV_FMT_Q4_K:
+    case QMV_FMT_Q6_K: return 256;
+    default: return -1;
+    }
+}
+
+int64_t row_bytes_of(int fmt, int64_t k) {
+    switch (fmt) {
+    case QMV_FMT_F16:
+    case QMV_FMT_BF16: return 2 * k;
+    case QMV_FMT_Q4_0: return (k / 32) * 18;
+    case QMV_FMT_Q4_K: return (k / 256) * 144;
+    case QMV_FMT_Q6_K: return (k / 256) * 210;
+    default: return -1;
+    }
+}
+
+const char *fmt_name(int fmt) {
+    switch (fmt) {
+    case QMV_FMT_F16: return "f16";
+    case QMV_FMT_BF16: return "bf16";
+    case QMV_FMT_Q4_0: return "q4_0";
+    case QMV_FMT_Q4_K: return "q4_k";
+    case QMV_FMT_Q6_K: return "q6_k";
+    default: return "?";
+    }
+}
+
+// Which kernel family a request resolves to; -1 when the explicit choice
+// cannot serve the shape.
+int resolve_algo(int fmt, int64_t k, int64_t m, int algo) {
+    const bool mfma_ok = qmv::plan_mfma(fmt, k, 1, m, 256, nullptr);
+    qmv::GemvPlan gp;
+    const bool gemv_ok = qmv::plan_gemv(fmt, k, 1, 2, 256, &gp);
+    switch (algo) {
+    case QMV_ALGO_AUTO:
+        if (m >= 16 && mfma_ok) return QMV_ALGO_MFMA;
+        return gemv_ok ? QMV_ALGO_GEMV : QMV_ALGO_SIMPLE;
+    case QMV_ALGO_GEMV: return gemv_ok ? QMV_ALGO_GEMV : -1;
+    case QMV_ALGO_MFMA: return mfma_ok ? QMV_ALGO_MFMA : -1;
+    case QMV_ALGO_SIMPLE: return QMV_ALGO_SIMPLE;
+    default: return -1;
+    }
+}
+
+} // namespace
+
+extern "C" {
+
+int qmv_create(void) {
+    std::lock_guard<std::mutex> lk(g_mu);
+    t_err.clear();
+    if (g_refs.load() > 0) {
+        g_refs++;
+        return QMV_OK;
+    }
+    int count = 0;
+    hipError_t e = hipGetDeviceCount(&count);
+    if (e != hipSuccess || count <= 0) {
+        (void)hipGetLastError();
+        return fail(QMV_ERR_NO_DEVICE, "qmv_create: no HIP device (%s)",
+                    e != hipSuccess ? hipGetErrorString(e) : "count is 0");
+    }
+    std::vector<DevInfo> devs((size_t)count);
+    bool any = false;
+    for (int d = 0; d < count; d++) {
+        hipDeviceProp_t prop;
+        e = hipGetDeviceProperties(&prop, d);
+        if (e != hipSuccess)
+            return fail(QMV_ERR_HIP, "qmv_create: hipGetDeviceProperties(%d): %s", d,
+                        hipGetErrorString(e));
+        devs[d].gfx950 = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+        devs[d].num_cu = prop.multiProcessorCount > 0 ? prop.multiProcessorCount : 1;
+        any = any || devs[d].gfx950;
+    }
+    if (!any) return fail(QMV_ERR_UNSUPPORTED_ARCH, "qmv_create: no gfx950 device visible");
+    g_dev = devs;
+    g_refs = 1;
+    return QMV_OK;
+}
+
+void qmv_destroy(void) {
+    std::lock_guard<std::mutex> lk(g_mu);
+    if (g_refs.load() <= 0) return;
+    if (--g_refs == 0) g_dev.clear();
+}
+
+int64_t qmv_weight_bytes(int format, int64_t k, int64_t n) {
+    const int64_t qk = block_elems(format);
+    if (qk <= 0 || k < 0 || n < 0 || k % qk != 0) return -1;
+    return row_bytes_of(format, k) * n;
+}
+
+const char *qmv_last_error(void) { return t_err.c_str(); }
+
+const char *qmv_status_string(int status) {
+    switch (status) {
+    case QMV_OK: return "QMV_OK";
+    case QMV_ERR_INVALID_ARGUMENT: return "QMV_ERR_INVALID_ARGUMENT";
+    case QMV_ERR_MISALIGNED: return "QMV_ERR_MISALIGNED";
+    case QMV_ERR_NOT_INITIALIZED: return "QMV_ERR_NOT_INITIALIZED";
+    case QMV_ERR_NO_DEVICE: return "QMV_ERR_NO_DEVICE";
+    case QMV_ERR_UNSUPPORTED_ARCH: return "QMV_ERR_UNSUPPORTED_ARCH";
+    case QMV_ERR_HIP: return "QMV_ERR_HIP";
+    case QMV_ERR_UNSUPPORTED: return "QMV_ERR_UNSUPPORTED";
+    default: return "QMV_ERR_UNKNOWN";
+    }
+}
+
+const char *qmv_kernel_name(int format, int64_t k, int64_t m_tokens, int algo) {
+    thread_local std::string name;
+    if (block_elems(format) <= 0 || k <= 0 || k % block_elems(format) != 0 || m_tokens < 0)
+        return "";
+    const int a = resolve_algo(format, k, m_tokens, algo);
+    if (a == QMV_ALGO_GEMV) {
+        qmv::GemvPlan p;
+        qmv::plan_gemv(format, k, 1, 2, 256, &p);
+        name = qmv::gemv_kernel_name(p);
+    } else if (a == QMV_ALGO_MFMA) {
+        qmv::MfmaPlan p;
+        qmv::plan_mfma(format, k, 1, m_tokens, 256, &p);
+        name = qmv::mfma_kernel_name(p);
+    } else if (a == QMV_ALGO_SIMPLE) {
+        name = "qmv_simple";
+    } else {
+        name = "";
+    }
+    return name.c_str();
+}
+
+int qmv_run_ex(int format, const void *W, const float *x, float *y, int64_t k, int64_t n,
+               int64_t m_tokens, int64_t j_start, int64_t j_end, int accumulate, void *stream,
+               int algo) {
+    t_err.clear();
+    // ---- host-side validation: nothing is enqueued on failure
+    const int64_t qk = block_elems(format);
+    if (qk <= 0) return fail(QMV_ERR_INVALID_ARGUMENT, "unknown format %d", format);
+    if (k < 0 || n < 0 || m_tokens < 0)
+        return fail(QMV_ERR_INVALID_ARGUMENT, "negative shape k=%lld n=%lld m=%lld",
+                    (long long)k, (long long)n, (long long)m_tokens);
+    if (k % qk != 0)
+        return fail(QMV_ERR_INVALID_ARGUMENT, "k %lld must be a multiple of %lld for %s",
+                    (long long)k, (long long)qk, fmt_name(format));
+    if (j_start < 0 || j_end < j_start || j_end > n)
+        return fail(QMV_ERR_INVALID_ARGUMENT, "row range [%lld, %lld) outside [0, %lld)",
+                    (long long)j_start, (long long)j_end, (long long)n);
+    if (accumulate != 0 && accumulate != 1)
+        return fail(QMV_ERR_INVALID_ARGUMENT, "accumulate must be 0 or 1, got %d", accumulate);
+    if (algo < QMV_ALGO_AUTO || algo > QMV_ALGO_SIMPLE)
+        return fail(QMV_ERR_INVALID_ARGUMENT, "unknown algo %d", algo);
+    const bool work = m_tokens > 0 && j_end > j_start;
+    if (work) {
+        if (!y) return fail(QMV_ERR_INVALID_ARGUMENT, "y is NULL");
+        if (k > 0 && (!W || !x)) return fail(QMV_ERR_INVALID_ARGUMENT, "W or x is NULL");
+        if (((uintptr_t)W & 15) != 0)
+            return fail(QMV_ERR_MISALIGNED, "W must be 16-byte aligned");
+        if (((uintptr_t)x & 3) != 0 || ((uintptr_t)y & 3) != 0)
+            return fail(QMV_ERR_MISALIGNED, "x and y must be 4-byte aligned");
+    }
+    if (g_refs.load() <= 0)
+        return fail(QMV_ERR_NOT_INITIALIZED, "qmv_run before qmv_create");
+    if (!work) return QMV_OK;
+
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(QMV_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+    if (dev < 0 || (size_t)dev >= g_dev.size() || !g_dev[(size_t)dev].gfx950)
+        return fail(QMV_ERR_UNSUPPORTED_ARCH, "device %d is not gfx950", dev);
+    const int num_cu = g_dev[(size_t)dev].num_cu;
+    hipStream_t s = (hipStream_t)stream;
+    const uint8_t *Wb = (const uint8_t *)W;
+    const int64_t rb = row_bytes_of(format, k);
+
+    if (k == 0) {
+        if (accumulate) return QMV_OK;
+        e = qmv::launch_fill_zero(y, n, m_tokens, j_start, j_end, s);
+        if (e != hipSuccess) return fail(QMV_ERR_HIP, "fill launch: %s", hipGetErrorString(e));
+        return QMV_OK;
+    }
+
+    const int a = resolve_algo(format, k, m_tokens, algo);
+    if (a < 0)
+        return fail(QMV_ERR_UNSUPPORTED, "algo %d cannot serve %s with k=%lld m=%lld", algo,
+                    fmt_name(format), (long long)k, (long long)m_tokens);
+    const int64_t rows = j_end - j_start;
+    if (a == QMV_ALGO_SIMPLE) {
+        e = qmv::launch_simple(format, Wb, x, y, k, n, m_tokens, rb, j_start, j_end,
+                               accumulate, s);
+        if (e != hipSuccess) return fail(QMV_ERR_HIP, "simple launch: %s", hipGetErrorString(e));
+        return QMV_OK;
+    }
+    if (a == QMV_ALGO_MFMA) {
+        qmv::MfmaPlan p;
+        if (!qmv::plan_mfma(format, k, rows, m_tokens, num_cu, &p))
+            return fail(QMV_ERR_UNSUPPORTED, "mfma plan failed");
+        e = qmv::launch_mfma(p, Wb, x, y, k, n, m_tokens, rb, j_start, j_end, accumulate, s);
+        if (e != hipSuccess) return fail(QMV_ERR_HIP, "mfma launch: %s", hipGetErrorString(e));
+        return QMV_OK;
+    }
+    // streaming GEMV: tokens in groups of up to two per launch
+    for (int64_t t0 = 0; t0 < m_tokens;) {
+        qmv::GemvPlan p;
+        const int mt_max = (m_tokens - t0) >= 2 ? 2 : 1;
+        if (!qmv::plan_gemv(format, k, rows, mt_max, num_cu, &p))
+            return fail(QMV_ERR_UNSUPPORTED, "gemv plan failed");
+        e = qmv::launch_gemv(p, Wb, x + t0 * k, y + t0 * n, k, n, rb, j_start, j_end,
+                             accumulate, s);
+        if (e != hipSuccess) return fail(QMV_ERR_HIP, "gemv launch: %s", hipGetErrorString(e));
+        t0 += p.MT;
+    }
+    return QMV_OK;
+}
+
+int qmv_run(int format, const void *W, const float *x, float *y, int64_t k, int64_t n,
+            int64_t m_tokens, int64_t j_start, int64_t j_end, int accumulate, void *stream) {
+    return qmv_run_ex(format, W, x, y, k, n, m_tokens, j_start, j_end, accumulate, stream,
+                      QMV_ALGO_AUTO);
+}
+
+} // extern "C"

@@ -1,0 +1,59 @@
+// Internal declarations shared by the kernel files and the C-ABI layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace qmv {
+
+enum Fmt { FMT_F16 = 1, FMT_BF16 = 2, FMT_Q4_0 = 3, FMT_Q4_K = 4, FMT_Q6_K = 5 };
+
+// Geometry of one streaming-GEMV launch (see qmv_gemv.hip for the mapping).
+struct GemvPlan {
+    int fmt;
+    int U;        // 64-weight units per row (k / 64)
+    int UPL;      // units per lane (1 or 2)
+    int L;        // lanes per row slot (ceil(U / UPL))
+    int G;        // lanes per shuffle-reduction group: power of two <= 16 dividing L
+    int NG;       // reduction groups per row slot (L / G)
+    int P;        // row slots per workgroup
+    int T;        // threads per workgroup (P * L)
+    int RB;       // rows per slot per batch
+    int MT;       // tokens per launch (1 or 2)
+    int grid;     // workgroups
+    int x_in_lds; // stage x through LDS before loading it into registers
+    size_t lds_bytes;
+};
+
+// Geometry of one N-token MFMA launch.
+struct MfmaPlan {
+    int fmt;
+    int tiles_m, tiles_n;
+    int grid;
+    size_t lds_bytes;
+};
+
+// Fill the geometry for a GEMV launch of up to mt_max tokens over `rows` rows.
+// Returns false when the shape is outside what the streaming kernel covers.
+bool plan_gemv(int fmt, int64_t k, int64_t rows, int mt_max, int num_cu, GemvPlan *p);
+
+hipError_t launch_gemv(const GemvPlan &p, const uint8_t *W, const float *x, float *y,
+                       int64_t k, int64_t n, int64_t row_bytes, int64_t j_start,
+                       int64_t j_end, int accumulate, hipStream_t stream);
+const char *gemv_kernel_name(const GemvPlan &p);
+
+hipError_t launch_simple(int fmt, const uint8_t *W, const float *x, float *y, int64_t k,
+                         int64_t n, int64_t m, int64_t row_bytes, int64_t j_start,
+                         int64_t j_end, int accumulate, hipStream_t stream);
+
+hipError_t launch_fill_zero(float *y, int64_t n, int64_t m, int64_t j_start, int64_t j_end,
+                            hipStream_t stream);
+
+bool plan_mfma(int fmt, int64_t k, int64_t rows, int64_t m, int num_cu, MfmaPlan *p);
+hipError_t launch_mfma(const MfmaPlan &p, const uint8_t *W, const float *x, float *y,
+                       int64_t k, int64_t n, int64_t m, int64_t row_bytes, int64_t j_start,
+                       int64_t j_end, int accumulate, hipStream_t stream);
+const char *mfma_kernel_name(const MfmaPlan &p);
+
+} // namespace qmv

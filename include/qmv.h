@@ -1,0 +1,137 @@
+/*
+ * qmv.h -- C ABI of the block-quantized matrix-vector library for AMD
+ * Instinct MI355X (gfx950).
+ *
+ * Operation (rullama 0.5.0, src/backend/matmul.rs, module doc and the CPU
+ * helper `cpu_matmul_f32` of its tests): W holds n rows of k weights, stored
+ * row after row in GGUF block form; for every token t and output j,
+ *
+ *     y[t*n + j] = sum_{i<k} x[t*k + i] * w_j[i]
+ *
+ * where w_j[i] is weight i of row j decoded from its block. Batched x/y are
+ * token-major, as in the batched matmul tests of the same page
+ * (`x_batch[b*k..]`, `y[b*n..]`).
+ *
+ * Row range and accumulate (rullama 0.5.0, src/backend/dispatch/mod.rs,
+ * struct MatmulBackInputParams): a call touches only outputs j_start <= j <
+ * j_end, so callers can tile a vocabulary-sized product into several
+ * launches; accumulate = 0 writes the result, accumulate = 1 adds it to what y
+ * holds. Outputs outside the range are never read or written. (The pages
+ * apply the range to the summed axis of the transposed product; here it
+ * selects rows of W, i.e. outputs of the forward product.)
+ *
+ * All pointers are device pointers (memory from hipMalloc or a torch CUDA
+ * tensor) unless stated. The caller owns every buffer; the library keeps no
+ * pointer after a call returns and allocates no memory per call.
+ */
+#ifndef QMV_H
+#define QMV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Weight formats. Block sizes: rullama 0.5.0, src/backend/matmul.rs, fns
+ * matmul_f16, matmul_bf16 (2 bytes per weight), matmul_q4_0 (18 bytes per 32),
+ * matmul_q4_k (144 bytes per 256), matmul_q6_k (210 bytes per 256). */
+enum qmv_format {
+    QMV_FMT_F16 = 1,
+    QMV_FMT_BF16 = 2,
+    QMV_FMT_Q4_0 = 3,
+    QMV_FMT_Q4_K = 4,
+    QMV_FMT_Q6_K = 5
+};
+
+/* Kernel families selectable with qmv_run_ex. */
+enum qmv_algo {
+    QMV_ALGO_AUTO = 0,   /* GEMV for small m_tokens, MFMA tiles for prefill-sized m */
+    QMV_ALGO_GEMV = 1,   /* streaming matvec; m_tokens handled in small groups    */
+    QMV_ALGO_MFMA = 2,   /* N-token tiles decoded to exact bf16 codes in LDS, MFMA */
+    QMV_ALGO_SIMPLE = 3  /* one wave per row, any valid shape (slow, for checks)   */
+};
+
+/* Status codes. 0 is success; every error is negative. */
+#define QMV_OK 0
+#define QMV_ERR_INVALID_ARGUMENT (-1) /* bad format, shape, range or null pointer  */
+#define QMV_ERR_MISALIGNED (-2)       /* W not 16-byte or x/y not 4-byte aligned    */
+#define QMV_ERR_NOT_INITIALIZED (-3)  /* qmv_run before qmv_create                  */
+#define QMV_ERR_NO_DEVICE (-4)        /* no HIP device visible                      */
+#define QMV_ERR_UNSUPPORTED_ARCH (-5) /* current device is not gfx950               */
+#define QMV_ERR_HIP (-6)              /* a HIP runtime call or launch failed        */
+#define QMV_ERR_UNSUPPORTED (-7)      /* valid request this kernel family cannot do */
+
+/* Initialise the process-wide context: counts the HIP devices and records,
+ * per device, whether it is gfx950 and its compute-unit count. Reference
+ * counted: every successful qmv_create needs one qmv_destroy. Returns QMV_OK,
+ * QMV_ERR_NO_DEVICE when no device is visible (nothing is then initialised),
+ * or QMV_ERR_UNSUPPORTED_ARCH when no visible device is gfx950. Must not race
+ * with qmv_run or qmv_destroy. */
+int qmv_create(void);
+
+/* Enqueue y (=|+=) x @ W for rows [j_start, j_end) on `stream` (a hipStream_t;
+ * NULL is the default stream) of the current device, with the kernel family
+ * chosen automatically. Never synchronises; the caller keeps W, x and y alive
+ * until the stream work completes.
+ *
+ *   format      one of enum qmv_format.
+ *   W           n rows of qmv_weight_bytes(format, k, 1) bytes, 16-byte aligned.
+ *   x           m_tokens x k f32, token-major, 4-byte aligned.
+ *   y           m_tokens x n f32, token-major, 4-byte aligned; indexed by the
+ *               absolute row j, not j - j_start.
+ *   k           weights per row: a multiple of 32 (Q4_0), 256 (Q4_K, Q6_K) or
+ *               2 (F16, BF16) (rullama 0.5.0, src/backend/matmul.rs, the shape
+ *               checks of each matmul_* function).
+ *   n           rows of W.
+ *   m_tokens    number of tokens (x rows / y rows), >= 0.
+ *   j_start, j_end  0 <= j_start <= j_end <= n.
+ *   accumulate  0: y = result; 1: y += result (each output read once, added,
+ *               written once).
+ *
+ * Returns QMV_OK after a successful enqueue (or when there is nothing to do:
+ * m_tokens == 0 or j_start == j_end). With k == 0 the sum is empty: y is set
+ * to 0, or left as is when accumulate = 1. Argument errors are detected on the
+ * host before anything is enqueued; nothing is written to y then. The result
+ * of one row does not depend on j_start/j_end, so any tiling of [0, n) gives
+ * bit-identical outputs. Reentrant across streams and threads. */
+int qmv_run(int format, const void *W, const float *x, float *y, int64_t k, int64_t n,
+            int64_t m_tokens, int64_t j_start, int64_t j_end, int accumulate,
+            void *stream);
+
+/* qmv_run with an explicit kernel family (enum qmv_algo). QMV_ALGO_MFMA
+ * supports Q4_0, Q4_K and Q6_K and needs k to be a multiple of 256; otherwise
+ * it returns QMV_ERR_UNSUPPORTED. All families meet the same accuracy
+ * contract; they may differ in the last bits. */
+int qmv_run_ex(int format, const void *W, const float *x, float *y, int64_t k, int64_t n,
+               int64_t m_tokens, int64_t j_start, int64_t j_end, int accumulate,
+               void *stream, int algo);
+
+/* Release one reference to the context; the last one frees it. Safe to call
+ * when not initialised. Must not race with qmv_run or qmv_create. */
+void qmv_destroy(void);
+
+/* Bytes of W for n rows of k weights, or -1 if the format is unknown or k is
+ * not a whole number of blocks (rullama 0.5.0, src/backend/matmul.rs, the
+ * expected byte counts checked by each matmul_* function: k*n*2,
+ * (k/32)*18*n, (k/256)*144*n, (k/256)*210*n). Host-only; needs no context. */
+int64_t qmv_weight_bytes(int format, int64_t k, int64_t n);
+
+/* Message for the last failing call on this thread (empty if none). The
+ * pointer stays valid until the next library call on the same thread. */
+const char *qmv_last_error(void);
+
+/* Short name of a status code. */
+const char *qmv_status_string(int status);
+
+/* Name of the kernel that qmv_run_ex would launch for these arguments, or ""
+ * when the request is invalid. Host-only; needs no context or device. Used
+ * to find the launch in profiler output. */
+const char *qmv_kernel_name(int format, int64_t k, int64_t m_tokens, int algo);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QMV_H */

@@ -1,0 +1,287 @@
+"""GPU path against the CPU oracle, element by element, through the C ABI.
+
+Acceptance per output: |y_gpu - y_ref| <= 1e-4 * sum_i |x_i * w_ji| (plus half
+an f32 ulp of the expected value when accumulating onto a base), and cosine
+>= 0.9999 over all checked outputs. Outputs outside [j_start, j_end) must keep
+their sentinel bits. Tiling must not change a single bit.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from block_quantized_matvec_gguf_amd import binding as qb
+from block_quantized_matvec_gguf_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+F16, BF16, Q4_0, Q4_K, Q6_K = synth.F16, synth.BF16, synth.Q4_0, synth.Q4_K, synth.Q6_K
+SENTINEL = np.float32(-7777.25)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu_context():
+    assert torch.cuda.is_available(), "the GPU tests need a visible GPU"
+    qb.ensure_context()
+    yield
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def gen(fmt, k, n, m, seed):
+    rng = np.random.default_rng(seed)
+    W = synth.gen_weights(fmt, rng, n, k)
+    x = synth.gen_x(rng, m, k)
+    return W, x
+
+
+def run_gpu(fmt, W, x, k, n, base, algo="auto", j0=0, j1=None, accumulate=False,
+            Wd=None, xd=None):
+    Wd = dev(W) if Wd is None else Wd
+    xd = dev(x) if xd is None else xd
+    yd = dev(base)
+    qb.matvec(fmt, Wd, xd, k, n, y=yd, j_start=j0, j_end=j1, accumulate=accumulate,
+              algo=algo)
+    torch.cuda.synchronize()
+    return yd.cpu().numpy()
+
+
+def check_case(fmt, k, n, m, algo="auto", j0=0, j1=None, accumulate=False, seed=1,
+               rows=None, W=None, x=None):
+    print("case fmt=%s k=%d n=%d m=%d algo=%s range=[%d,%s) acc=%d"
+          % (synth.FORMAT_NAMES[fmt], k, n, m, algo, j0, j1, accumulate), flush=True)
+    if W is None:
+        W, x = gen(fmt, k, n, m, seed)
+    j1 = n if j1 is None else j1
+    rng = np.random.default_rng(seed + 99)
+    if accumulate:
+        base = rng.uniform(-1, 1, size=(m, n)).astype(np.float32)
+    else:
+        base = np.full((m, n), SENTINEL, dtype=np.float32)
+    y = run_gpu(fmt, W, x, k, n, base, algo, j0, j1, accumulate)
+    outside = np.ones(n, dtype=bool)
+    outside[j0:j1] = False
+    assert np.array_equal(y[:, outside].view(np.uint32), base[:, outside].view(np.uint32)), \
+        "outputs outside the row range changed"
+    sel = np.arange(j0, j1) if rows is None else np.asarray(rows)
+    yref, sref = oracle.gemv_rows(fmt, W, x, k, n, sel)
+    res = oracle.check_parity(y[:, sel], yref, sref, base=base[:, sel] if accumulate else None)
+    assert res["ok"], res
+    return y, W, x
+
+
+# ------------------------------------------------------------ small shapes
+
+@pytest.mark.parametrize("algo", ["auto", "gemv", "simple"])
+def test_q4_0_small_workload(algo):
+    """Q4_0, k=256, n=512, m=1: the small measured workload."""
+    f, W, x, spec = synth.workload("q4_0_small")
+    check_case(f, spec["k"], spec["n"], 1, algo=algo, W=W, x=x)
+
+
+SHAPES = [(256, 37, 1), (768, 1000, 2), (2560, 333, 3), (6400, 129, 1), (512, 1, 1)]
+
+
+@pytest.mark.parametrize("fmt", [Q4_0, Q4_K, Q6_K, BF16, F16],
+                         ids=lambda f: synth.FORMAT_NAMES[f])
+@pytest.mark.parametrize("k,n,m", SHAPES)
+@pytest.mark.parametrize("algo", ["gemv", "simple"])
+def test_formats_ragged(fmt, k, n, m, algo):
+    check_case(fmt, k, n, m, algo=algo, seed=k * 7 + n + m + fmt)
+
+
+@pytest.mark.parametrize("fmt", [Q4_0, Q4_K, Q6_K, BF16, F16],
+                         ids=lambda f: synth.FORMAT_NAMES[f])
+def test_row_range_and_accumulate(fmt):
+    k, n, m = 1280 if fmt in (Q4_0, BF16, F16) else 1536, 777, 2
+    check_case(fmt, k, n, m, j0=13, j1=700, seed=5)
+    check_case(fmt, k, n, m, j0=100, j1=101, accumulate=True, seed=6)
+    check_case(fmt, k, n, m, j0=0, j1=n, accumulate=True, seed=7)
+
+
+def test_pages_q4_0_case():
+    """The pages' Q4_0 parity case (rullama 0.5.0, src/backend/matmul.rs, test
+    q4_0_matmul_gpu_vs_cpu_oracle): k=128, n=16, d in [-0.1, 0.1), random code
+    bytes, x in [-0.5, 0.5); its bar is max_abs < 1e-4."""
+    rng = np.random.default_rng(0x12345678)
+    k, n = 128, 16
+    W = synth.gen_q4_0(rng, n, k, d_range=(-0.1, 0.1))
+    x = rng.uniform(-0.5, 0.5, size=(1, k)).astype(np.float32)
+    y, _, _ = check_case(Q4_0, k, n, 1, W=W, x=x)
+    yref, _ = oracle.gemv(Q4_0, W, x, k, n)
+    assert np.max(np.abs(y - yref)) < 1e-4
+
+
+def test_identity_f16():
+    """W = I with n = k = 4 (the pages' f16_matmul_3x4_eye): y = x. Goes
+    through the per-element kernel since k is not a multiple of 64."""
+    k = n = 4
+    W = np.eye(n, k).astype("<f2").view(np.uint8).reshape(-1)
+    x = ((np.arange(k) + 1) * 0.25).astype(np.float32).reshape(1, k)
+    y = run_gpu(F16, W, x, k, n, np.zeros((1, n), np.float32))
+    assert np.array_equal(y[0], x[0])
+
+
+@pytest.mark.parametrize("fmt", [F16, BF16])
+@pytest.mark.parametrize("algo", ["gemv", "simple"])
+def test_exact_small_integers(fmt, algo):
+    """Integer weights and dyadic x: every partial sum is exact in f32, so the
+    GPU must equal the oracle bit for bit (a dropped or doubled term shows)."""
+    rng = np.random.default_rng(31)
+    k, n, m = 1024, 300, 2
+    wi = rng.integers(-9, 10, size=(n, k))
+    x = (rng.integers(-8, 9, size=(m, k)) / 8.0).astype(np.float32)
+    if fmt == F16:
+        W = wi.astype("<f2").view(np.uint8).reshape(-1)
+    else:
+        W = synth.bf16_bits(wi.astype(np.float32)).astype("<u2").view(np.uint8).reshape(-1)
+    y = run_gpu(fmt, W, x, k, n, np.zeros((m, n), np.float32), algo=algo)
+    yref, _ = oracle.gemv(fmt, W, x, k, n)
+    assert np.array_equal(y.astype(np.float64), yref)
+
+
+def test_zero_blocks():
+    k, n = 512, 64
+    blk = np.zeros((n * k // 32, 18), np.uint8)
+    blk[:, 0:2] = np.array([0x00, 0x3C], np.uint8)  # d = 1
+    blk[:, 2:] = 0x88  # every code 8
+    x = synth.gen_x(np.random.default_rng(3), 1, k)
+    y = run_gpu(Q4_0, blk.reshape(-1), x, k, n, np.full((1, n), SENTINEL, np.float32))
+    assert not np.any(y)
+    W = synth.gen_q6_k(np.random.default_rng(4), n, k)
+    W.reshape(-1, 210)[:, 208:210] = 0  # d = 0
+    y = run_gpu(Q6_K, W, x, k, n, np.full((1, n), SENTINEL, np.float32))
+    assert not np.any(y)
+
+
+def test_empty_and_degenerate():
+    # k == 0: empty sum -> zeros, or unchanged with accumulate
+    x = np.zeros((2, 0), np.float32)
+    W = np.zeros(0, np.uint8)
+    base = np.full((2, 9), 3.5, np.float32)
+    Wd = torch.zeros(0, dtype=torch.uint8, device="cuda")
+    xd = torch.zeros((2, 0), dtype=torch.float32, device="cuda")
+    y = run_gpu(Q4_K, W, x, 0, 9, base, j0=2, j1=7, Wd=Wd, xd=xd)
+    assert np.all(y[:, 2:7] == 0) and np.all(y[:, :2] == 3.5) and np.all(y[:, 7:] == 3.5)
+    y = run_gpu(Q4_K, W, x, 0, 9, base, accumulate=True, Wd=Wd, xd=xd)
+    assert np.all(y == 3.5)
+    # empty range and zero tokens are no-ops
+    Wq, xq = gen(Q6_K, 256, 10, 1, 8)
+    y = run_gpu(Q6_K, Wq, xq, 256, 10, np.full((1, 10), SENTINEL, np.float32), j0=4, j1=4)
+    assert np.all(y == SENTINEL)
+    yd = dev(np.full((0, 10), SENTINEL, np.float32))
+    rc = qb.qmv_run(Q6_K, dev(Wq).data_ptr(), dev(xq).data_ptr(), yd.data_ptr(), 256, 10, 0,
+                    0, 10, 0, torch.cuda.current_stream().cuda_stream)
+    assert rc == qb.QMV_OK
+
+
+@pytest.mark.parametrize("fmt,k,n", [(Q4_0, 96, 50), (F16, 10, 33), (BF16, 2, 5),
+                                     (F16, 72, 20)])
+def test_shapes_only_the_simple_kernel_covers(fmt, k, n):
+    check_case(fmt, k, n, 2, algo="auto", seed=k + n)
+    W, x = gen(fmt, k, n, 1, 1)
+    with pytest.raises(qb.QmvError) as e:
+        run_gpu(fmt, W, x, k, n, np.zeros((1, n), np.float32), algo="gemv")
+    assert e.value.status == qb.QMV_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("fmt,k,n,m", [(Q4_K, 65536, 40, 1), (Q6_K, 16384, 100, 2),
+                                       (BF16, 40960, 24, 1), (Q4_0, 12800, 64, 3)])
+def test_long_rows(fmt, k, n, m):
+    """Long rows: two units per lane and/or x loaded straight from global
+    memory instead of LDS."""
+    check_case(fmt, k, n, m, algo="gemv", seed=k + m)
+
+
+def test_misaligned_pointers_rejected():
+    W, x = gen(Q4_K, 256, 4, 1, 2)
+    Wd = dev(np.concatenate([np.zeros(16, np.uint8), W]))
+    xd, yd = dev(x), dev(np.zeros((1, 4), np.float32))
+    s = torch.cuda.current_stream().cuda_stream
+    rc = qb.qmv_run(Q4_K, Wd.data_ptr() + 2, xd.data_ptr(), yd.data_ptr(), 256, 4, 1, 0, 4, 0, s)
+    assert rc == qb.QMV_ERR_MISALIGNED
+    rc = qb.qmv_run(Q4_K, Wd.data_ptr() + 16, xd.data_ptr(), yd.data_ptr(), 256, 4, 1, 0, 4, 0, s)
+    assert rc == qb.QMV_OK
+    torch.cuda.synchronize()
+
+
+def test_run_to_run_determinism():
+    k, n = 2560, 4096
+    W, x = gen(Q6_K, k, n, 1, 9)
+    Wd, xd = dev(W), dev(x)
+    base = np.zeros((1, n), np.float32)
+    y1 = run_gpu(Q6_K, W, x, k, n, base, Wd=Wd, xd=xd)
+    y2 = run_gpu(Q6_K, W, x, k, n, base, Wd=Wd, xd=xd)
+    assert np.array_equal(y1.view(np.uint32), y2.view(np.uint32))
+
+
+# ------------------------------------------------------- measured workloads
+
+@pytest.mark.parametrize("name", ["bf16_ffn_up", "f16_ffn_up", "q4_k_ffn_up"])
+def test_ffn_up_workloads_full(name):
+    """k=2560, n=10240, m=1, every output against the oracle."""
+    f, W, x, spec = synth.workload(name)
+    check_case(f, spec["k"], spec["n"], 1, W=W, x=x)
+
+
+@pytest.fixture(scope="module")
+def vocab():
+    f, W, x, spec = synth.workload("q6_k_vocab_outproj")
+    return f, W, x, spec, dev(W), dev(x)
+
+
+def _vocab_sample_rows(n, tiles):
+    rng = np.random.default_rng(77)
+    edges = [t * n // tiles for t in range(tiles + 1)]
+    rows = set(range(64)) | set(range(n - 64, n))
+    for e in edges[1:-1]:
+        rows |= set(range(e - 3, e + 3))
+    rows |= set(rng.integers(0, n, 2048).tolist())
+    return np.array(sorted(rows), dtype=np.int64)
+
+
+def test_vocab_q6_k_untiled_and_tiled(vocab):
+    """Q6_K output projection k=2560, n=262144 (vocab), m=1. Untiled against
+    sampled oracle rows; 8 j-range tiles (a) with accumulate=0 bit-equal to
+    untiled, (b) the pages' convention (tile 0 writes, tiles 1..7 add) onto
+    zeros bit-equal to untiled, (c) all tiles accumulating onto a base equal
+    to base + untiled in f32, and within tolerance of base + oracle."""
+    f, W, x, spec, Wd, xd = vocab
+    k, n, tiles = spec["k"], spec["n"], spec["tiles"]
+    print("vocab untiled", flush=True)
+    y_un = run_gpu(f, W, x, k, n, np.zeros((1, n), np.float32), Wd=Wd, xd=xd)
+    rows = _vocab_sample_rows(n, tiles)
+    yref, sref = oracle.gemv_rows(f, W, x, k, n, rows)
+    res = oracle.check_parity(y_un[:, rows], yref, sref)
+    assert res["ok"], res
+    edges = [t * n // tiles for t in range(tiles + 1)]
+
+    def tiled(init, acc_of):
+        yd = dev(init)
+        for t in range(tiles):
+            qb.matvec(f, Wd, xd, k, n, y=yd, j_start=edges[t], j_end=edges[t + 1],
+                      accumulate=acc_of(t))
+        torch.cuda.synchronize()
+        return yd.cpu().numpy()
+
+    print("vocab tiled", flush=True)
+    y_a = tiled(np.full((1, n), SENTINEL, np.float32), lambda t: False)
+    assert np.array_equal(y_a.view(np.uint32), y_un.view(np.uint32))
+    y_b = tiled(np.zeros((1, n), np.float32), lambda t: t > 0)
+    assert np.array_equal(y_b.view(np.uint32), y_un.view(np.uint32))
+    base = np.random.default_rng(5).uniform(-1, 1, size=(1, n)).astype(np.float32)
+    y_c = tiled(base, lambda t: True)
+    assert np.array_equal(y_c.view(np.uint32), (base + y_un).view(np.uint32))
+    res = oracle.check_parity(y_c[:, rows], yref, sref, base=base[:, rows])
+    assert res["ok"], res
+
+
+def test_prefill_shape_gemv_path():
+    """Q4_K, m=64, k=4096, n=14336 through the streaming kernel (tokens in
+    pairs), sampled rows against the oracle for all 64 tokens."""
+    f, W, x, spec = synth.workload("q4_k_prefill")
+    rows = np.unique(np.concatenate([np.arange(32), np.arange(spec["n"] - 32, spec["n"]),
+                                     np.random.default_rng(6).integers(0, spec["n"], 192)]))
+    check_case(f, spec["k"], spec["n"], spec["m"], algo="gemv", W=W, x=x, rows=rows)

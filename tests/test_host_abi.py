@@ -1,0 +1,113 @@
+"""The C-ABI library on the host (no GPU needed): it loads, exports every
+symbol include/qmv.h declares, and rejects bad arguments before touching a
+device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from block_quantized_matvec_gguf_amd import binding as qb
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(qb.LIB_PATH):
+        from block_quantized_matvec_gguf_amd import build
+        build.build()
+    return qb.load()
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "qmv.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(qmv_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for need in ("qmv_create", "qmv_run", "qmv_destroy", "qmv_run_ex", "qmv_weight_bytes",
+                 "qmv_last_error"):
+        assert need in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    raw = ctypes.CDLL(qb.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(raw, name), name
+
+
+def test_weight_bytes(lib):
+    assert qb.qmv_weight_bytes(qb.QMV_FMT_F16, 2560, 10240) == 2560 * 10240 * 2
+    assert qb.qmv_weight_bytes(qb.QMV_FMT_BF16, 64, 3) == 384
+    assert qb.qmv_weight_bytes(qb.QMV_FMT_Q4_0, 256, 512) == 8 * 18 * 512
+    assert qb.qmv_weight_bytes(qb.QMV_FMT_Q4_K, 2560, 10240) == 14745600
+    assert qb.qmv_weight_bytes(qb.QMV_FMT_Q6_K, 2560, 262144) == 550502400
+    assert qb.qmv_weight_bytes(qb.QMV_FMT_Q4_K, 4096, 14336) == 33030144
+    assert qb.qmv_weight_bytes(qb.QMV_FMT_Q4_0, 48, 1) == -1
+    assert qb.qmv_weight_bytes(qb.QMV_FMT_Q6_K, 128, 1) == -1
+    assert qb.qmv_weight_bytes(qb.QMV_FMT_F16, 3, 1) == -1
+    assert qb.qmv_weight_bytes(9, 256, 1) == -1
+    assert qb.qmv_weight_bytes(qb.QMV_FMT_Q4_0, 0, 7) == 0
+
+
+def test_status_strings(lib):
+    assert qb.qmv_status_string(0) == "QMV_OK"
+    assert qb.qmv_status_string(qb.QMV_ERR_NOT_INITIALIZED) == "QMV_ERR_NOT_INITIALIZED"
+    assert qb.qmv_status_string(-99) == "QMV_ERR_UNKNOWN"
+
+
+def test_kernel_names(lib):
+    assert qb.qmv_kernel_name(qb.QMV_FMT_Q6_K, 2560, 1) == "qmv_gemv<q6_k>"
+    assert qb.qmv_kernel_name(qb.QMV_FMT_Q4_0, 96, 1) == "qmv_simple"
+    assert qb.qmv_kernel_name(qb.QMV_FMT_Q4_0, 96, 1, qb.QMV_ALGO_GEMV) == ""
+    assert qb.qmv_kernel_name(qb.QMV_FMT_F16, 10, 1) == "qmv_simple"
+    assert qb.qmv_kernel_name(qb.QMV_FMT_Q4_K, 300, 1) == ""
+
+
+def _run(**kw):
+    a = dict(format=qb.QMV_FMT_Q4_K, W=0x1000, x=0x2000, y=0x3000, k=256, n=8, m_tokens=1,
+             j_start=0, j_end=8, accumulate=0, stream=None, algo=0)
+    a.update(kw)
+    return qb.qmv_run_ex(a["format"], a["W"], a["x"], a["y"], a["k"], a["n"], a["m_tokens"],
+                         a["j_start"], a["j_end"], a["accumulate"], a["stream"], a["algo"])
+
+
+def test_argument_errors_are_host_side(lib):
+    E = qb.QMV_ERR_INVALID_ARGUMENT
+    assert _run(format=0) == E
+    assert _run(k=300) == E
+    assert _run(format=qb.QMV_FMT_F16, k=7) == E
+    assert _run(k=-256) == E
+    assert _run(n=-1) == E
+    assert _run(m_tokens=-1) == E
+    assert _run(j_start=5, j_end=4) == E
+    assert _run(j_end=9) == E
+    assert _run(j_start=-1) == E
+    assert _run(accumulate=2) == E
+    assert _run(algo=7) == E
+    assert _run(y=0) == E
+    assert _run(W=0) == E
+    assert _run(j_end=9) == E and "row range" in qb.qmv_last_error()
+    assert _run(W=0x1001) == qb.QMV_ERR_MISALIGNED
+    assert _run(x=0x2002) == qb.QMV_ERR_MISALIGNED
+    assert _run(y=0x3001) == qb.QMV_ERR_MISALIGNED
+    assert qb.qmv_last_error()
+
+
+def test_run_before_create(lib):
+    # this process never called qmv_create
+    assert _run() == qb.QMV_ERR_NOT_INITIALIZED
+    assert "qmv_create" in qb.qmv_last_error()
+    qb.qmv_destroy()  # safe when not initialised
+
+
+def test_create_without_a_device(lib):
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is visible")
+    rc = qb.qmv_create()
+    assert rc in (qb.QMV_ERR_NO_DEVICE, qb.QMV_ERR_UNSUPPORTED_ARCH)
+    assert _run() == qb.QMV_ERR_NOT_INITIALIZED
