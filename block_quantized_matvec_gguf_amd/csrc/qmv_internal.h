@@ -21,7 +21,8 @@ struct GemvPlan {
     int T;        // threads per workgroup (P * L)
     int RB;       // rows per slot per batch
     int MT;       // tokens per launch (1 or 2)
-    int grid;     // workgroups
+    int grid;     // workgroups wanted (one per batch); the launch caps it at residency
+    int num_cu;   // compute units of the device
     int x_in_lds; // stage x through LDS before loading it into registers
     size_t lds_bytes;
 };
