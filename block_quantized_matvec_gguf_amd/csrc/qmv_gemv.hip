@@ -6,17 +6,28 @@
 // MatmulBackInputParams (applied here to output rows).
 //
 // Mapping. A row of k weights is cut into U = k/64 "units" of 64 weights. A
-// workgroup holds P row slots of L lanes; lane l of a slot owns units
-// l, l+L (UPL of them) for the whole launch, so the 64 x values of each owned
-// unit (and the per-group sums of x the block formulas need) are loaded into
-// registers once, from LDS, at kernel start. The workgroup then streams
-// batches of P*RB rows: slot s takes rows base+s, base+s+P, ..., every lane
-// issues the loads of its unit in all RB rows first (non-temporal, coalesced
-// across the lanes of a slot), then decodes and multiplies. Per-lane partial
-// sums of a row are reduced with DPP inside aligned groups of G lanes, and the
-// L/G group sums go through LDS (double-buffered, one barrier per batch).
-// Every row's reduction order depends only on k, never on j_start/j_end, so
-// any tiling of the rows gives bit-identical outputs.
+// workgroup holds P row slots of L lanes; lane l of a slot owns units l,
+// l+L, ... (UPL of them) for the whole launch, so the 64 x values of each
+// owned unit sit in registers, loaded once at kernel start from a transposed
+// copy of x in LDS (conflict-free). The workgroup then processes batches of
+// P*RB consecutive rows (slot s takes rows base+s, base+s+P, ...). Per-lane
+// partial sums of a row are reduced with DPP inside aligned groups of G lanes;
+// the L/G group sums of each row go through LDS. Every row's arithmetic and
+// reduction order depend only on k, never on the row range, so any tiling of
+// the rows gives bit-identical outputs.
+//
+// Weight streaming. Wave loads must cover whole, contiguous cache lines: a
+// load instruction whose 64 lanes touch scattered 16-byte pieces costs the L1
+// one tag lookup per line piece and multiplies the L1->L2 requests.
+//  * F16/BF16 rows are plain arrays: each lane loads eight 16-byte chunks at a
+//    stride of U chunks, so every load instruction reads one contiguous span
+//    ("direct" kernel).
+//  * Block formats (Q4_0, Q4_K, Q6_K) interleave fields of odd sizes. There
+//    each batch's rows, one contiguous byte range, are copied with coalesced
+//    16-byte loads into registers one batch ahead, then written to a
+//    double-buffered LDS area from which lanes read their unit's fields
+//    ("staged" kernel). One LDS-only barrier per batch covers both the buffer
+//    swap and the cross-group reduction.
 //
 // Decode. Codes are masked into bytes and converted with one instruction per
 // weight: Q4_0 and Q6_K codes as signed bytes holding a multiple of q-8 or
@@ -36,32 +47,43 @@ namespace qmv {
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
-// 4-byte aligned multi-dword loads (dword alignment is all global loads need).
-typedef uint32_t u32x4a __attribute__((ext_vector_type(4), aligned(4)));
-typedef uint32_t u32x2a __attribute__((ext_vector_type(2), aligned(4)));
+// LDS reads at 2-byte alignment (block fields): single ds_read_b128/b64.
+typedef uint32_t u32x4h __attribute__((ext_vector_type(4), aligned(2)));
+typedef uint32_t u32x2h __attribute__((ext_vector_type(2), aligned(2)));
 
 __device__ __forceinline__ u32x4 ld16(const uint8_t *p) {
     return __builtin_nontemporal_load((const u32x4 *)p);
 }
-__device__ __forceinline__ u32x4 ld16a4(const uint8_t *p) {
-    u32x4a v = __builtin_nontemporal_load((const u32x4a *)p);
+__device__ __forceinline__ u32x4 lds16(const uint8_t *p) {
+    const u32x4h v = *(const u32x4h *)p;
     return u32x4{v.x, v.y, v.z, v.w};
 }
-__device__ __forceinline__ u32x2 ld8a4(const uint8_t *p) {
-    u32x2a v = __builtin_nontemporal_load((const u32x2a *)p);
+__device__ __forceinline__ u32x2 lds8(const uint8_t *p) {
+    const u32x2h v = *(const u32x2h *)p;
     return u32x2{v.x, v.y};
 }
-__device__ __forceinline__ uint32_t ld4(const uint8_t *p) {
-    return __builtin_nontemporal_load((const uint32_t *)p);
+__device__ __forceinline__ uint32_t lds2(const uint8_t *p) { return *(const uint16_t *)p; }
+// LDS serves 16- and 8-byte reads that are not naturally aligned, but only
+// with a large stall, so fields of the 2-byte aligned block formats are read
+// as the dwords covering them (ds_read2_b32) and shifted into place with
+// v_alignbyte_b32. The dword after a field is read even when the field is
+// dword aligned; it lies inside the LDS allocation and is then not used.
+__device__ __forceinline__ u32x4 lds16u(const uint8_t *p) {
+    const uint32_t sh = (uint32_t)(uintptr_t)p & 3u;
+    const uint32_t *d = (const uint32_t *)(p - sh);
+    const uint32_t w0 = d[0], w1 = d[1], w2 = d[2], w3 = d[3], w4 = d[4];
+    return u32x4{__builtin_amdgcn_alignbyte(w1, w0, sh), __builtin_amdgcn_alignbyte(w2, w1, sh),
+                 __builtin_amdgcn_alignbyte(w3, w2, sh), __builtin_amdgcn_alignbyte(w4, w3, sh)};
 }
-__device__ __forceinline__ uint32_t ld2(const uint8_t *p) {
-    return __builtin_nontemporal_load((const uint16_t *)p);
+__device__ __forceinline__ u32x2 lds8u(const uint8_t *p) {
+    const uint32_t sh = (uint32_t)(uintptr_t)p & 3u;
+    const uint32_t *d = (const uint32_t *)(p - sh);
+    const uint32_t w0 = d[0], w1 = d[1], w2 = d[2];
+    return u32x2{__builtin_amdgcn_alignbyte(w1, w0, sh), __builtin_amdgcn_alignbyte(w2, w1, sh)};
 }
-__device__ __forceinline__ const uint8_t *align4_down(const uint8_t *p) {
-    return p - ((uintptr_t)p & 3);
-}
+
 // Keeps the compiler from folding a byte mask into per-element bit-field
-// extracts, so that the byte conversions select v_cvt_f32_ubyte0..3.
+// extracts, so that the byte conversions select v_cvt_f32_{ubyte,i32 sdwa}.
 __device__ __forceinline__ uint32_t opaque(uint32_t v) {
     asm("" : "+v"(v));
     return v;
@@ -70,24 +92,15 @@ __device__ __forceinline__ float ub0(uint32_t v) { return (float)(v & 0xffu); }
 __device__ __forceinline__ float ub1(uint32_t v) { return (float)((v >> 8) & 0xffu); }
 __device__ __forceinline__ float ub2(uint32_t v) { return (float)((v >> 16) & 0xffu); }
 __device__ __forceinline__ float ub3(uint32_t v) { return (float)(v >> 24); }
+__device__ __forceinline__ float sb0(uint32_t v) { return (float)(int)(int8_t)(v & 0xffu); }
+__device__ __forceinline__ float sb1(uint32_t v) { return (float)(int)(int8_t)((v >> 8) & 0xffu); }
+__device__ __forceinline__ float sb2(uint32_t v) { return (float)(int)(int8_t)((v >> 16) & 0xffu); }
+__device__ __forceinline__ float sb3(uint32_t v) { return (float)((int)v >> 24); }
 __device__ __forceinline__ float f16lo(uint32_t v) {
     return (float)__builtin_bit_cast(_Float16, (uint16_t)(v & 0xffffu));
 }
 __device__ __forceinline__ float f16hi(uint32_t v) {
     return (float)__builtin_bit_cast(_Float16, (uint16_t)(v >> 16));
-}
-// Signed bytes: each selects v_cvt_f32_i32 with an SDWA sign-extended byte.
-__device__ __forceinline__ float sb0(uint32_t v) { return (float)(int)(int8_t)(v & 0xffu); }
-__device__ __forceinline__ float sb1(uint32_t v) { return (float)(int)(int8_t)((v >> 8) & 0xffu); }
-__device__ __forceinline__ float sb2(uint32_t v) { return (float)(int)(int8_t)((v >> 16) & 0xffu); }
-__device__ __forceinline__ float sb3(uint32_t v) { return (float)((int)v >> 24); }
-// acc + sum_b signed_byte_b(q) * x[b]
-__device__ __forceinline__ float sdot4(uint32_t q, const float *x, float acc) {
-    acc = fmaf(sb0(q), x[0], acc);
-    acc = fmaf(sb1(q), x[1], acc);
-    acc = fmaf(sb2(q), x[2], acc);
-    acc = fmaf(sb3(q), x[3], acc);
-    return acc;
 }
 // acc + sum_b byte_b(q) * x[b]
 __device__ __forceinline__ float dot4(uint32_t q, const float *x, float acc) {
@@ -97,26 +110,56 @@ __device__ __forceinline__ float dot4(uint32_t q, const float *x, float acc) {
     acc = fmaf(ub3(q), x[3], acc);
     return acc;
 }
+// acc + sum_b signed_byte_b(q) * x[b]
+__device__ __forceinline__ float sdot4(uint32_t q, const float *x, float acc) {
+    acc = fmaf(sb0(q), x[0], acc);
+    acc = fmaf(sb1(q), x[1], acc);
+    acc = fmaf(sb2(q), x[2], acc);
+    acc = fmaf(sb3(q), x[3], acc);
+    return acc;
+}
+__device__ __forceinline__ void put4(float *d, f32x4 v) {
+    d[0] = v.x;
+    d[1] = v.y;
+    d[2] = v.z;
+    d[3] = v.w;
+}
+
+// Each unit type below provides
+//   Raw                 registers holding one unit of one row
+//   load_lds / load     read them from the staged row in LDS / from global memory
+//   X, x4_index, x4_slot, put_x, finish_x
+//                       the unit's 64 x values as 16 float4 pieces: piece i of
+//                       unit u is float4 number x4_index(u, i) of x; x4_slot
+//                       is the inverse
+//   dot                 the unit's contribution to the row's dot product
 
 // ------------------------------------------------------------ Q4_0 units
-// A unit is two consecutive 18-byte blocks (36 bytes, dword aligned when the
-// row is, i.e. when k % 64 == 0). Block layout: f16 d, 16 code bytes; element
-// e < 16 is the low nibble of byte e, e >= 16 the high nibble of byte e-16;
-// value d*(q-8). The signed code q-8 is the 4-bit two's-complement reading of
-// q^8: each nibble is XORed with 8 and moved to the top of its byte, where a
-// sign-extending byte conversion yields 16*(q-8) exactly. Summing signed
-// codes keeps the rounding error proportional to sum|w*x| (an all-8 block
-// gives exactly 0).
+// A unit is two consecutive 18-byte blocks. Block layout: f16 d, 16 code
+// bytes; element e < 16 is the low nibble of byte e, e >= 16 the high nibble
+// of byte e-16; value d*(q-8). The signed code q-8 is the 4-bit two's
+// complement reading of q^8: each nibble is XORed with 8 and moved to the top
+// of its byte, where a sign-extending byte conversion yields 16*(q-8)
+// exactly. Summing signed codes keeps the rounding error proportional to
+// sum|w*x| (an all-8 block gives exactly 0).
 struct UQ4_0 {
-    struct Raw { u32x4 a, b; uint32_t c; };
+    struct Raw { u32x4 q0, q1; uint32_t d0, d1; };
     struct X { float lo[2][16], hi[2][16]; };
-    static __device__ __forceinline__ void load(Raw &r, const uint8_t *row, int u, int) {
-        const uint8_t *p = row + 36 * u;
-        r.a = ld16a4(p);
-        r.b = ld16a4(p + 16);
-        r.c = ld4(p + 32);
+    // The unit starts dword aligned (rows are 36*U bytes and every batch
+    // starts at a dword multiple in LDS): nine aligned dwords hold both blocks.
+    static __device__ __forceinline__ void load_lds(Raw &r, const uint8_t *row, int u) {
+        const uint32_t *w = (const uint32_t *)(row + 36 * u);
+        uint32_t e[9];
+#pragma unroll
+        for (int i = 0; i < 9; i++) e[i] = w[i];
+        r.d0 = e[0] & 0xffffu;
+        r.q0 = u32x4{__builtin_amdgcn_alignbyte(e[1], e[0], 2),
+                     __builtin_amdgcn_alignbyte(e[2], e[1], 2),
+                     __builtin_amdgcn_alignbyte(e[3], e[2], 2),
+                     __builtin_amdgcn_alignbyte(e[4], e[3], 2)};
+        r.d1 = e[4] >> 16;
+        r.q1 = u32x4{e[5], e[6], e[7], e[8]};
     }
-    // x of unit u as 16 float4 pieces: piece i is x4[16u + i]
     static __device__ __forceinline__ int x4_index(int u, int i, int) { return 16 * u + i; }
     static __device__ __forceinline__ void x4_slot(int q, int, int &u, int &i) {
         u = q >> 4;
@@ -124,12 +167,11 @@ struct UQ4_0 {
     }
     static __device__ __forceinline__ void put_x(X &x, int i, f32x4 v) {
         const int b = i >> 3, j = i & 7;
-        float *d = j < 4 ? &x.lo[b][4 * j] : &x.hi[b][4 * (j - 4)];
-        d[0] = v.x; d[1] = v.y; d[2] = v.z; d[3] = v.w;
+        put4(j < 4 ? &x.lo[b][4 * j] : &x.hi[b][4 * (j - 4)], v);
     }
     static __device__ __forceinline__ void finish_x(X &) {}
-    static __device__ __forceinline__ float block(const uint32_t q[4], uint32_t dbits,
-                                                  const X &x, int b) {
+    static __device__ __forceinline__ float block(u32x4 qv, uint32_t dbits, const X &x, int b) {
+        const uint32_t q[4] = {qv.x, qv.y, qv.z, qv.w};
         float acc_lo = 0.f, acc_hi = 0.f;
 #pragma unroll
         for (int j = 0; j < 4; j++) {
@@ -142,14 +184,7 @@ struct UQ4_0 {
         return (f16lo(dbits) * 0.0625f) * (acc_lo + acc_hi);
     }
     static __device__ __forceinline__ float dot(const Raw &r, const X &x, int) {
-        uint32_t e[9] = {r.a.x, r.a.y, r.a.z, r.a.w, r.b.x, r.b.y, r.b.z, r.b.w, r.c};
-        uint32_t q0[4], q1[4];
-#pragma unroll
-        for (int j = 0; j < 4; j++) {
-            q0[j] = __builtin_amdgcn_alignbyte(e[j + 1], e[j], 2); // bytes 2..17
-            q1[j] = e[5 + j];                                      // bytes 20..35
-        }
-        return block(q0, e[0], x, 0) + block(q1, e[4] >> 16, x, 1);
+        return block(r.q0, r.d0, x, 0) + block(r.q1, r.d1, x, 1);
     }
 };
 
@@ -160,22 +195,20 @@ struct UQ4_0 {
 struct UQ4_K {
     struct Raw { u32x4 hd, q0, q1; };
     struct X { float lo[32], hi[32]; float slo, shi; };
-    static __device__ __forceinline__ void load(Raw &r, const uint8_t *row, int u, int) {
+    static __device__ __forceinline__ void load_lds(Raw &r, const uint8_t *row, int u) {
         const uint8_t *sb = row + 144 * (u >> 2);
-        int c = u & 3;
-        r.hd = ld16(sb);
-        r.q0 = ld16(sb + 16 + 32 * c);
-        r.q1 = ld16(sb + 32 + 32 * c);
+        const int c = u & 3;
+        r.hd = lds16(sb);
+        r.q0 = lds16(sb + 16 + 32 * c);
+        r.q1 = lds16(sb + 32 + 32 * c);
     }
-    // x of unit u (weights 64u .. 64u+63) as 16 float4 pieces
     static __device__ __forceinline__ int x4_index(int u, int i, int) { return 16 * u + i; }
     static __device__ __forceinline__ void x4_slot(int q, int, int &u, int &i) {
         u = q >> 4;
         i = q & 15;
     }
     static __device__ __forceinline__ void put_x(X &x, int i, f32x4 v) {
-        float *d = i < 8 ? &x.lo[4 * i] : &x.hi[4 * (i - 8)];
-        d[0] = v.x; d[1] = v.y; d[2] = v.z; d[3] = v.w;
+        put4(i < 8 ? &x.lo[4 * i] : &x.hi[4 * (i - 8)], v);
     }
     static __device__ __forceinline__ void finish_x(X &x) {
         float a = 0.f, b = 0.f;
@@ -192,17 +225,17 @@ struct UQ4_K {
                                                      int s, uint32_t &sc, uint32_t &mn) {
         const bool low = s < 4;
         const int t = 8 * (s & 3);
-        uint32_t a = low ? d1 : d3, b = low ? d2 : d3;
-        int sa = t, sb = low ? t : t + 4, hs = low ? t + 4 : t + 6;
+        const uint32_t a = low ? d1 : d3, b = low ? d2 : d3;
+        const int sa = t, sb = low ? t : t + 4, hs = low ? t + 4 : t + 6;
         sc = ((a >> sa) & 15u) | (((d1 >> hs) & 3u) << 4);
         mn = ((b >> sb) & 15u) | (((d2 >> hs) & 3u) << 4);
     }
     static __device__ __forceinline__ float dot(const Raw &r, const X &x, int u) {
-        uint32_t q[8] = {r.q0.x, r.q0.y, r.q0.z, r.q0.w, r.q1.x, r.q1.y, r.q1.z, r.q1.w};
+        const uint32_t q[8] = {r.q0.x, r.q0.y, r.q0.z, r.q0.w, r.q1.x, r.q1.y, r.q1.z, r.q1.w};
         float acc_lo = 0.f, acc_hi = 0.f;
 #pragma unroll
         for (int i = 0; i < 8; i++) {
-            uint32_t lo = opaque(q[i] & 0x0f0f0f0fu), hi = opaque(q[i] & 0xf0f0f0f0u);
+            const uint32_t lo = opaque(q[i] & 0x0f0f0f0fu), hi = opaque(q[i] & 0xf0f0f0f0u);
             acc_lo = dot4(lo, &x.lo[4 * i], acc_lo);
             acc_hi = dot4(hi, &x.hi[4 * i], acc_hi); // 16x the high nibble
         }
@@ -224,39 +257,24 @@ struct UQ4_K {
 // ql[64h + 16lq + i] (g = 0 low nibble, g = 2 high nibble) and
 // ql[64h + 32 + 16lq + i] (g = 1, 3), their top 2 bits are bits 2g..2g+1 of
 // qh[32h + 16lq + i], and their scales are the int8 scales[8h + 2g + lq].
-// Super-blocks are 210 bytes, so a field may start 2 bytes off a dword
-// boundary: each 16-byte field is loaded as the covering dwords and shifted
-// into place with v_alignbyte_b32 (every load stays inside its super-block).
-// The signed code q-32 is the 6-bit two's-complement reading of q^32: the
-// high 2-bit fields are XORed with 0b10, the 6-bit code is assembled in the
-// top of its byte, and a sign-extending byte conversion yields 4*(q-32).
+// Super-blocks are 210 bytes, so fields may sit 2 bytes off a dword
+// boundary (read through lds16u/lds8u). The signed code q-32 is the 6-bit
+// two's-complement reading of q^32: the high 2-bit fields are XORed with
+// 0b10, the 6-bit code is assembled in the top of its byte, and a
+// sign-extending byte conversion yields 4*(q-32).
 struct UQ6_K {
-    struct Raw { u32x4 a, b, h; uint32_t a4, b4, h4; u32x2 s01; uint32_t s2, d, sh; };
+    struct Raw { u32x4 a, b, h; u32x2 s; uint32_t d; };
     struct X { float v[4][16]; };
-    static __device__ __forceinline__ void load(Raw &r, const uint8_t *row, int u, int) {
+    static __device__ __forceinline__ void load_lds(Raw &r, const uint8_t *row, int u) {
         const uint8_t *o = row + 210 * (u >> 2);
         const int h = (u >> 1) & 1, lq = u & 1;
-        const int fa = 64 * h + 16 * lq, fh = 128 + 32 * h + 16 * lq, fs = 192 + 8 * h;
-        // sh = 0 or 2. al = o - sh is dword aligned; every field's covering
-        // dwords start at al + offset, and the dword after each 16-byte field
-        // (needed only when sh = 2) sits at o + sh + offset + 12, which for
-        // sh = 0 re-reads the field's last dword. Nothing reaches past the
-        // super-block's last byte.
-        const uint32_t sh = (uint32_t)(uintptr_t)o & 3u;
-        const uint8_t *al = o - sh;
-        const uint8_t *tl = o + sh;
-        r.sh = sh;
-        r.a = ld16a4(al + fa);
-        r.a4 = ld4(tl + fa + 12);
-        r.b = ld16a4(al + fa + 32);
-        r.b4 = ld4(tl + fa + 44);
-        r.h = ld16a4(al + fh);
-        r.h4 = ld4(tl + fh + 12);
-        r.s01 = ld8a4(al + fs);
-        r.s2 = ld4(tl + fs + 4);
-        r.d = ld2(o + 208);
+        r.a = lds16u(o + 64 * h + 16 * lq);
+        r.b = lds16u(o + 64 * h + 32 + 16 * lq);
+        r.h = lds16u(o + 128 + 32 * h + 16 * lq);
+        r.s = lds8u(o + 192 + 8 * h);
+        r.d = lds2(o + 208);
     }
-    // x of unit u: piece i = 4g + i4 holds weights 128h + 32g + 16lq + 4i4 .. +3
+    // piece i = 4g + i4 holds weights 128h + 32g + 16lq + 4i4 .. +3
     static __device__ __forceinline__ int x4_index(int u, int i, int) {
         return 64 * (u >> 2) + 32 * ((u >> 1) & 1) + 8 * (i >> 2) + 4 * (u & 1) + (i & 3);
     }
@@ -265,24 +283,13 @@ struct UQ6_K {
         i = 4 * ((q >> 3) & 3) + (q & 3);
     }
     static __device__ __forceinline__ void put_x(X &x, int i, f32x4 v) {
-        float *d = &x.v[i >> 2][4 * (i & 3)];
-        d[0] = v.x; d[1] = v.y; d[2] = v.z; d[3] = v.w;
+        put4(&x.v[i >> 2][4 * (i & 3)], v);
     }
     static __device__ __forceinline__ void finish_x(X &) {}
     static __device__ __forceinline__ float dot(const Raw &r, const X &x, int u) {
-        const uint32_t sh = r.sh;
-        uint32_t A[4], B[4], H[4];
-        const uint32_t av[5] = {r.a.x, r.a.y, r.a.z, r.a.w, r.a4};
-        const uint32_t bv[5] = {r.b.x, r.b.y, r.b.z, r.b.w, r.b4};
-        const uint32_t hv[5] = {r.h.x, r.h.y, r.h.z, r.h.w, r.h4};
-#pragma unroll
-        for (int j = 0; j < 4; j++) {
-            A[j] = __builtin_amdgcn_alignbyte(av[j + 1], av[j], sh);
-            B[j] = __builtin_amdgcn_alignbyte(bv[j + 1], bv[j], sh);
-            H[j] = __builtin_amdgcn_alignbyte(hv[j + 1], hv[j], sh);
-        }
-        const uint32_t S0 = __builtin_amdgcn_alignbyte(r.s01.y, r.s01.x, sh);
-        const uint32_t S1 = __builtin_amdgcn_alignbyte(r.s2, r.s01.y, sh);
+        const uint32_t A[4] = {r.a.x, r.a.y, r.a.z, r.a.w};
+        const uint32_t B[4] = {r.b.x, r.b.y, r.b.z, r.b.w};
+        const uint32_t H[4] = {r.h.x, r.h.y, r.h.z, r.h.w};
         float acc[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int j = 0; j < 4; j++) {
@@ -300,10 +307,10 @@ struct UQ6_K {
         const int lq8 = 8 * (u & 1);
         const float d = f16lo(r.d) * 0.25f;
         // the scale bytes are signed: extract with sign extension, convert as int
-        const float s0 = (float)(int)__builtin_amdgcn_sbfe((int)S0, lq8, 8);
-        const float s1 = (float)(int)__builtin_amdgcn_sbfe((int)S0, lq8 + 16, 8);
-        const float s2 = (float)(int)__builtin_amdgcn_sbfe((int)S1, lq8, 8);
-        const float s3 = (float)(int)__builtin_amdgcn_sbfe((int)S1, lq8 + 16, 8);
+        const float s0 = (float)(int)__builtin_amdgcn_sbfe((int)r.s.x, lq8, 8);
+        const float s1 = (float)(int)__builtin_amdgcn_sbfe((int)r.s.x, lq8 + 16, 8);
+        const float s2 = (float)(int)__builtin_amdgcn_sbfe((int)r.s.y, lq8, 8);
+        const float s3 = (float)(int)__builtin_amdgcn_sbfe((int)r.s.y, lq8 + 16, 8);
         float r0 = (d * s0) * acc[0];
         r0 = fmaf(d * s1, acc[1], r0);
         r0 = fmaf(d * s2, acc[2], r0);
@@ -314,7 +321,7 @@ struct UQ6_K {
 // ------------------------------------------------------- F16 / BF16 units
 // A unit is the eight 8-weight chunks u, u+U, ..., u+7U of the row (16 bytes
 // each), so that for a fixed chunk index the lanes of a slot read one
-// contiguous span.
+// contiguous span straight from global memory.
 template <bool BF>
 struct UHalf {
     struct Raw { u32x4 c[8]; };
@@ -323,7 +330,7 @@ struct UHalf {
 #pragma unroll
         for (int c = 0; c < 8; c++) r.c[c] = ld16(row + 16 * (u + U * c));
     }
-    // x of unit u: piece i = 2c + hf holds weights 8(u + cU) + 4hf .. +3
+    // piece i = 2c + hf holds weights 8(u + cU) + 4hf .. +3
     static __device__ __forceinline__ int x4_index(int u, int i, int U) {
         return 2 * (u + U * (i >> 1)) + (i & 1);
     }
@@ -334,8 +341,7 @@ struct UHalf {
         i = 2 * c + (q & 1);
     }
     static __device__ __forceinline__ void put_x(X &x, int i, f32x4 v) {
-        float *d = &x.v[i >> 1][4 * (i & 1)];
-        d[0] = v.x; d[1] = v.y; d[2] = v.z; d[3] = v.w;
+        put4(&x.v[i >> 1][4 * (i & 1)], v);
     }
     static __device__ __forceinline__ void finish_x(X &) {}
     static __device__ __forceinline__ float dot(const Raw &r, const X &x, int) {
@@ -361,7 +367,15 @@ struct UHalf {
     }
 };
 
-// ------------------------------------------------------------- reduction
+// ------------------------------------------------------ shared device code
+// Workgroup barrier that orders LDS only: global loads in flight (the next
+// batch of weights) are not drained, unlike __syncthreads().
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // Sum over aligned groups of G lanes (G a power of two <= 16); every lane of
 // a group ends with the group sum. Order of additions is fixed.
 template <int CTRL>
@@ -377,185 +391,383 @@ __device__ __forceinline__ float group_sum(float v, int G) {
     return v;
 }
 
-// ---------------------------------------------------------------- kernel
-// Workgroup barrier that orders LDS only: global loads in flight (the next
-// batch of weights) are not drained, unlike __syncthreads().
-__device__ __forceinline__ void lds_barrier() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
-
-template <class F, int MT, int UPL, int RB>
-__global__ __launch_bounds__(512) void qmv_gemv(const uint8_t *__restrict__ W,
-                                                 const float *__restrict__ x,
-                                                 float *__restrict__ y, int64_t k, int64_t n,
-                                                 int64_t row_bytes, int64_t j_start,
-                                                 int64_t j_end, int accumulate, int U, int L,
-                                                 int P, int G, int x_in_lds) {
-    extern __shared__ float smem[];
-    const int tid = threadIdx.x;
-    const int T = blockDim.x;
-    const int slot = tid / L;
-    const int lane = tid - slot * L;
-    const int NG = L / G;
-    const int64_t rows_per_batch = (int64_t)P * RB;
-    const int64_t stride = (int64_t)gridDim.x * rows_per_batch;
-    const uint8_t *Wslot = W + (int64_t)slot * row_bytes;
-
+// Lane geometry common to both kernels.
+template <int UPL>
+struct Lanes {
+    int tid, T, slot, lane, NG;
     int uid[UPL];  // units owned by this lane
-    int ulod[UPL]; // unit actually loaded: padding lanes re-read a valid unit
+    int ulod[UPL]; // unit actually read: padding lanes re-read a valid unit
     bool uvalid[UPL];
+    __device__ __forceinline__ Lanes(int U, int L, int G) {
+        tid = threadIdx.x;
+        T = blockDim.x;
+        slot = tid / L;
+        lane = tid - slot * L;
+        NG = L / G;
 #pragma unroll
-    for (int i = 0; i < UPL; i++) {
-        uid[i] = lane + i * L;
-        uvalid[i] = uid[i] < U;
-        ulod[i] = uvalid[i] ? uid[i] : U - 1;
-    }
-
-    // 1. x, first part: coalesced float4 loads into registers (4 per thread;
-    // indexes clamped so the loads are unconditional).
-    const int n4 = (int)(k >> 2);    // float4 pieces per token
-    const int nt4 = n4 * MT;         // for all tokens
-    const f32x4 *x4 = (const f32x4 *)x;
-    f32x4 xa[4];
-    if (x_in_lds) {
-#pragma unroll
-        for (int s = 0; s < 4; s++) {
-            const int q = tid + s * T;
-            xa[s] = x4[q < nt4 ? q : nt4 - 1];
+        for (int i = 0; i < UPL; i++) {
+            uid[i] = lane + i * L;
+            uvalid[i] = uid[i] < U;
+            ulod[i] = uvalid[i] ? uid[i] : U - 1;
         }
     }
+};
 
-    // 2. weight loads of the first batch (every workgroup has one: the grid
-    // never exceeds the batch count). Rows are base + r*P + slot: the r*P
-    // part is uniform across the workgroup (scalar address arithmetic), the
-    // slot part a per-lane constant. Loads are branch-free: a row past j_end
-    // re-reads row j_end-1 and its result is dropped, which lets the compiler
-    // count outstanding loads exactly.
+// x, first part: coalesced float4 loads into registers (4 per thread; the
+// index is clamped so the loads are unconditional and their count is known).
+__device__ __forceinline__ void x_prefetch(const float *x, int nt4, int tid, int T,
+                                           f32x4 xa[4]) {
+    const f32x4 *x4 = (const f32x4 *)x;
+#pragma unroll
+    for (int s = 0; s < 4; s++) {
+        const int q = tid + s * T;
+        xa[s] = x4[q < nt4 ? q : nt4 - 1];
+    }
+}
+
+// x into LDS, transposed so that piece i of unit u of token t sits at
+// [t*n4 + i*U + u]: the per-lane reads are then consecutive across lanes.
+template <class F>
+__device__ __forceinline__ void x_to_lds(const float *x, f32x4 *xl, int n4, int nt4, int U,
+                                         int tid, int T, const f32x4 xa[4]) {
+    auto put = [&](int q, f32x4 v) {
+        const int t = q / n4, r = q - t * n4;
+        int u, i;
+        F::x4_slot(r, U, u, i);
+        xl[t * n4 + i * U + u] = v;
+    };
+#pragma unroll
+    for (int s = 0; s < 4; s++)
+        if (tid + s * T < nt4) put(tid + s * T, xa[s]);
+    const f32x4 *x4 = (const f32x4 *)x;
+    for (int q = tid + 4 * T; q < nt4; q += T) put(q, x4[q]);
+}
+
+template <class F, int MT, int UPL>
+__device__ __forceinline__ void x_units_from_lds(typename F::X (&xu)[MT][UPL], const f32x4 *xl,
+                                                 int n4, int U, const int (&ulod)[UPL]) {
+#pragma unroll
+    for (int i = 0; i < UPL; i++)
+#pragma unroll
+        for (int t = 0; t < MT; t++) {
+#pragma unroll
+            for (int p = 0; p < 16; p++) F::put_x(xu[t][i], p, xl[t * n4 + p * U + ulod[i]]);
+            F::finish_x(xu[t][i]);
+        }
+}
+
+// x straight from global memory, one float at a time (any 4-byte alignment).
+template <class F, int MT, int UPL>
+__device__ __forceinline__ void x_units_from_global(typename F::X (&xu)[MT][UPL],
+                                                    const float *x, int64_t k, int U,
+                                                    const int (&ulod)[UPL]) {
+#pragma unroll
+    for (int i = 0; i < UPL; i++)
+#pragma unroll
+        for (int t = 0; t < MT; t++) {
+#pragma unroll
+            for (int p = 0; p < 16; p++) {
+                const float *src = x + t * k + 4 * F::x4_index(ulod[i], p, U);
+                F::put_x(xu[t][i], p, f32x4{src[0], src[1], src[2], src[3]});
+            }
+            F::finish_x(xu[t][i]);
+        }
+}
+
+// Outputs of a batch are numbered q = (slot*RB + r)*MT + t (row base + r*P +
+// slot, token t). With accumulate, the old values of y are read one batch
+// ahead, together with that batch's weights, and parked in LDS (ybuf): a
+// global read issued later than the weight prefetch would make the in-order
+// load counter drain that prefetch.
+template <int MT, int RB>
+struct YPrefetch {
+    float v[2];
+    __device__ __forceinline__ void fetch(const float *y, int64_t n, int64_t b, int64_t j_end,
+                                          int P, int tid, int T) {
+        const int nq = P * RB * MT;
+#pragma unroll
+        for (int s = 0; s < 2; s++) {
+            int q = tid + s * T;
+            q = q < nq ? q : nq - 1;
+            const int t = q % MT, rr = q / MT;
+            const int64_t j = b + (int64_t)(rr % RB) * P + rr / RB;
+            v[s] = y[t * n + (j < j_end ? j : j_end - 1)];
+        }
+    }
+    __device__ __forceinline__ void stash(float *ybuf, int P, int tid, int T) const {
+        const int nq = P * RB * MT;
+#pragma unroll
+        for (int s = 0; s < 2; s++)
+            if (tid + s * T < nq) ybuf[tid + s * T] = v[s];
+    }
+};
+
+// Store one output (ybuf holds the old values when accumulating).
+__device__ __forceinline__ void store_y(float *dst, float v, int accumulate, const float *ybuf,
+                                        int q) {
+    *dst = accumulate ? ybuf[q] + v : v;
+}
+
+// Sum the NG group partials of every (row, token) of a batch and store them.
+template <int MT, int RB>
+__device__ __forceinline__ void finish_batch(const float *rb, const float *ybuf, int NG, int P,
+                                             int tid, int T, int64_t base, int64_t j_end,
+                                             float *y, int64_t n, int accumulate) {
+    for (int q = tid; q < P * RB * MT; q += T) {
+        const int t = q % MT;
+        const int rr = q / MT; // slot * RB + r
+        const int s = rr / RB, r = rr % RB;
+        const int64_t j = base + (int64_t)r * P + s;
+        if (j < j_end) {
+            const float *src = rb + q * NG;
+            float v = src[0];
+            for (int g = 1; g < NG; g++) v += src[g];
+            store_y(y + t * n + j, v, accumulate, ybuf, q);
+        }
+    }
+}
+
+// DPP-reduce the batch partials, then either store (one group per row) or
+// leave the group sums in LDS for finish_batch.
+template <int MT, int RB, int UPL>
+__device__ __forceinline__ void reduce_batch(float (&part)[RB][MT], const Lanes<UPL> &ln, int G,
+                                             int P, float *rb, const float *ybuf, int64_t base,
+                                             int64_t j_end, float *y, int64_t n,
+                                             int accumulate) {
+#pragma unroll
+    for (int r = 0; r < RB; r++)
+#pragma unroll
+        for (int t = 0; t < MT; t++) part[r][t] = group_sum(part[r][t], G);
+    if (ln.NG == 1) {
+        if (ln.lane == 0) {
+#pragma unroll
+            for (int r = 0; r < RB; r++) {
+                const int64_t j = base + (int64_t)r * P + ln.slot;
+                if (j < j_end) {
+#pragma unroll
+                    for (int t = 0; t < MT; t++)
+                        store_y(y + t * n + j, part[r][t], accumulate, ybuf,
+                                (ln.slot * RB + r) * MT + t);
+                }
+            }
+        }
+    } else if ((ln.lane & (G - 1)) == 0) {
+        const int g = ln.lane / G;
+#pragma unroll
+        for (int r = 0; r < RB; r++)
+#pragma unroll
+            for (int t = 0; t < MT; t++)
+                rb[((ln.slot * RB + r) * MT + t) * ln.NG + g] = part[r][t];
+    }
+}
+
+// ------------------------------------------------------- direct kernel
+// F16/BF16: every lane loads its units straight from global memory; the next
+// batch's loads are issued before the current batch is reduced. XL: x goes
+// through LDS (else each lane reads its x units from global memory).
+template <class F, int MT, int UPL, int RB, bool XL>
+__global__ __launch_bounds__(512) void qmv_gemv_direct(const uint8_t *__restrict__ W,
+                                                        const float *__restrict__ x,
+                                                        float *__restrict__ y, int64_t k,
+                                                        int64_t n, int64_t row_bytes,
+                                                        int64_t j_start, int64_t j_end,
+                                                        int accumulate, int U, int L, int P,
+                                                        int G, int) {
+    extern __shared__ float smem[];
+    const Lanes<UPL> ln(U, L, G);
+    const int64_t rows_per_batch = (int64_t)P * RB;
+    const int64_t stride = (int64_t)gridDim.x * rows_per_batch;
+    const uint8_t *Wslot = W + (int64_t)ln.slot * row_bytes;
+    const int n4 = (int)(k >> 2), nt4 = n4 * MT;
+    const int nq = P * RB * MT;
+    float *red = smem + (XL ? k * MT : 0); // 2 x nq*NG group sums, then 2 x nq old y
+    float *ybuf = red + 2 * nq * ln.NG;
+
+    typename F::X xu[MT][UPL];
+    if (!XL) x_units_from_global<F, MT, UPL>(xu, x, k, U, ln.ulod);
+    f32x4 xa[4];
+    if (XL) x_prefetch(x, nt4, ln.tid, ln.T, xa);
+
+    // Rows are base + r*P + slot: the r*P part is uniform across the
+    // workgroup (scalar address arithmetic), the slot part a per-lane
+    // constant. Loads are branch-free: a row past j_end re-reads row j_end-1
+    // and its result is dropped, which lets the compiler count outstanding
+    // loads exactly.
     typename F::Raw raw[RB][UPL];
+    YPrefetch<MT, RB> yp;
     int64_t base = j_start + (int64_t)blockIdx.x * rows_per_batch;
     const uint8_t *last_row = W + (j_end - 1) * row_bytes;
     auto issue = [&](int64_t b) {
 #pragma unroll
         for (int r = 0; r < RB; r++) {
             const int64_t jr = b + (int64_t)r * P;
-            const uint8_t *row = jr + slot < j_end ? Wslot + jr * row_bytes : last_row;
+            const uint8_t *row = jr + ln.slot < j_end ? Wslot + jr * row_bytes : last_row;
 #pragma unroll
-            for (int i = 0; i < UPL; i++) F::load(raw[r][i], row, ulod[i], U);
+            for (int i = 0; i < UPL; i++) F::load(raw[r][i], row, ln.ulod[i], U);
         }
+        if (accumulate) yp.fetch(y, n, b, j_end, P, ln.tid, ln.T);
     };
-    issue(base);
+    issue(base); // every workgroup has a first batch: the grid never exceeds the batch count
 
-    // 3. x into LDS, transposed so that piece i of unit u sits at [i*U + u]:
-    // the per-lane reads below are then consecutive across lanes (no bank
-    // conflicts). The first 4T pieces come from registers, the rest (long
-    // rows only) are copied here.
-    typename F::X xu[MT][UPL];
-    f32x4 *xl = (f32x4 *)smem;
-    if (x_in_lds) {
-        auto put = [&](int q, f32x4 v) {
-            const int t = q / n4, r = q - t * n4;
-            int u, i;
-            F::x4_slot(r, U, u, i);
-            xl[t * n4 + i * U + u] = v;
-        };
-#pragma unroll
-        for (int s = 0; s < 4; s++)
-            if (tid + s * T < nt4) put(tid + s * T, xa[s]);
-        for (int q = tid + 4 * T; q < nt4; q += T) put(q, x4[q]);
+    if (XL) {
+        f32x4 *xl = (f32x4 *)smem;
+        x_to_lds<F>(x, xl, n4, nt4, U, ln.tid, ln.T, xa);
         lds_barrier();
-#pragma unroll
-        for (int i = 0; i < UPL; i++)
-#pragma unroll
-            for (int t = 0; t < MT; t++) {
-#pragma unroll
-                for (int p = 0; p < 16; p++)
-                    F::put_x(xu[t][i], p, xl[t * n4 + p * U + ulod[i]]);
-                F::finish_x(xu[t][i]);
-            }
-    } else {
-        // x straight from global memory, one float at a time (any 4-byte alignment)
-#pragma unroll
-        for (int i = 0; i < UPL; i++)
-#pragma unroll
-            for (int t = 0; t < MT; t++) {
-#pragma unroll
-                for (int p = 0; p < 16; p++) {
-                    const float *src = x + t * k + 4 * F::x4_index(ulod[i], p, U);
-                    F::put_x(xu[t][i], p, f32x4{src[0], src[1], src[2], src[3]});
-                }
-                F::finish_x(xu[t][i]);
-            }
+        x_units_from_lds<F, MT, UPL>(xu, xl, n4, U, ln.ulod);
     }
-    float *red = smem + (x_in_lds ? k * MT : 0);
-    const int red_half = P * RB * MT * NG;
     int buf = 0;
 
-    // 4. stream: decode batch i, issue the loads of batch i+1, then reduce
-    // and store batch i while those loads are in flight.
     for (; base < j_end; base += stride) {
         float part[RB][MT];
 #pragma unroll
         for (int r = 0; r < RB; r++) {
-            const bool live = base + (int64_t)r * P + slot < j_end;
+            const bool live = base + (int64_t)r * P + ln.slot < j_end;
 #pragma unroll
             for (int t = 0; t < MT; t++) {
                 float v = 0.f;
                 if (live) {
 #pragma unroll
                     for (int i = 0; i < UPL; i++)
-                        if (uvalid[i]) v += F::dot(raw[r][i], xu[t][i], uid[i]);
+                        if (ln.uvalid[i]) v += F::dot(raw[r][i], xu[t][i], ln.uid[i]);
                 }
                 part[r][t] = v;
             }
         }
+        float *yb = ybuf + buf * nq;
+        if (accumulate) yp.stash(yb, P, ln.tid, ln.T);
         if (base + stride < j_end) issue(base + stride);
-#pragma unroll
-        for (int r = 0; r < RB; r++)
-#pragma unroll
-            for (int t = 0; t < MT; t++) part[r][t] = group_sum(part[r][t], G);
-        if (NG == 1) {
-            if (lane == 0) {
-#pragma unroll
-                for (int r = 0; r < RB; r++) {
-                    const int64_t j = base + (int64_t)r * P + slot;
-                    if (j < j_end) {
-#pragma unroll
-                        for (int t = 0; t < MT; t++) {
-                            float *dst = y + t * n + j;
-                            *dst = accumulate ? *dst + part[r][t] : part[r][t];
-                        }
-                    }
-                }
-            }
-        } else {
-            float *rb = red + buf * red_half;
-            if ((lane & (G - 1)) == 0) {
-                const int g = lane / G;
-#pragma unroll
-                for (int r = 0; r < RB; r++)
-#pragma unroll
-                    for (int t = 0; t < MT; t++)
-                        rb[((slot * RB + r) * MT + t) * NG + g] = part[r][t];
-            }
+        float *rb = red + buf * nq * ln.NG;
+        if (ln.NG == 1 && accumulate) lds_barrier();
+        reduce_batch<MT, RB, UPL>(part, ln, G, P, rb, yb, base, j_end, y, n, accumulate);
+        if (ln.NG > 1) {
             lds_barrier();
-            for (int q = tid; q < P * RB * MT; q += blockDim.x) {
-                const int t = q % MT;
-                const int rr = q / MT; // slot * RB + r
-                const int s = rr / RB, r = rr % RB;
-                const int64_t j = base + (int64_t)r * P + s;
-                if (j < j_end) {
-                    const float *src = rb + q * NG;
-                    float v = src[0];
-                    for (int g = 1; g < NG; g++) v += src[g];
-                    float *dst = y + t * n + j;
-                    *dst = accumulate ? *dst + v : v;
-                }
-            }
-            buf ^= 1;
+            finish_batch<MT, RB>(rb, yb, ln.NG, P, ln.tid, ln.T, base, j_end, y, n,
+                                 accumulate);
         }
+        buf ^= 1;
     }
+}
+
+// ------------------------------------------------------- staged kernel
+// Block formats. The byte range of a batch, [base*row_bytes,
+// end*row_bytes), is copied in 16-byte pieces aligned down to 16 bytes (so
+// up to 15 bytes before it and, at the very end of W, up to 15 bytes after it
+// inside the same 16-byte granule, are read and ignored; W is 16-byte
+// aligned, so such a granule never crosses a page). The copy goes straight
+// from memory into LDS (buffer_load_dwordx4 ... lds): each wave instruction
+// moves one contiguous kilobyte, no registers hold the data, and the
+// compiler does not make the decode's LDS reads of the other buffer wait for
+// it. The batch start is the scalar base of a buffer descriptor sized to the
+// batch; piece offsets are per-lane constants clamped to the last piece (the
+// descriptor's range check is a second guard). The copy of batch i+1 runs
+// while batch i is decoded and is waited for at the end-of-batch barrier.
+// Every wave writes all its NPT kilobyte slots, so a buffer is NPT*T*16
+// bytes. XL: x goes through LDS.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t batch_rsrc(const uint8_t *p, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc((void *)p, (short)0, bytes, 0x00020000);
+}
+
+// Single-token, one-row-per-slot instances fit in 128 registers without
+// spilling, i.e. 4 waves per SIMD; the others are left to the compiler.
+template <int MT, int UPL, int RB, int NPT>
+struct StagedOccupancy {
+    static constexpr int waves = (MT == 1 && UPL == 1 && RB == 1 && NPT <= 4) ? 4 : 1;
+};
+
+template <class F, int MT, int UPL, int RB, int NPT, bool XL>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(
+    StagedOccupancy<MT, UPL, RB, NPT>::waves))) void qmv_gemv_staged(const uint8_t *__restrict__ W,
+                                                                  const float *__restrict__ x,
+                                                                  float *__restrict__ y,
+                                                                  int64_t k, int64_t n,
+                                                                  int64_t row_bytes,
+                                                                  int64_t j_start, int64_t j_end,
+                                                                  int accumulate, int U, int L,
+                                                                  int P, int G, int buf_bytes) {
+    extern __shared__ float smem[];
+    const Lanes<UPL> ln(U, L, G);
+    const int64_t rows_per_batch = (int64_t)P * RB;
+    const int64_t stride = (int64_t)gridDim.x * rows_per_batch;
+    const int n4 = (int)(k >> 2), nt4 = n4 * MT;
+    const int nq = P * RB * MT;
+    const int rbytes = (int)row_bytes; // a row of one batch fits in LDS, so in 32 bits
+    const int wave = ln.tid >> 6;
+    // LDS: [x][weight buffer 0][weight buffer 1][2 x group sums][2 x old y]
+    uint8_t *wb = (uint8_t *)(smem + (XL ? k * MT : 0));
+    float *red = (float *)(wb + 2 * buf_bytes);
+    float *ybuf = red + 2 * nq * ln.NG;
+
+    YPrefetch<MT, RB> yp;
+    // Start copying batch b into weight buffer bi (and read its old y).
+    auto copy = [&](int64_t b, int bi) {
+        const int64_t r1 = b + rows_per_batch < j_end ? b + rows_per_batch : j_end;
+        const int64_t s0 = b * row_bytes, s1 = r1 * row_bytes;
+        const int64_t a0 = s0 & ~(int64_t)15;
+        const int np = (int)((((s1 + 15) & ~(int64_t)15) - a0) >> 4);
+        const __amdgpu_buffer_rsrc_t rs = batch_rsrc(W + a0, 16 * np);
+        const int last = 16 * (np - 1);
+        uint8_t *dst = wb + bi * buf_bytes;
+#pragma unroll
+        for (int s = 0; s < NPT; s++) {
+            const int off = 16 * (ln.tid + s * ln.T);
+            // lane l of this wave writes piece s*T + 64*wave + l
+            uint8_t *slot = dst + __builtin_amdgcn_readfirstlane(16 * (s * ln.T + 64 * wave));
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rs, (__attribute__((address_space(3))) void *)slot, 16, off < last ? off : last, 0,
+                0, 2 /* nontemporal */);
+        }
+        if (accumulate) yp.fetch(y, n, b, j_end, P, ln.tid, ln.T);
+    };
+
+    typename F::X xu[MT][UPL];
+    if (!XL) x_units_from_global<F, MT, UPL>(xu, x, k, U, ln.ulod);
+    int64_t base = j_start + (int64_t)blockIdx.x * rows_per_batch;
+    f32x4 xa[4];
+    if (XL) x_prefetch(x, nt4, ln.tid, ln.T, xa);
+    copy(base, 0); // every workgroup has a first batch: the grid never exceeds the batch count
+    f32x4 *xl = (f32x4 *)smem;
+    if (XL) x_to_lds<F>(x, xl, n4, nt4, U, ln.tid, ln.T, xa);
+    if (accumulate) yp.stash(ybuf, P, ln.tid, ln.T);
+    lds_barrier();
+    if (XL) x_units_from_lds<F, MT, UPL>(xu, xl, n4, U, ln.ulod);
+
+    int cur = 0;
+    int64_t prev = -1; // batch whose group sums wait in LDS
+    for (; base < j_end; base += stride) {
+        const int64_t nb = base + stride;
+        if (nb < j_end) copy(nb, cur ^ 1);
+        if (ln.NG > 1 && prev >= 0)
+            finish_batch<MT, RB>(red + (cur ^ 1) * nq * ln.NG, ybuf + (cur ^ 1) * nq, ln.NG,
+                                 P, ln.tid, ln.T, prev, j_end, y, n, accumulate);
+        const int off = (int)((base * row_bytes) & 15);
+        const uint8_t *bl = wb + cur * buf_bytes + off;
+        float part[RB][MT];
+#pragma unroll
+        for (int r = 0; r < RB; r++) {
+            const int rr = r * P + ln.slot;
+            const bool live = base + rr < j_end;
+            const uint8_t *row = bl + (live ? rr : 0) * rbytes;
+#pragma unroll
+            for (int t = 0; t < MT; t++) part[r][t] = 0.f;
+#pragma unroll
+            for (int i = 0; i < UPL; i++) {
+                typename F::Raw raw;
+                F::load_lds(raw, row, ln.ulod[i]);
+#pragma unroll
+                for (int t = 0; t < MT; t++)
+                    if (live && ln.uvalid[i]) part[r][t] += F::dot(raw, xu[t][i], ln.uid[i]);
+            }
+        }
+        reduce_batch<MT, RB, UPL>(part, ln, G, P, red + cur * nq * ln.NG, ybuf + cur * nq, base,
+                                  j_end, y, n, accumulate);
+        if (accumulate && nb < j_end) yp.stash(ybuf + (cur ^ 1) * nq, P, ln.tid, ln.T);
+        lds_barrier(); // also waits for the copy of the next batch
+        prev = base;
+        cur ^= 1;
+    }
+    if (ln.NG > 1 && prev >= 0)
+        finish_batch<MT, RB>(red + (cur ^ 1) * nq * ln.NG, ybuf + (cur ^ 1) * nq, ln.NG, P,
+                             ln.tid, ln.T, prev, j_end, y, n, accumulate);
 }
 
 // -------------------------------------------------------------- planning
@@ -568,14 +780,11 @@ static int gcd_i(int a, int b) {
     return a;
 }
 
-static int default_rb(int fmt) {
-    switch (fmt) {
-    case FMT_Q4_0: return 4;
-    case FMT_Q4_K: return 4;
-    case FMT_Q6_K: return 2;
-    default: return 2; // F16 / BF16: 32 dwords of raw data per unit-row
-    }
+static bool staged_format(int fmt) {
+    return fmt == FMT_Q4_0 || fmt == FMT_Q4_K || fmt == FMT_Q6_K;
 }
+
+static constexpr size_t LDS_BUDGET = 80 * 1024; // weight buffers + reductions
 
 bool plan_gemv(int fmt, int64_t k, int64_t rows, int mt_max, int num_cu, GemvPlan *p) {
     if (k <= 0 || k % 64 != 0) return false;
@@ -592,41 +801,72 @@ bool plan_gemv(int fmt, int64_t k, int64_t rows, int mt_max, int num_cu, GemvPla
     g.P = 64 / gcd_i(g.L, 64);
     while (g.P * g.L * 2 <= 256) g.P *= 2;
     if (g.P * g.L > 512) g.P = 512 / g.L > 0 ? 512 / g.L : 1;
+    // small problems: fewer row slots per workgroup, so that more
+    // workgroups share the rows
+    while (g.P > 1 && g.P * g.L > 64 && (rows + g.P - 1) / g.P < num_cu) g.P /= 2;
     g.T = g.P * g.L;
     g.MT = (g.UPL == 1 && mt_max >= 2) ? 2 : 1;
-    g.RB = default_rb(fmt);
-    int64_t batches = (rows + (int64_t)g.P * g.RB - 1) / ((int64_t)g.P * g.RB);
-    if (batches < 2 * num_cu) {
-        g.RB = 1;
-        batches = (rows + g.P - 1) / g.P;
+    const int64_t rb = fmt == FMT_F16 || fmt == FMT_BF16 ? 2 * k
+                       : fmt == FMT_Q4_0                ? (k / 32) * 18
+                       : fmt == FMT_Q4_K                ? (k / 256) * 144
+                                                        : (k / 256) * 210;
+    g.staged = staged_format(fmt) ? 1 : 0;
+    // Rows per slot per batch: the largest of 2 and 1 that fits the register
+    // budget (staged: at most 8 pieces per thread) and the LDS budget,
+    // keeping at least two batches per compute unit where the rows allow.
+    g.RB = 0;
+    // first within the budget that leaves room for two workgroups per compute
+    // unit; long rows fall back to one workgroup per compute unit
+    for (int attempt = 0; attempt < 2 && g.RB == 0; attempt++)
+    for (int cand = 2; cand >= 1 && g.RB == 0; cand /= 2) {
+        const int64_t budget = attempt == 0 ? (int64_t)LDS_BUDGET : (int64_t)144 * 1024;
+        if (!g.staged && cand > 1 && (g.MT > 1 || g.UPL > 1)) continue; // registers
+        int npt = 0;
+        if (g.staged) {
+            const int64_t pieces = ((int64_t)g.P * cand * rb + 30 + 15) / 16;
+            const int64_t need = (pieces + g.T - 1) / g.T;
+            npt = need <= 2 ? 2 : need <= 4 ? 4 : need <= 8 ? 8 : 0;
+            if (npt == 0) continue;
+        }
+        const int64_t buf = (int64_t)npt * g.T * 16;
+        const int64_t red = (int64_t)2 * g.P * cand * g.MT * (g.NG + 1) * 4;
+        if (2 * buf + red > budget) continue;
+        if ((int64_t)g.P * cand * g.MT > 2 * (int64_t)g.T) continue; // y prefetch: 2 per thread
+        const int64_t batches = (rows + (int64_t)g.P * cand - 1) / ((int64_t)g.P * cand);
+        if (cand > 1 && batches < 2 * (int64_t)num_cu) continue;
+        g.RB = cand;
+        g.npt = npt;
+        g.buf_bytes = (int)buf;
     }
-    // Upper bound here; the launch clamps it to what stays resident
-    // (compute units x workgroups per compute unit).
-    g.grid = (int)(batches < (int64_t)1 << 30 ? batches : (int64_t)1 << 30);
+    if (g.RB == 0) return false;
+    const int64_t batches = (rows + (int64_t)g.P * g.RB - 1) / ((int64_t)g.P * g.RB);
+    // upper bound; the launch clamps it to what stays resident
+    g.grid = (int)(batches < ((int64_t)1 << 30) ? batches : ((int64_t)1 << 30));
     if (g.grid < 1) g.grid = 1;
     g.num_cu = num_cu;
-    // LDS: the reduction buffers, plus x when everything fits in 64 KB
-    // (otherwise each lane loads its x units straight from global memory).
-    const size_t red = g.NG > 1 ? (size_t)2 * g.P * g.RB * g.MT * g.NG * sizeof(float) : 0;
     const size_t xb = (size_t)k * g.MT * sizeof(float);
-    g.x_in_lds = (xb + red <= 64 * 1024) ? 1 : 0;
-    g.lds_bytes = (g.x_in_lds ? xb : 0) + red;
+    const size_t red = (size_t)2 * g.P * g.RB * g.MT * (g.NG + 1) * sizeof(float);
+    const size_t wbuf = (size_t)2 * g.buf_bytes;
+    // x goes through LDS when everything fits in 96 KB; otherwise each lane
+    // reads its x units straight from global memory
+    g.x_in_lds = (xb + wbuf + red <= 96 * 1024) ? 1 : 0;
+    g.lds_bytes = (g.x_in_lds ? xb : 0) + wbuf + red;
+    if (g.lds_bytes > 160 * 1024) return false;
     *p = g;
     return true;
 }
 
-// Resident workgroups per compute unit for one kernel instance at a given
-// block size and LDS size (cached: the query only reads kernel metadata).
-template <class F, int MT, int UPL, int RB>
-static int resident_per_cu(int T, size_t lds) {
+// Resident workgroups per compute unit for one kernel at a given block size
+// and LDS size (cached: the query only reads kernel metadata).
+template <typename K>
+static int resident_per_cu(K kernel, int T, size_t lds) {
     static std::mutex mu;
     static std::map<std::pair<int, size_t>, int> cache;
     std::lock_guard<std::mutex> lk(mu);
     auto it = cache.find({T, lds});
     if (it != cache.end()) return it->second;
     int nb = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, qmv_gemv<F, MT, UPL, RB>, T, lds) !=
-            hipSuccess ||
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, kernel, T, lds) != hipSuccess ||
         nb < 1) {
         (void)hipGetLastError();
         nb = 1;
@@ -635,40 +875,93 @@ static int resident_per_cu(int T, size_t lds) {
     return nb;
 }
 
-template <class F, int MT, int UPL, int RB>
-static hipError_t launch_t(const GemvPlan &p0, const uint8_t *W, const float *x, float *y,
-                           int64_t k, int64_t n, int64_t row_bytes, int64_t j0, int64_t j1,
-                           int acc, hipStream_t s) {
-    GemvPlan p = p0;
-    if (p.x_in_lds && ((uintptr_t)x & 15) != 0) { // the LDS copy moves 16-byte pieces
-        p.x_in_lds = 0;
-        p.lds_bytes -= (size_t)k * p.MT * sizeof(float);
-    }
-    const int64_t cap = (int64_t)p.num_cu * resident_per_cu<F, MT, UPL, RB>(p.T, p.lds_bytes);
+template <typename K>
+static hipError_t launch_k(K kernel, const GemvPlan &p, const uint8_t *W, const float *x,
+                           float *y, int64_t k, int64_t n, int64_t row_bytes, int64_t j0,
+                           int64_t j1, int acc, hipStream_t s) {
+    if (p.lds_bytes > 64 * 1024 &&
+        hipFuncSetAttribute((const void *)kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)p.lds_bytes) != hipSuccess)
+        return hipGetLastError();
+    const int64_t cap = (int64_t)p.num_cu * resident_per_cu(kernel, p.T, p.lds_bytes);
     const int grid = (int)(p.grid < cap ? p.grid : cap);
-    hipLaunchKernelGGL((qmv_gemv<F, MT, UPL, RB>), dim3(grid), dim3(p.T), p.lds_bytes, s, W, x,
-                       y, k, n, row_bytes, j0, j1, acc, p.U, p.L, p.P, p.G, p.x_in_lds);
+    hipLaunchKernelGGL(kernel, dim3(grid), dim3(p.T), p.lds_bytes, s, W, x, y, k, n, row_bytes,
+                       j0, j1, acc, p.U, p.L, p.P, p.G, p.buf_bytes);
     return hipGetLastError();
 }
 
+template <class F, int MT, int UPL, int RB, bool XL>
+static hipError_t launch_staged_npt(const GemvPlan &p, const uint8_t *W, const float *x,
+                                    float *y, int64_t k, int64_t n, int64_t rb, int64_t j0,
+                                    int64_t j1, int acc, hipStream_t s) {
+    switch (p.npt) {
+    case 2:
+        return launch_k(qmv_gemv_staged<F, MT, UPL, RB, 2, XL>, p, W, x, y, k, n, rb, j0, j1,
+                        acc, s);
+    case 4:
+        return launch_k(qmv_gemv_staged<F, MT, UPL, RB, 4, XL>, p, W, x, y, k, n, rb, j0, j1,
+                        acc, s);
+    default:
+        return launch_k(qmv_gemv_staged<F, MT, UPL, RB, 8, XL>, p, W, x, y, k, n, rb, j0, j1,
+                        acc, s);
+    }
+}
+
+template <class F, int MT, int UPL, bool XL>
+static hipError_t launch_staged_rb(const GemvPlan &p, const uint8_t *W, const float *x,
+                                   float *y, int64_t k, int64_t n, int64_t rb, int64_t j0,
+                                   int64_t j1, int acc, hipStream_t s) {
+    if (p.RB == 2) return launch_staged_npt<F, MT, UPL, 2, XL>(p, W, x, y, k, n, rb, j0, j1, acc, s);
+    return launch_staged_npt<F, MT, UPL, 1, XL>(p, W, x, y, k, n, rb, j0, j1, acc, s);
+}
+
+template <class F, int MT, int UPL, bool XL>
+static hipError_t launch_direct_rb(const GemvPlan &p, const uint8_t *W, const float *x,
+                                   float *y, int64_t k, int64_t n, int64_t rb, int64_t j0,
+                                   int64_t j1, int acc, hipStream_t s) {
+    if (p.RB == 2)
+        return launch_k(qmv_gemv_direct<F, MT, UPL, 2, XL>, p, W, x, y, k, n, rb, j0, j1, acc,
+                        s);
+    return launch_k(qmv_gemv_direct<F, MT, UPL, 1, XL>, p, W, x, y, k, n, rb, j0, j1, acc, s);
+}
+
+// x goes through LDS when the plan allows it and x is 16-byte aligned (the
+// LDS copy moves 16-byte pieces).
+static bool use_x_lds(GemvPlan &p, const float *x, int64_t k) {
+    if (p.x_in_lds && ((uintptr_t)x & 15) == 0) return true;
+    if (p.x_in_lds) p.lds_bytes -= (size_t)k * p.MT * sizeof(float);
+    p.x_in_lds = 0;
+    return false;
+}
+
 template <class F>
-static hipError_t launch_f(const GemvPlan &p, const uint8_t *W, const float *x, float *y,
-                           int64_t k, int64_t n, int64_t rb, int64_t j0, int64_t j1, int acc,
-                           hipStream_t s) {
-    const int R = default_rb(p.fmt);
-    if (p.UPL == 2) {
-        if (p.RB == 1) return launch_t<F, 1, 2, 1>(p, W, x, y, k, n, rb, j0, j1, acc, s);
-        if (R == 4) return launch_t<F, 1, 2, 4>(p, W, x, y, k, n, rb, j0, j1, acc, s);
-        return launch_t<F, 1, 2, 2>(p, W, x, y, k, n, rb, j0, j1, acc, s);
+static hipError_t launch_staged(const GemvPlan &p0, const uint8_t *W, const float *x, float *y,
+                                int64_t k, int64_t n, int64_t rb, int64_t j0, int64_t j1, int acc,
+                                hipStream_t s) {
+    GemvPlan p = p0;
+    if (use_x_lds(p, x, k)) {
+        if (p.UPL == 2) return launch_staged_rb<F, 1, 2, true>(p, W, x, y, k, n, rb, j0, j1, acc, s);
+        if (p.MT == 2) return launch_staged_rb<F, 2, 1, true>(p, W, x, y, k, n, rb, j0, j1, acc, s);
+        return launch_staged_rb<F, 1, 1, true>(p, W, x, y, k, n, rb, j0, j1, acc, s);
     }
-    if (p.MT == 2) {
-        if (p.RB == 1) return launch_t<F, 2, 1, 1>(p, W, x, y, k, n, rb, j0, j1, acc, s);
-        if (R == 4) return launch_t<F, 2, 1, 4>(p, W, x, y, k, n, rb, j0, j1, acc, s);
-        return launch_t<F, 2, 1, 2>(p, W, x, y, k, n, rb, j0, j1, acc, s);
+    if (p.UPL == 2) return launch_staged_rb<F, 1, 2, false>(p, W, x, y, k, n, rb, j0, j1, acc, s);
+    if (p.MT == 2) return launch_staged_rb<F, 2, 1, false>(p, W, x, y, k, n, rb, j0, j1, acc, s);
+    return launch_staged_rb<F, 1, 1, false>(p, W, x, y, k, n, rb, j0, j1, acc, s);
+}
+
+template <class F>
+static hipError_t launch_direct(const GemvPlan &p0, const uint8_t *W, const float *x, float *y,
+                                int64_t k, int64_t n, int64_t rb, int64_t j0, int64_t j1, int acc,
+                                hipStream_t s) {
+    GemvPlan p = p0;
+    if (use_x_lds(p, x, k)) {
+        if (p.UPL == 2) return launch_direct_rb<F, 1, 2, true>(p, W, x, y, k, n, rb, j0, j1, acc, s);
+        if (p.MT == 2) return launch_direct_rb<F, 2, 1, true>(p, W, x, y, k, n, rb, j0, j1, acc, s);
+        return launch_direct_rb<F, 1, 1, true>(p, W, x, y, k, n, rb, j0, j1, acc, s);
     }
-    if (p.RB == 1) return launch_t<F, 1, 1, 1>(p, W, x, y, k, n, rb, j0, j1, acc, s);
-    if (R == 4) return launch_t<F, 1, 1, 4>(p, W, x, y, k, n, rb, j0, j1, acc, s);
-    return launch_t<F, 1, 1, 2>(p, W, x, y, k, n, rb, j0, j1, acc, s);
+    if (p.UPL == 2) return launch_direct_rb<F, 1, 2, false>(p, W, x, y, k, n, rb, j0, j1, acc, s);
+    if (p.MT == 2) return launch_direct_rb<F, 2, 1, false>(p, W, x, y, k, n, rb, j0, j1, acc, s);
+    return launch_direct_rb<F, 1, 1, false>(p, W, x, y, k, n, rb, j0, j1, acc, s);
 }
 
 hipError_t launch_gemv(const GemvPlan &p, const uint8_t *W, const float *x, float *y,
@@ -676,24 +969,28 @@ hipError_t launch_gemv(const GemvPlan &p, const uint8_t *W, const float *x, floa
                        int64_t j_end, int accumulate, hipStream_t stream) {
     switch (p.fmt) {
     case FMT_Q4_0:
-        return launch_f<UQ4_0>(p, W, x, y, k, n, row_bytes, j_start, j_end, accumulate, stream);
+        return launch_staged<UQ4_0>(p, W, x, y, k, n, row_bytes, j_start, j_end, accumulate,
+                                    stream);
     case FMT_Q4_K:
-        return launch_f<UQ4_K>(p, W, x, y, k, n, row_bytes, j_start, j_end, accumulate, stream);
+        return launch_staged<UQ4_K>(p, W, x, y, k, n, row_bytes, j_start, j_end, accumulate,
+                                    stream);
     case FMT_Q6_K:
-        return launch_f<UQ6_K>(p, W, x, y, k, n, row_bytes, j_start, j_end, accumulate, stream);
+        return launch_staged<UQ6_K>(p, W, x, y, k, n, row_bytes, j_start, j_end, accumulate,
+                                    stream);
     case FMT_BF16:
-        return launch_f<UHalf<true>>(p, W, x, y, k, n, row_bytes, j_start, j_end, accumulate,
-                                     stream);
+        return launch_direct<UHalf<true>>(p, W, x, y, k, n, row_bytes, j_start, j_end,
+                                          accumulate, stream);
     case FMT_F16:
-        return launch_f<UHalf<false>>(p, W, x, y, k, n, row_bytes, j_start, j_end, accumulate,
-                                      stream);
+        return launch_direct<UHalf<false>>(p, W, x, y, k, n, row_bytes, j_start, j_end,
+                                           accumulate, stream);
     default: return hipErrorInvalidValue;
     }
 }
 
 const char *gemv_kernel_name(const GemvPlan &p) {
-    static const char *names[] = {"", "qmv_gemv<f16>", "qmv_gemv<bf16>", "qmv_gemv<q4_0>",
-                                  "qmv_gemv<q4_k>", "qmv_gemv<q6_k>"};
+    static const char *names[] = {"", "qmv_gemv_direct<f16>", "qmv_gemv_direct<bf16>",
+                                  "qmv_gemv_staged<q4_0>", "qmv_gemv_staged<q4_k>",
+                                  "qmv_gemv_staged<q6_k>"};
     return (p.fmt >= 1 && p.fmt <= 5) ? names[p.fmt] : "";
 }
 

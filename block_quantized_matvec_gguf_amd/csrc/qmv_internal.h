@@ -24,6 +24,9 @@ struct GemvPlan {
     int grid;     // workgroups wanted (one per batch); the launch caps it at residency
     int num_cu;   // compute units of the device
     int x_in_lds; // stage x through LDS before loading it into registers
+    int staged;   // weights go through LDS (block formats)
+    int buf_bytes; // bytes of one LDS weight buffer (staged kernel)
+    int npt;      // 16-byte weight pieces per thread per batch (staged kernel)
     size_t lds_bytes;
 };
 

@@ -60,7 +60,7 @@ def test_status_strings(lib):
 
 
 def test_kernel_names(lib):
-    assert qb.qmv_kernel_name(qb.QMV_FMT_Q6_K, 2560, 1) == "qmv_gemv<q6_k>"
+    assert qb.qmv_kernel_name(qb.QMV_FMT_Q6_K, 2560, 1) == "qmv_gemv_staged<q6_k>"
     assert qb.qmv_kernel_name(qb.QMV_FMT_Q4_0, 96, 1) == "qmv_simple"
     assert qb.qmv_kernel_name(qb.QMV_FMT_Q4_0, 96, 1, qb.QMV_ALGO_GEMV) == ""
     assert qb.qmv_kernel_name(qb.QMV_FMT_F16, 10, 1) == "qmv_simple"
