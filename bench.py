@@ -1,0 +1,260 @@
+#!/usr/bin/env python3
+"""Benchmark of the block-quantized GEMV on one MI355X.
+
+Metric: effective weight-read GB/s (quantized weight bytes / time) and the
+fraction of MI355X HBM peak. Default workload: the Q6_K output projection,
+k=2560, n=262144 (vocabulary), m=1, y = x @ W; one step is one launch over
+all rows. W is rotated over enough copies that HBM, not the 256 MB
+last-level cache, serves it. The same rows as 8 row-range tiles accumulating
+into y are timed as well and reported under "tiled".
+
+Prints ONE JSON line. Extra modes:
+  --summarize-pmc CSV...   turn rocprofv3 counter CSVs of this script into
+                           the traffic summary under profiles/
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+KERNEL_SOURCES = ["block_quantized_matvec_gguf_amd/csrc/qmv_gemv.hip",
+                  "block_quantized_matvec_gguf_amd/csrc/qmv_api.cpp",
+                  "block_quantized_matvec_gguf_amd/csrc/qmv_internal.h"]
+METRIC = "effective weight-read GB/s and % of MI355X HBM peak for quantized GEMV"
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def traffic_path(workload: str) -> str:
+    return os.path.join(ROOT, "profiles", "traffic_%s.json" % workload)
+
+
+def load_traffic(workload: str):
+    """HBM bytes per launch from committed counter runs, or None when absent
+    or taken on a different kernel source."""
+    p = traffic_path(workload)
+    if not os.path.exists(p):
+        return None
+    with open(p) as f:
+        t = json.load(f)
+    if t.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    return t
+
+
+def summarize_pmc(args):
+    """Average FETCH_SIZE / WRITE_SIZE per dispatch of the GEMV kernel and of
+    the calibration copy (torch copy of a known byte count) and write the
+    traffic summary for the workload."""
+    import csv
+    per = {}
+    for path in args.summarize_pmc:
+        for r in csv.DictReader(open(path)):
+            name = r["Kernel_Name"]
+            key = "gemv" if "qmv_gemv" in name else ("copy" if "neg_kernel" in name or
+                                                     ("elementwise" in name and "neg" in name)
+                                                     else None)
+            if key is None:
+                continue
+            per.setdefault((key, r["Counter_Name"]), []).append(float(r["Counter_Value"]))
+
+    def avg(key, c):
+        v = per.get((key, c), [])
+        return sum(v) / len(v) if v else None
+
+    copy_bytes = args.calib_bytes
+    cf, cw = avg("copy", "FETCH_SIZE"), avg("copy", "WRITE_SIZE")
+    gf, gw = avg("gemv", "FETCH_SIZE"), avg("gemv", "WRITE_SIZE")
+    out = {"workload": args.workload, "kernel_source_sha256": kernel_source_hash(),
+           "gemv_fetch_kib_per_dispatch": gf, "gemv_write_kib_per_dispatch": gw,
+           "copy_bytes": copy_bytes, "copy_fetch_kib": cf, "copy_write_kib": cw}
+    if cf and gf is not None:
+        out["fetch_factor"] = copy_bytes / (cf * 1024.0)
+        out["fetch_bytes_per_launch"] = gf * 1024.0 * out["fetch_factor"]
+    if cw and gw is not None:
+        out["write_factor"] = copy_bytes / (cw * 1024.0)
+        out["write_bytes_per_launch"] = gw * 1024.0 * out["write_factor"]
+    if "fetch_bytes_per_launch" in out and "write_bytes_per_launch" in out:
+        out["bytes_per_launch"] = out["fetch_bytes_per_launch"] + out["write_bytes_per_launch"]
+    os.makedirs(os.path.dirname(traffic_path(args.workload)), exist_ok=True)
+    with open(traffic_path(args.workload), "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="q6_k_vocab_outproj")
+    ap.add_argument("--algo", default="auto")
+    ap.add_argument("--tiles", type=int, default=None, help="tiles of the auxiliary run")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-tiled", action="store_true",
+                    help="skip the tiled run (profiling runs: one launch shape only)")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run a plain copy of --calib-bytes (counter calibration)")
+    ap.add_argument("--calib-bytes", type=int, default=512 * 1024 * 1024)
+    ap.add_argument("--summarize-pmc", nargs="*", default=None)
+    args = ap.parse_args()
+
+    if args.summarize_pmc:
+        summarize_pmc(args)
+        return
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: the GEMV shards by output rows with no "
+              "exchange inside the product, and this build runs on a single MI355X "
+              "(requested --gpus %d, WORLD_SIZE %d)" % (args.gpus, world), file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from block_quantized_matvec_gguf_amd import binding as qb
+    from block_quantized_matvec_gguf_amd import synth
+
+    fmt, W, x, spec = synth.workload(args.workload)
+    k, n, m = spec["k"], spec["n"], spec["m"]
+    tiles = args.tiles if args.tiles is not None else spec.get("tiles", 8)
+    algo = qb.ALGOS[args.algo]
+    wbytes = W.nbytes
+    copies = max(1, int(np.ceil(1.1e9 / wbytes)))
+    dev = torch.device("cuda:0")
+    Wd = [torch.from_numpy(W).to(dev)]
+    for _ in range(copies - 1):
+        Wd.append(Wd[0].clone())
+    xd = torch.from_numpy(x).to(dev)
+    yd = torch.zeros((m, n), dtype=torch.float32, device=dev)
+    qb.ensure_context()
+    lib = qb.load()
+    stream = torch.cuda.current_stream(dev)
+    sp = stream.cuda_stream
+    wp = [w.data_ptr() for w in Wd]
+    xp, yp = xd.data_ptr(), yd.data_ptr()
+
+    def run(i, j0=0, j1=n, acc=0):
+        rc = lib.qmv_run_ex(fmt, wp[i % copies], xp, yp, k, n, m, j0, j1, acc, sp, algo)
+        if rc != 0:
+            raise RuntimeError("qmv_run_ex: %s %s" % (qb.qmv_status_string(rc),
+                                                      qb.qmv_last_error()))
+
+    # ---- main timed region: one launch over all rows per step
+    for i in range(args.warmup):
+        run(i)
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for i in range(args.steps):
+        run(i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_s = ev0.elapsed_time(ev1) * 1e-3
+    step_s = max(wall, gpu_s) / args.steps
+    launch_s = gpu_s / args.steps
+    y_main = yd.cpu().numpy()
+
+    # ---- auxiliary: the same rows as row-range tiles accumulating into y
+    edges = [t * n // tiles for t in range(tiles + 1)]
+    tstep = None
+    if not args.no_tiled:
+        yd.zero_()
+        for i in range(max(1, args.warmup // 4)):
+            for t in range(tiles):
+                run(i, edges[t], edges[t + 1], 1)
+        torch.cuda.synchronize()
+        tsteps = max(1, args.steps // 2)
+        e2, e3 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        e2.record(stream)
+        for i in range(tsteps):
+            for t in range(tiles):
+                run(i, edges[t], edges[t + 1], 1)
+        e3.record(stream)
+        torch.cuda.synchronize()
+        twall = time.perf_counter() - t0
+        tgpu = e2.elapsed_time(e3) * 1e-3
+        tstep = max(twall, tgpu) / tsteps
+
+    if args.calibrate_copy:
+        # a plain elementwise kernel that reads and writes calib_bytes each
+        a = torch.ones(args.calib_bytes // 4, dtype=torch.float32, device=dev)
+        b = torch.empty_like(a)
+        torch.neg(a, out=b)
+        torch.cuda.synchronize()
+        del a, b
+
+    alg_bytes = wbytes + m * k * 4 + m * n * 4       # W + x + y written once
+    achieved = alg_bytes / launch_s / 1e9
+    value = wbytes / step_s / 1e9
+    traffic = load_traffic(args.workload)
+    out = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_s * 1e3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded; value distributions of the measured workload)",
+        "config": {"workload": args.workload, "format": synth.FORMAT_NAMES[fmt], "k": k,
+                   "n": n, "m_tokens": m, "accumulate": 0, "weight_bytes": wbytes,
+                   "weight_copies_rotated": copies,
+                   "kernel": qb.qmv_kernel_name(fmt, k, m, algo)},
+        "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
+        "rows_per_s": round(m * n / step_s, 1),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": (round(traffic["bytes_per_launch"])
+                                 if traffic and "bytes_per_launch" in traffic else None),
+                     "algorithmic_bytes_per_launch": alg_bytes,
+                     "launch_us": round(launch_s * 1e6, 3)},
+    }
+    if tstep is not None:
+        out["tiled"] = {"tiles": tiles, "accumulate": 1, "ms_per_step": round(tstep * 1e3, 5),
+                        "value": round(wbytes / tstep / 1e9, 1),
+                        "pct_hbm_peak": round(100.0 * wbytes / tstep / 1e9 / HBM_PEAK_GBS, 2)}
+
+    if not args.no_cpu_baseline:
+        import oracle
+        threads = max(1, min(os.cpu_count() or 1, 16))
+        # the whole workload when it is small enough, else a bounded row sample
+        rows = n if k * n <= 2_000_000_000 else max(1, 2_000_000_000 // k)
+        t0 = time.perf_counter()
+        yref, sref = oracle.gemv(fmt, W, x, k, n, 0, rows, threads=threads)
+        dt = time.perf_counter() - t0
+        out["cpu_baseline"] = {
+            "value": round(rows * (wbytes / n) / dt / 1e9, 3), "unit": "GB/s",
+            "cores": threads, "kind": "oracle",
+            "sample": "rows 0..%d of %d (%s), m=%d, f64 accumulation; %.2f s" % (
+                rows, n, "all" if rows == n else "first rows", m, dt)}
+        res = oracle.check_parity(y_main[:, :rows], yref, sref)
+        out["parity"] = {"ok": res["ok"], "max_err_over_tol": round(res["max_ratio"], 5),
+                         "cosine": res["cosine"], "outputs": res["n"]}
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
