@@ -27,7 +27,9 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFS = 2500.0   # dense bf16 matrix-core peak of MI355X
 KERNEL_SOURCES = ["block_quantized_matvec_gguf_amd/csrc/qmv_gemv.hip",
+                  "block_quantized_matvec_gguf_amd/csrc/qmv_mfma.hip",
                   "block_quantized_matvec_gguf_amd/csrc/qmv_api.cpp",
                   "block_quantized_matvec_gguf_amd/csrc/qmv_internal.h"]
 METRIC = "effective weight-read GB/s and % of MI355X HBM peak for quantized GEMV"
@@ -206,6 +208,26 @@ def main():
     achieved = alg_bytes / launch_s / 1e9
     value = wbytes / step_s / 1e9
     traffic = load_traffic(args.workload)
+    traffic_bytes = (round(traffic["bytes_per_launch"])
+                     if traffic and "bytes_per_launch" in traffic else None)
+    hbm = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+           "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic_bytes,
+           "algorithmic_bytes_per_launch": alg_bytes, "launch_us": round(launch_s * 1e6, 3)}
+    kname = qb.qmv_kernel_name(fmt, k, m, algo)
+    if kname.startswith("qmv_mfma"):
+        # matrix-core kernel: 2*m*k*n algorithmic flops against the dense bf16
+        # peak (x enters as two bf16 terms, so the units execute twice that)
+        flops = 2.0 * m * k * n
+        tf = flops / launch_s / 1e12
+        roofline = {"bound": "mfma", "achieved": round(tf, 2), "peak": MFMA_BF16_PEAK_TFS,
+                    "unit": "TFLOP/s", "frac": round(tf / MFMA_BF16_PEAK_TFS, 4),
+                    "traffic": traffic_bytes, "algorithmic_flops_per_launch": flops,
+                    "executed_mfma_flops_per_launch": 2 * flops,
+                    "launch_us": round(launch_s * 1e6, 3),
+                    "hbm": {k_: hbm[k_] for k_ in ("achieved", "peak", "unit", "frac",
+                                                   "algorithmic_bytes_per_launch")}}
+    else:
+        roofline = hbm
     out = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -222,15 +244,10 @@ def main():
         "config": {"workload": args.workload, "format": synth.FORMAT_NAMES[fmt], "k": k,
                    "n": n, "m_tokens": m, "accumulate": 0, "weight_bytes": wbytes,
                    "weight_copies_rotated": copies,
-                   "kernel": qb.qmv_kernel_name(fmt, k, m, algo)},
+                   "kernel": kname},
         "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "rows_per_s": round(m * n / step_s, 1),
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": (round(traffic["bytes_per_launch"])
-                                 if traffic and "bytes_per_launch" in traffic else None),
-                     "algorithmic_bytes_per_launch": alg_bytes,
-                     "launch_us": round(launch_s * 1e6, 3)},
+        "roofline": roofline,
     }
     if tstep is not None:
         out["tiled"] = {"tiles": tiles, "accumulate": 1, "ms_per_step": round(tstep * 1e3, 5),
@@ -241,7 +258,7 @@ def main():
         import oracle
         threads = max(1, min(os.cpu_count() or 1, 16))
         # the whole workload when it is small enough, else a bounded row sample
-        rows = n if k * n <= 2_000_000_000 else max(1, 2_000_000_000 // k)
+        rows = n if k * n * m <= 4_000_000_000 else max(1, 4_000_000_000 // (k * m))
         t0 = time.perf_counter()
         yref, sref = oracle.gemv(fmt, W, x, k, n, 0, rows, threads=threads)
         dt = time.perf_counter() - t0

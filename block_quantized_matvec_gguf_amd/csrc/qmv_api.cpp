@@ -223,10 +223,16 @@ int qmv_run_ex(int format, const void *W, const float *x, float *y, int64_t k, i
         return QMV_OK;
     }
 
-    const int a = resolve_algo(format, k, m_tokens, algo);
+    int a = resolve_algo(format, k, m_tokens, algo);
     if (a < 0)
         return fail(QMV_ERR_UNSUPPORTED, "algo %d cannot serve %s with k=%lld m=%lld", algo,
                     fmt_name(format), (long long)k, (long long)m_tokens);
+    if (a == QMV_ALGO_MFMA && ((uintptr_t)x & 15) != 0) {
+        // the matrix-core kernel reads x in 16-byte pieces
+        if (algo == QMV_ALGO_MFMA)
+            return fail(QMV_ERR_MISALIGNED, "the MFMA kernel needs x 16-byte aligned");
+        a = resolve_algo(format, k, 1, QMV_ALGO_AUTO);
+    }
     const int64_t rows = j_end - j_start;
     if (a == QMV_ALGO_SIMPLE) {
         e = qmv::launch_simple(format, Wb, x, y, k, n, m_tokens, rb, j_start, j_end,

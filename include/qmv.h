@@ -49,7 +49,7 @@ enum qmv_format {
 enum qmv_algo {
     QMV_ALGO_AUTO = 0,   /* GEMV for small m_tokens, MFMA tiles for prefill-sized m */
     QMV_ALGO_GEMV = 1,   /* streaming matvec; m_tokens handled in small groups    */
-    QMV_ALGO_MFMA = 2,   /* N-token tiles decoded to exact bf16 codes in LDS, MFMA */
+    QMV_ALGO_MFMA = 2,   /* N-token tiles on the bf16 matrix cores, exact codes    */
     QMV_ALGO_SIMPLE = 3  /* one wave per row, any valid shape (slow, for checks)   */
 };
 
@@ -101,9 +101,11 @@ int qmv_run(int format, const void *W, const float *x, float *y, int64_t k, int6
             void *stream);
 
 /* qmv_run with an explicit kernel family (enum qmv_algo). QMV_ALGO_MFMA
- * supports Q4_0, Q4_K and Q6_K and needs k to be a multiple of 256; otherwise
- * it returns QMV_ERR_UNSUPPORTED. All families meet the same accuracy
- * contract; they may differ in the last bits. */
+ * supports Q4_K with k a multiple of 256 (otherwise QMV_ERR_UNSUPPORTED) and
+ * needs x 16-byte aligned (otherwise QMV_ERR_MISALIGNED). QMV_ALGO_AUTO takes
+ * it for m_tokens >= 16 when it applies and x is 16-byte aligned, else the
+ * GEMV family. All families meet the same accuracy contract; they may differ
+ * in the last bits. */
 int qmv_run_ex(int format, const void *W, const float *x, float *y, int64_t k, int64_t n,
                int64_t m_tokens, int64_t j_start, int64_t j_end, int accumulate,
                void *stream, int algo);

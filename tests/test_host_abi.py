@@ -65,6 +65,11 @@ def test_kernel_names(lib):
     assert qb.qmv_kernel_name(qb.QMV_FMT_Q4_0, 96, 1, qb.QMV_ALGO_GEMV) == ""
     assert qb.qmv_kernel_name(qb.QMV_FMT_F16, 10, 1) == "qmv_simple"
     assert qb.qmv_kernel_name(qb.QMV_FMT_Q4_K, 300, 1) == ""
+    # prefill-sized token counts go to the matrix-core kernel where it applies
+    assert qb.qmv_kernel_name(qb.QMV_FMT_Q4_K, 4096, 64) == "qmv_mfma<q4_k>"
+    assert qb.qmv_kernel_name(qb.QMV_FMT_Q4_K, 4096, 15) == "qmv_gemv_staged<q4_k>"
+    assert qb.qmv_kernel_name(qb.QMV_FMT_Q4_K, 256, 1, qb.QMV_ALGO_MFMA) == "qmv_mfma<q4_k>"
+    assert qb.qmv_kernel_name(qb.QMV_FMT_BF16, 4096, 64, qb.QMV_ALGO_MFMA) == ""
 
 
 def _run(**kw):
