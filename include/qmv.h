@@ -22,7 +22,8 @@
  *
  * All pointers are device pointers (memory from hipMalloc or a torch CUDA
  * tensor) unless stated. The caller owns every buffer; the library keeps no
- * pointer after a call returns and allocates no memory per call.
+ * pointer after a call returns. The GEMV and per-row families allocate no
+ * memory; the matrix-core family takes stream-ordered scratch (qmv_run_ex).
  */
 #ifndef QMV_H
 #define QMV_H
@@ -102,10 +103,14 @@ int qmv_run(int format, const void *W, const float *x, float *y, int64_t k, int6
 
 /* qmv_run with an explicit kernel family (enum qmv_algo). QMV_ALGO_MFMA
  * supports Q4_K with k a multiple of 256 (otherwise QMV_ERR_UNSUPPORTED) and
- * needs x 16-byte aligned (otherwise QMV_ERR_MISALIGNED). QMV_ALGO_AUTO takes
- * it for m_tokens >= 16 when it applies and x is 16-byte aligned, else the
- * GEMV family. All families meet the same accuracy contract; they may differ
- * in the last bits. */
+ * needs x 16-byte aligned (otherwise QMV_ERR_MISALIGNED). It is the one
+ * family that uses scratch memory: x is first rewritten into matrix-core
+ * operand order in a buffer of about m_tokens*k*4.2 bytes, taken from and
+ * returned to the current memory pool of the stream's device with
+ * hipMallocAsync / hipFreeAsync on `stream` (QMV_ERR_HIP if that fails).
+ * QMV_ALGO_AUTO takes it for m_tokens >= 16 when it applies and x is 16-byte
+ * aligned, else the GEMV family. All families meet the same accuracy
+ * contract; they may differ in the last bits. */
 int qmv_run_ex(int format, const void *W, const float *x, float *y, int64_t k, int64_t n,
                int64_t m_tokens, int64_t j_start, int64_t j_end, int accumulate,
                void *stream, int algo);
