@@ -28,16 +28,24 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFS = 2500.0   # dense bf16 matrix-core peak of MI355X
-KERNEL_SOURCES = ["block_quantized_matvec_gguf_amd/csrc/qmv_gemv.hip",
-                  "block_quantized_matvec_gguf_amd/csrc/qmv_mfma.hip",
-                  "block_quantized_matvec_gguf_amd/csrc/qmv_api.cpp",
+# Sources of each kernel family (the traffic summary of a workload is valid
+# only for the sources it was measured on).
+COMMON_SOURCES = ["block_quantized_matvec_gguf_amd/csrc/qmv_api.cpp",
                   "block_quantized_matvec_gguf_amd/csrc/qmv_internal.h"]
+FAMILY_SOURCES = {"gemv": ["block_quantized_matvec_gguf_amd/csrc/qmv_gemv.hip"],
+                  "mfma": ["block_quantized_matvec_gguf_amd/csrc/qmv_mfma.hip"],
+                  "simple": ["block_quantized_matvec_gguf_amd/csrc/qmv_simple.hip"]}
 METRIC = "effective weight-read GB/s and % of MI355X HBM peak for quantized GEMV"
 
 
-def kernel_source_hash() -> str:
+def kernel_family(kernel_name: str) -> str:
+    return ("mfma" if kernel_name.startswith("qmv_mfma") else
+            "simple" if kernel_name.startswith("qmv_simple") else "gemv")
+
+
+def kernel_source_hash(family: str) -> str:
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in COMMON_SOURCES + FAMILY_SOURCES[family]:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()
@@ -47,7 +55,7 @@ def traffic_path(workload: str) -> str:
     return os.path.join(ROOT, "profiles", "traffic_%s.json" % workload)
 
 
-def load_traffic(workload: str):
+def load_traffic(workload: str, family: str):
     """HBM bytes per launch from committed counter runs, or None when absent
     or taken on a different kernel source."""
     p = traffic_path(workload)
@@ -55,7 +63,7 @@ def load_traffic(workload: str):
         return None
     with open(p) as f:
         t = json.load(f)
-    if t.get("kernel_source_sha256") != kernel_source_hash():
+    if t.get("kernel_source_sha256") != kernel_source_hash(family):
         return None
     return t
 
@@ -65,13 +73,20 @@ def summarize_pmc(args):
     the calibration copy (torch copy of a known byte count) and write the
     traffic summary for the workload."""
     import csv
+    from block_quantized_matvec_gguf_amd import binding as qb
+    from block_quantized_matvec_gguf_amd import synth
+    spec = synth.WORKLOADS[args.workload]
+    family = kernel_family(qb.qmv_kernel_name(synth.fmt_id(spec["fmt"]), spec["k"], spec["m"],
+                                              qb.ALGOS[args.algo]))
+    # the dispatches counted: the main kernel of the family (not x staging)
+    main_kernel = {"gemv": "qmv_gemv", "mfma": "qmv_mfma_q4_k", "simple": "qmv_simple"}[family]
     per = {}
     for path in args.summarize_pmc:
         for r in csv.DictReader(open(path)):
             name = r["Kernel_Name"]
-            key = "gemv" if "qmv_gemv" in name else ("copy" if "neg_kernel" in name or
-                                                     ("elementwise" in name and "neg" in name)
-                                                     else None)
+            key = "gemv" if main_kernel in name else ("copy" if "neg_kernel" in name or
+                                                      ("elementwise" in name and "neg" in name)
+                                                      else None)
             if key is None:
                 continue
             per.setdefault((key, r["Counter_Name"]), []).append(float(r["Counter_Value"]))
@@ -83,7 +98,8 @@ def summarize_pmc(args):
     copy_bytes = args.calib_bytes
     cf, cw = avg("copy", "FETCH_SIZE"), avg("copy", "WRITE_SIZE")
     gf, gw = avg("gemv", "FETCH_SIZE"), avg("gemv", "WRITE_SIZE")
-    out = {"workload": args.workload, "kernel_source_sha256": kernel_source_hash(),
+    out = {"workload": args.workload, "kernel_family": family,
+           "kernel_source_sha256": kernel_source_hash(family),
            "gemv_fetch_kib_per_dispatch": gf, "gemv_write_kib_per_dispatch": gw,
            "copy_bytes": copy_bytes, "copy_fetch_kib": cf, "copy_write_kib": cw}
     if cf and gf is not None:
@@ -122,9 +138,9 @@ def main():
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU: the GEMV shards by output rows with no "
-              "exchange inside the product, and this build runs on a single MI355X "
-              "(requested --gpus %d, WORLD_SIZE %d)" % (args.gpus, world), file=sys.stderr)
+        print("bench.py measures one GPU; runs on several GPUs are not implemented (the "
+              "product would shard by output rows with no exchange inside it). Requested "
+              "--gpus %d, WORLD_SIZE %d." % (args.gpus, world), file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -207,13 +223,13 @@ def main():
     alg_bytes = wbytes + m * k * 4 + m * n * 4       # W + x + y written once
     achieved = alg_bytes / launch_s / 1e9
     value = wbytes / step_s / 1e9
-    traffic = load_traffic(args.workload)
+    kname = qb.qmv_kernel_name(fmt, k, m, algo)
+    traffic = load_traffic(args.workload, kernel_family(kname))
     traffic_bytes = (round(traffic["bytes_per_launch"])
                      if traffic and "bytes_per_launch" in traffic else None)
     hbm = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
            "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic_bytes,
            "algorithmic_bytes_per_launch": alg_bytes, "launch_us": round(launch_s * 1e6, 3)}
-    kname = qb.qmv_kernel_name(fmt, k, m, algo)
     if kname.startswith("qmv_mfma"):
         # matrix-core kernel: 2*m*k*n algorithmic flops against the dense bf16
         # peak (x enters as two bf16 terms, so the units execute twice that)
