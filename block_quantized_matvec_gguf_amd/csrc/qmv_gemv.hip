@@ -23,11 +23,11 @@
 //    stride of U chunks, so every load instruction reads one contiguous span
 //    ("direct" kernel).
 //  * Block formats (Q4_0, Q4_K, Q6_K) interleave fields of odd sizes. There
-//    each batch's rows, one contiguous byte range, are copied with coalesced
-//    16-byte loads into registers one batch ahead, then written to a
-//    double-buffered LDS area from which lanes read their unit's fields
-//    ("staged" kernel). One LDS-only barrier per batch covers both the buffer
-//    swap and the cross-group reduction.
+//    each batch's rows, one contiguous byte range, are copied one batch ahead
+//    straight from memory into a double-buffered LDS area (buffer_load ...
+//    lds, one contiguous kilobyte per wave instruction), from which lanes
+//    read their unit's fields ("staged" kernel). One LDS-only barrier per
+//    batch covers the buffer swap and the cross-group reduction.
 //
 // Decode. Codes are masked into bytes and converted with one instruction per
 // weight: Q4_0 and Q6_K codes as signed bytes holding a multiple of q-8 or
@@ -658,11 +658,10 @@ __global__ __launch_bounds__(512) void qmv_gemv_direct(const uint8_t *__restrict
 // moves one contiguous kilobyte, no registers hold the data, and the
 // compiler does not make the decode's LDS reads of the other buffer wait for
 // it. The batch start is the scalar base of a buffer descriptor sized to the
-// batch; piece offsets are per-lane constants clamped to the last piece (the
-// descriptor's range check is a second guard). The copy of batch i+1 runs
-// while batch i is decoded and is waited for at the end-of-batch barrier.
-// Every wave writes all its NPT kilobyte slots, so a buffer is NPT*T*16
-// bytes. XL: x goes through LDS.
+// batch; lanes whose piece lies past the batch issue no copy (the
+// descriptor's range check is a second guard), so a buffer holds exactly the
+// largest batch. The copy of batch i+1 runs while batch i is decoded and is
+// waited for at the end-of-batch barrier. XL: x goes through LDS.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t batch_rsrc(const uint8_t *p, int bytes) {
     return __builtin_amdgcn_make_buffer_rsrc((void *)p, (short)0, bytes, 0x00020000);
 }
@@ -712,9 +711,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(
             const int off = 16 * (ln.tid + s * ln.T);
             // lane l of this wave writes piece s*T + 64*wave + l
             uint8_t *slot = dst + __builtin_amdgcn_readfirstlane(16 * (s * ln.T + 64 * wave));
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rs, (__attribute__((address_space(3))) void *)slot, 16, off < last ? off : last, 0,
-                0, 2 /* nontemporal */);
+            if (off <= last) // the buffer holds exactly the batch's pieces
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    rs, (__attribute__((address_space(3))) void *)slot, 16, off, 0, 0,
+                    2 /* nontemporal */);
         }
         if (accumulate) yp.fetch(y, n, b, j_end, P, ln.tid, ln.T);
     };
@@ -821,6 +821,9 @@ bool plan_gemv(int fmt, int64_t k, int64_t rows, int mt_max, int num_cu, GemvPla
     for (int cand = 2; cand >= 1 && g.RB == 0; cand /= 2) {
         const int64_t budget = attempt == 0 ? (int64_t)LDS_BUDGET : (int64_t)144 * 1024;
         if (!g.staged && cand > 1 && (g.MT > 1 || g.UPL > 1)) continue; // registers
+        // staged: one row per slot per batch (two measured slower: the larger
+        // buffers leave fewer workgroups per compute unit)
+        if (g.staged && cand > 1) continue;
         int npt = 0;
         if (g.staged) {
             const int64_t pieces = ((int64_t)g.P * cand * rb + 30 + 15) / 16;
@@ -828,7 +831,10 @@ bool plan_gemv(int fmt, int64_t k, int64_t rows, int mt_max, int num_cu, GemvPla
             npt = need <= 2 ? 2 : need <= 4 ? 4 : need <= 8 ? 8 : 0;
             if (npt == 0) continue;
         }
-        const int64_t buf = (int64_t)npt * g.T * 16;
+        // exactly the batch's pieces (rounded to 64 bytes): the copy skips
+        // lanes past the last piece
+        const int64_t buf = g.staged ? ((((g.P * cand * rb + 30 + 15) / 16) * 16 + 63) & ~(int64_t)63)
+                                     : 0;
         const int64_t red = (int64_t)2 * g.P * cand * g.MT * (g.NG + 1) * 4;
         if (2 * buf + red > budget) continue;
         if ((int64_t)g.P * cand * g.MT > 2 * (int64_t)g.T) continue; // y prefetch: 2 per thread
