@@ -4,7 +4,8 @@ This module only draws random numbers and lays them out as stored blocks; it
 holds none of the product's arithmetic (no decoding, no dot products). Both the
 GPU path's tests/benchmark and the CPU oracle consume what it produces.
 
-Value distributions follow the five workloads the method is measured on:
+Value distributions follow the five workloads the method is measured on (the
+Q8_0 and Q5_0 draws mirror Q4_0's, as no measured workload uses them):
 
 * Q4_0: per 32-weight block an f16 scale d ~ U[0.001, 0.02] and 16 uniform
   random code bytes (so every 4-bit code is uniform on 0..15).
@@ -13,6 +14,11 @@ Value distributions follow the five workloads the method is measured on:
   6-bit scale and min is then uniform on 0..63) and 128 uniform code bytes.
 * Q6_K: 128 uniform ql bytes, 64 uniform qh bytes, 16 signed 8-bit scales
   uniform on -32..31 and f16 d ~ U[0.0005, 0.01].
+* Q8_0: per 32-weight block f16 d ~ U[0.001, 0.02] and 32 uniform random code
+  bytes (every signed 8-bit code uniform on -128..127).
+* Q5_0: per 32-weight block f16 d ~ U[0.001, 0.02], a uniform random 32-bit
+  word of fifth bits and 16 uniform code bytes (every 5-bit code uniform on
+  0..31).
 * F16 / BF16: weights ~ N(0, 0.02), rounded to nearest-even in the storage
   type (f64 draw -> f32 -> storage type).
 * x: f32 ~ U[-1, 1].
@@ -23,12 +29,14 @@ from __future__ import annotations
 
 import numpy as np
 
-F16, BF16, Q4_0, Q4_K, Q6_K = 1, 2, 3, 4, 5
-FORMAT_IDS = {"f16": F16, "bf16": BF16, "q4_0": Q4_0, "q4_k": Q4_K, "q6_k": Q6_K}
+F16, BF16, Q4_0, Q4_K, Q6_K, Q8_0, Q5_0 = 1, 2, 3, 4, 5, 6, 7
+FORMAT_IDS = {"f16": F16, "bf16": BF16, "q4_0": Q4_0, "q4_k": Q4_K, "q6_k": Q6_K,
+              "q8_0": Q8_0, "q5_0": Q5_0}
 FORMAT_NAMES = {v: k for k, v in FORMAT_IDS.items()}
 
 # weights per block, bytes per block (GGUF block sizes)
-BLOCK = {F16: (1, 2), BF16: (1, 2), Q4_0: (32, 18), Q4_K: (256, 144), Q6_K: (256, 210)}
+BLOCK = {F16: (1, 2), BF16: (1, 2), Q4_0: (32, 18), Q4_K: (256, 144), Q6_K: (256, 210),
+         Q8_0: (32, 34), Q5_0: (32, 22)}
 
 
 def fmt_id(fmt) -> int:
@@ -109,10 +117,30 @@ def gen_q6_k(rng, n, k, d_range=(0.0005, 0.01)) -> np.ndarray:
     return blk.reshape(-1)
 
 
+def gen_q8_0(rng, n, k, d_range=(0.001, 0.02)) -> np.ndarray:
+    if k % 32:
+        raise ValueError("Q8_0 needs k % 32 == 0")
+    nb = n * (k // 32)
+    blk = np.empty((nb, 34), dtype=np.uint8)
+    blk[:, 0:2] = _f16_bytes(rng.uniform(d_range[0], d_range[1], size=nb))
+    blk[:, 2:34] = rng.integers(0, 256, size=(nb, 32), dtype=np.uint8)
+    return blk.reshape(-1)
+
+
+def gen_q5_0(rng, n, k, d_range=(0.001, 0.02)) -> np.ndarray:
+    if k % 32:
+        raise ValueError("Q5_0 needs k % 32 == 0")
+    nb = n * (k // 32)
+    blk = np.empty((nb, 22), dtype=np.uint8)
+    blk[:, 0:2] = _f16_bytes(rng.uniform(d_range[0], d_range[1], size=nb))
+    blk[:, 2:22] = rng.integers(0, 256, size=(nb, 20), dtype=np.uint8)
+    return blk.reshape(-1)
+
+
 def gen_weights(fmt, rng, n, k) -> np.ndarray:
     f = fmt_id(fmt)
     return {F16: gen_f16, BF16: gen_bf16, Q4_0: gen_q4_0, Q4_K: gen_q4_k,
-            Q6_K: gen_q6_k}[f](rng, n, k)
+            Q6_K: gen_q6_k, Q8_0: gen_q8_0, Q5_0: gen_q5_0}[f](rng, n, k)
 
 
 # The measured workloads. Seeds: W stream 0x51A70000 + id, x stream 0x51A71000 + id.
@@ -121,6 +149,8 @@ WORKLOADS = {
     "bf16_ffn_up": dict(id=2, fmt="bf16", k=2560, n=10240, m=1),
     "f16_ffn_up": dict(id=2, fmt="f16", k=2560, n=10240, m=1),
     "q4_k_ffn_up": dict(id=3, fmt="q4_k", k=2560, n=10240, m=1),
+    "q8_0_ffn_up": dict(id=6, fmt="q8_0", k=2560, n=10240, m=1),
+    "q5_0_ffn_up": dict(id=7, fmt="q5_0", k=2560, n=10240, m=1),
     "q6_k_vocab_outproj": dict(id=4, fmt="q6_k", k=2560, n=262144, m=1, tiles=8),
     "q4_k_prefill": dict(id=5, fmt="q4_k", k=4096, n=14336, m=64),
 }

@@ -10,8 +10,9 @@ This module only builds and loads that file and splits a row range across
 host threads; every row is still summed serially in the C code, so results do
 not depend on the thread count.
 
-Parity against real GGUF files is unpinned: the block layouts inside Q4_K and
-Q6_K are a reading of the ggml format, pinned by hand-built blocks only.
+Parity against real GGUF files is unpinned: the block layouts inside Q4_K,
+Q6_K and Q5_0 and the element order of Q4_0 are a reading of the ggml format,
+pinned by hand-built blocks only.
 """
 from __future__ import annotations
 
@@ -26,8 +27,9 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "qmv_oracle.c")
 _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 
-F16, BF16, Q4_0, Q4_K, Q6_K = 1, 2, 3, 4, 5
-FORMAT_NAMES = {F16: "f16", BF16: "bf16", Q4_0: "q4_0", Q4_K: "q4_k", Q6_K: "q6_k"}
+F16, BF16, Q4_0, Q4_K, Q6_K, Q8_0, Q5_0 = 1, 2, 3, 4, 5, 6, 7
+FORMAT_NAMES = {F16: "f16", BF16: "bf16", Q4_0: "q4_0", Q4_K: "q4_k", Q6_K: "q6_k",
+                Q8_0: "q8_0", Q5_0: "q5_0"}
 
 _lib = None
 

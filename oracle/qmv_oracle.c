@@ -20,7 +20,8 @@
  *
  * Block layouts. The pages give the block sizes (Q4_0 18 bytes per 32 weights,
  * Q4_K 144 bytes per 256, Q6_K 210 bytes per 256: matmul.rs, fns matmul_q4_0,
- * matmul_q4_k, matmul_q6_k) and where the f16 scale fields sit (dispatch/mod.rs,
+ * matmul_q4_k, matmul_q6_k; Q8_0 and Q5_0 blocks of 32 weights laid out field
+ * by field in the expert-matmul tests of dispatch/mod.rs) and where the f16 scale fields sit (dispatch/mod.rs,
  * the backward-input parity tests: Q4_0 d at bytes 0..2, Q4_K d at 0..2 and
  * dmin at 2..4, Q6_K d in the last two bytes). They call the CPU dequantizers
  * "ggml-exact" (matmul.rs, test q4_0_matmul_gpu_vs_cpu_oracle) but do not print
@@ -42,6 +43,8 @@
 #define ORACLE_Q4_0 3
 #define ORACLE_Q4_K 4
 #define ORACLE_Q6_K 5
+#define ORACLE_Q8_0 6
+#define ORACLE_Q5_0 7
 
 /* ---------------------------------------------------------------- scalars */
 
@@ -82,7 +85,9 @@ int64_t oracle_block_elems(int fmt)
     switch (fmt) {
     case ORACLE_F16:
     case ORACLE_BF16: return 1;
-    case ORACLE_Q4_0: return 32;
+    case ORACLE_Q4_0:
+    case ORACLE_Q8_0:
+    case ORACLE_Q5_0: return 32;
     case ORACLE_Q4_K:
     case ORACLE_Q6_K: return 256;
     default: return -1;
@@ -97,6 +102,8 @@ int64_t oracle_block_bytes(int fmt)
     case ORACLE_Q4_0: return 18;
     case ORACLE_Q4_K: return 144;
     case ORACLE_Q6_K: return 210;
+    case ORACLE_Q8_0: return 34;
+    case ORACLE_Q5_0: return 22;
     default: return -1;
     }
 }
@@ -180,6 +187,37 @@ float oracle_q6_k_elem(const uint8_t *blk, int e)
     return ds * (float)(q - 32);
 }
 
+/* Q8_0, 32 weights in 34 bytes: f16 d, then one signed 8-bit code per
+ * element in element order. Value d * q: exact in f32.
+ * (rullama 0.5.0, src/backend/dispatch/mod.rs, the batched expert-matmul
+ * test: blocks of QK8_0 weights with d in bytes 0..2 and the code bytes
+ * from byte 2 on; the signed reading is ggml's.) */
+float oracle_q8_0_elem(const uint8_t *blk, int e)
+{
+    float d = oracle_f16_to_f32(rd_u16(blk));
+    int q = (int)(int8_t)blk[2 + e];
+    return d * (float)q;
+}
+
+/* Q5_0, 32 weights in 22 bytes: f16 d, a little-endian 32-bit word qh of
+ * fifth bits, 16 bytes of 4-bit codes. Element e takes the low nibble of code
+ * byte e (e < 16) or the high nibble of code byte e-16 (e >= 16) as its low
+ * four bits and bit e of qh as its fifth bit; value d * (q - 16), exact in
+ * f32. (Same page and test module as Q8_0, the Q5_0 expert-matmul test: d in
+ * bytes 0..2, qh in bytes 2..6, the 16 code bytes from byte 6 on; the element
+ * order and the offset 16 are ggml's.) */
+float oracle_q5_0_elem(const uint8_t *blk, int e)
+{
+    float d = oracle_f16_to_f32(rd_u16(blk));
+    uint32_t qh = (uint32_t)blk[2] | ((uint32_t)blk[3] << 8) | ((uint32_t)blk[4] << 16) |
+                  ((uint32_t)blk[5] << 24);
+    const uint8_t *qs = blk + 6;
+    int lo = (e < 16) ? (qs[e] & 0x0f) : (qs[e - 16] >> 4);
+    int hi = (int)((qh >> e) & 1u);
+    int q = lo | (hi << 4);
+    return d * (float)(q - 16);
+}
+
 /* Decode weight i of one row (row points at the row's first byte). */
 float oracle_elem(int fmt, const uint8_t *row, int64_t i)
 {
@@ -189,6 +227,8 @@ float oracle_elem(int fmt, const uint8_t *row, int64_t i)
     case ORACLE_Q4_0: return oracle_q4_0_elem(row + (i / 32) * 18, (int)(i % 32));
     case ORACLE_Q4_K: return oracle_q4_k_elem(row + (i / 256) * 144, (int)(i % 256));
     case ORACLE_Q6_K: return oracle_q6_k_elem(row + (i / 256) * 210, (int)(i % 256));
+    case ORACLE_Q8_0: return oracle_q8_0_elem(row + (i / 32) * 34, (int)(i % 32));
+    case ORACLE_Q5_0: return oracle_q5_0_elem(row + (i / 32) * 22, (int)(i % 32));
     default: return NAN;
     }
 }

@@ -31,6 +31,7 @@ from block_quantized_matvec_gguf_amd import synth  # noqa: E402
 from conftest import read_golden  # noqa: E402
 
 F16, BF16, Q4_0, Q4_K, Q6_K = oracle.F16, oracle.BF16, oracle.Q4_0, oracle.Q4_K, oracle.Q6_K
+Q8_0, Q5_0 = oracle.Q8_0, oracle.Q5_0
 
 
 # ------------------------------------------------------------ test packers
@@ -91,6 +92,22 @@ def pack_q6_k(codes, scales, d: float) -> np.ndarray:
         qh[32 * h + l] |= hi << (2 * g)
     sc = [s & 0xFF for s in scales]
     return np.array(ql + qh + sc + f16_le(d), dtype=np.uint8)
+
+
+def pack_q8_0(codes, d: float) -> np.ndarray:
+    """codes: 32 ints -128..127 in element order."""
+    return np.array(f16_le(d) + [c & 0xFF for c in codes], dtype=np.uint8)
+
+
+def pack_q5_0(codes, d: float) -> np.ndarray:
+    """codes: 32 ints 0..31 in element order."""
+    codes = list(codes)
+    qh = 0
+    for e in range(32):
+        qh |= (codes[e] >> 4) << e
+    qs = [(codes[b] & 15) | ((codes[16 + b] & 15) << 4) for b in range(16)]
+    return np.array(f16_le(d) + [(qh >> (8 * i)) & 0xFF for i in range(4)] + qs,
+                    dtype=np.uint8)
 
 
 def hexbytes(s: str) -> np.ndarray:
@@ -273,6 +290,65 @@ def pin_q6_k_roundtrip():
             assert w[e] == want, e
 
 
+def _golden_blocks(name, fmt):
+    g = read_golden(name)
+    assert len(g["bytes"]) == len(g["values"]) > 0
+    for b, v in zip(g["bytes"], g["values"]):
+        blk = hexbytes(b)
+        want = np.array([float(t) for t in v.split()], dtype=np.float64)
+        got = oracle.dequant_row(fmt, blk, 32).astype(np.float64)
+        assert np.array_equal(got, want), (name, got, want)
+    return g
+
+
+def pin_q8_0_golden():
+    g = _golden_blocks("q8_0_hand_block.txt", Q8_0)
+    assert np.array_equal(pack_q8_0([l - 16 for l in range(32)], 1.0), hexbytes(g["bytes"][0]))
+
+
+def pin_q8_0_zero_blocks_and_roundtrip():
+    rng = np.random.default_rng(22)
+    assert not np.any(oracle.dequant_row(Q8_0, pack_q8_0([0] * 32, 3.25), 32))
+    codes = [int(c) for c in rng.integers(-128, 128, 32)]
+    assert not np.any(oracle.dequant_row(Q8_0, pack_q8_0(codes, 0.0), 32))
+    for _ in range(50):
+        codes = [int(c) for c in rng.integers(-128, 128, 32)]
+        d = float(np.float16(rng.uniform(-0.1, 0.1)))
+        got = oracle.dequant_row(Q8_0, pack_q8_0(codes, d), 32)
+        assert np.array_equal(got, np.float32(d) * np.array(codes, dtype=np.float32))
+
+
+def pin_q5_0_golden():
+    g = _golden_blocks("q5_0_hand_block.txt", Q5_0)
+    codes = [16 + l for l in range(16)] + [15 - l for l in range(16)]
+    assert np.array_equal(pack_q5_0(codes, 1.0), hexbytes(g["bytes"][0]))
+
+
+def pin_q5_0_fifth_bit_ownership():
+    """Low codes all 0 and only bit e of qh set: element e decodes to 0, every
+    other element to -16*d."""
+    for e in range(32):
+        codes = [0] * 32
+        codes[e] = 16
+        w = oracle.dequant_row(Q5_0, pack_q5_0(codes, 0.5), 32)
+        want = np.full(32, -8.0, dtype=np.float32)
+        want[e] = 0.0
+        assert np.array_equal(w, want), e
+
+
+def pin_q5_0_zero_blocks_and_roundtrip():
+    rng = np.random.default_rng(23)
+    assert not np.any(oracle.dequant_row(Q5_0, pack_q5_0([16] * 32, 1.5), 32))
+    codes = [int(c) for c in rng.integers(0, 32, 32)]
+    assert not np.any(oracle.dequant_row(Q5_0, pack_q5_0(codes, 0.0), 32))
+    for _ in range(50):
+        codes = [int(c) for c in rng.integers(0, 32, 32)]
+        d = float(np.float16(rng.uniform(-0.1, 0.1)))
+        got = oracle.dequant_row(Q5_0, pack_q5_0(codes, d), 32)
+        want = np.float32(d) * (np.array(codes, dtype=np.float32) - np.float32(16))
+        assert np.array_equal(got, want)
+
+
 def _random_matrix(fmt, n, k, seed):
     rng = np.random.default_rng(seed)
     return synth.gen_weights(fmt, rng, n, k)
@@ -280,7 +356,8 @@ def _random_matrix(fmt, n, k, seed):
 
 def pin_onehot_bruteforce():
     """x = e_i picks column i: y_j must equal the decoded weight w_j[i]."""
-    for fmt, k in ((Q4_0, 32), (Q4_0, 64), (Q4_K, 256), (Q6_K, 256), (F16, 24), (BF16, 24)):
+    for fmt, k in ((Q4_0, 32), (Q4_0, 64), (Q4_K, 256), (Q6_K, 256), (F16, 24), (BF16, 24),
+                   (Q8_0, 64), (Q5_0, 64)):
         n = 6
         W = _random_matrix(fmt, n, k, 100 + fmt)
         dense = oracle.dequant(fmt, W, k, n)
@@ -294,7 +371,7 @@ def pin_dense_route_matches_gemv():
     """Decode everything, then a library f64 matmul: same sums as the oracle's
     gemv to f64 rounding."""
     for fmt, k, n in ((Q4_0, 128, 16), (Q4_K, 512, 9), (Q6_K, 512, 7), (F16, 40, 5),
-                      (BF16, 64, 11)):
+                      (BF16, 64, 11), (Q8_0, 96, 8), (Q5_0, 160, 6)):
         W = _random_matrix(fmt, n, k, 200 + fmt)
         x = synth.gen_x(np.random.default_rng(300 + fmt), 3, k)
         dense = oracle.dequant(fmt, W, k, n).astype(np.float64)
@@ -347,12 +424,33 @@ def _factored_q6_k(W, x, k, n):
     return np.einsum("jb,jbhgc,tjbhgc->tj", d, sc, part)
 
 
+def _factored_q8_0(W, x, k, n):
+    blk = W.reshape(n, k // 32, 34)
+    d = blk[:, :, 0:2].copy().view("<f2")[..., 0].astype(np.float64)
+    codes = blk[:, :, 2:34].view(np.int8).astype(np.float64)  # (n, nb, 32)
+    xb = x.astype(np.float64).reshape(-1, k // 32, 32)
+    return np.einsum("jb,tbe,jbe->tj", d, xb, codes)
+
+
+def _factored_q5_0(W, x, k, n):
+    blk = W.reshape(n, k // 32, 22)
+    d = blk[:, :, 0:2].copy().view("<f2")[..., 0].astype(np.float64)
+    qh = blk[:, :, 2:6].copy().view("<u4")[..., 0].astype(np.int64)  # (n, nb)
+    qs = blk[:, :, 6:22].astype(np.int64)
+    low = np.concatenate([qs & 15, qs >> 4], axis=2)                   # (n, nb, 32)
+    fifth = (qh[..., None] >> np.arange(32)) & 1
+    codes = (low | (fifth << 4)) - 16
+    xb = x.astype(np.float64).reshape(-1, k // 32, 32)
+    return np.einsum("jb,tbe,jbe->tj", d, xb, codes.astype(np.float64))
+
+
 def pin_factored_route_matches_gemv():
     """Per-block factored sums (scale * sum(q*x) - min * sum(x)) in f64 agree
     with the oracle's decode-then-sum to within the f32 rounding of the decoded
     weights."""
     for fmt, k, n, fn in ((Q4_0, 256, 13, _factored_q4_0), (Q4_K, 768, 7, _factored_q4_k),
-                          (Q6_K, 512, 9, _factored_q6_k)):
+                          (Q6_K, 512, 9, _factored_q6_k), (Q8_0, 128, 11, _factored_q8_0),
+                          (Q5_0, 192, 10, _factored_q5_0)):
         W = _random_matrix(fmt, n, k, 400 + fmt)
         x = synth.gen_x(np.random.default_rng(500 + fmt), 2, k)
         want = fn(W, x, k, n)
@@ -392,7 +490,8 @@ def pin_identity_f16():
 
 def pin_linearity():
     rng = np.random.default_rng(20)
-    for fmt, k, n in ((Q4_K, 256, 6), (Q6_K, 256, 6), (Q4_0, 64, 6)):
+    for fmt, k, n in ((Q4_K, 256, 6), (Q6_K, 256, 6), (Q4_0, 64, 6), (Q8_0, 64, 6),
+                      (Q5_0, 64, 6)):
         W = _random_matrix(fmt, n, k, 600 + fmt)
         # dyadic x so that 2*x1 + x2 is exact in f32
         x1 = (rng.integers(-64, 65, size=(1, k)) / 64.0).astype(np.float32)

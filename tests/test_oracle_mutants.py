@@ -12,8 +12,8 @@ import oracle_pins
 SRC = os.path.join(os.path.dirname(oracle.__file__), "qmv_oracle.c")
 
 MUTANTS = {
-    "q4_0_nibble_halves_swapped": ("(qs[e] & 0x0f) : (qs[e - 16] >> 4)",
-                                   "(qs[e] >> 4) : (qs[e - 16] & 0x0f)"),
+    "q4_0_nibble_halves_swapped": ("int q = (e < 16) ? (qs[e] & 0x0f) : (qs[e - 16] >> 4)",
+                                   "int q = (e < 16) ? (qs[e] >> 4) : (qs[e - 16] & 0x0f)"),
     "q4_0_offset_7": ("d * (float)(q - 8)", "d * (float)(q - 7)"),
     "q4_k_scale_high_bits_wrong_byte": ("*scale = (sc[s + 4] & 0x0f) | ((sc[s - 4] >> 6) << 4);",
                                         "*scale = (sc[s + 4] & 0x0f) | ((sc[s] >> 6) << 4);"),
@@ -38,6 +38,16 @@ MUTANTS = {
                                 "(double)x[i * m + t] * (double)w[i]"),
     "gemv_bound_signed": ("mag += fabs(p);", "mag += p;"),
     "q6_k_d_offset": ("rd_u16(blk + 208)", "rd_u16(blk + 206)"),
+    "q8_0_unsigned_codes": ("int q = (int)(int8_t)blk[2 + e];", "int q = (int)blk[2 + e];"),
+    "q8_0_code_offset": ("int q = (int)(int8_t)blk[2 + e];", "int q = (int)(int8_t)blk[1 + e];"),
+    "q5_0_fifth_bit_low_half_only": ("int hi = (int)((qh >> e) & 1u);",
+                                     "int hi = (int)((qh >> (e % 16)) & 1u);"),
+    "q5_0_offset_15": ("return d * (float)(q - 16);", "return d * (float)(q - 15);"),
+    "q5_0_nibble_halves_swapped": ("int lo = (e < 16) ? (qs[e] & 0x0f) : (qs[e - 16] >> 4);",
+                                   "int lo = (e < 16) ? (qs[e] >> 4) : (qs[e - 16] & 0x0f);"),
+    "q5_0_qh_big_endian": ("uint32_t qh = (uint32_t)blk[2] | ((uint32_t)blk[3] << 8)",
+                           "uint32_t qh = (uint32_t)blk[5] | ((uint32_t)blk[3] << 8)"),
+    "q5_0_codes_at_byte_2": ("const uint8_t *qs = blk + 6;", "const uint8_t *qs = blk + 2;"),
 }
 
 
