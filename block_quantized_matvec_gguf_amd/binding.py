@@ -14,6 +14,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libqmv.so")
 
 QMV_FMT_F16, QMV_FMT_BF16, QMV_FMT_Q4_0, QMV_FMT_Q4_K, QMV_FMT_Q6_K = 1, 2, 3, 4, 5
+QMV_FMT_Q8_0, QMV_FMT_Q5_0 = 6, 7
 QMV_ALGO_AUTO, QMV_ALGO_GEMV, QMV_ALGO_MFMA, QMV_ALGO_SIMPLE = 0, 1, 2, 3
 ALGOS = {"auto": QMV_ALGO_AUTO, "gemv": QMV_ALGO_GEMV, "mfma": QMV_ALGO_MFMA,
          "simple": QMV_ALGO_SIMPLE}

@@ -42,7 +42,9 @@ int64_t block_elems(int fmt) {
     switch (fmt) {
     case QMV_FMT_F16:
     case QMV_FMT_BF16: return 2; // the pages require even k for 16-bit weights
-    case QMV_FMT_Q4_0: return 32;
+    case QMV_FMT_Q4_0:
+    case QMV_FMT_Q8_0:
+    case QMV_FMT_Q5_0: return 32;
     case QMV_FMT_Q4_K:
     case QMV_FMT_Q6_K: return 256;
     default: return -1;
@@ -56,6 +58,8 @@ int64_t row_bytes_of(int fmt, int64_t k) {
     case QMV_FMT_Q4_0: return (k / 32) * 18;
     case QMV_FMT_Q4_K: return (k / 256) * 144;
     case QMV_FMT_Q6_K: return (k / 256) * 210;
+    case QMV_FMT_Q8_0: return (k / 32) * 34;
+    case QMV_FMT_Q5_0: return (k / 32) * 22;
     default: return -1;
     }
 }
@@ -67,6 +71,8 @@ const char *fmt_name(int fmt) {
     case QMV_FMT_Q4_0: return "q4_0";
     case QMV_FMT_Q4_K: return "q4_k";
     case QMV_FMT_Q6_K: return "q6_k";
+    case QMV_FMT_Q8_0: return "q8_0";
+    case QMV_FMT_Q5_0: return "q5_0";
     default: return "?";
     }
 }

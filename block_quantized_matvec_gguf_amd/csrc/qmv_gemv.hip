@@ -22,20 +22,21 @@
 //  * F16/BF16 rows are plain arrays: each lane loads eight 16-byte chunks at a
 //    stride of U chunks, so every load instruction reads one contiguous span
 //    ("direct" kernel).
-//  * Block formats (Q4_0, Q4_K, Q6_K) interleave fields of odd sizes. There
-//    each batch's rows, one contiguous byte range, are copied one batch ahead
-//    straight from memory into a double-buffered LDS area (buffer_load ...
-//    lds, one contiguous kilobyte per wave instruction), from which lanes
-//    read their unit's fields ("staged" kernel). One LDS-only barrier per
-//    batch covers the buffer swap and the cross-group reduction.
+//  * Block formats (Q4_0, Q4_K, Q6_K, Q8_0, Q5_0) interleave fields of odd
+//    sizes. There each batch's rows, one contiguous byte range, are copied
+//    one batch ahead straight from memory into a double-buffered LDS area
+//    (buffer_load ... lds, one contiguous kilobyte per wave instruction),
+//    from which lanes read their unit's fields ("staged" kernel). One
+//    LDS-only barrier per batch covers the buffer swap and the cross-group
+//    reduction.
 //
 // Decode. Codes are masked into bytes and converted with one instruction per
-// weight: Q4_0 and Q6_K codes as signed bytes holding a multiple of q-8 or
-// q-32 (SDWA sign-extended v_cvt_f32_i32), Q4_K codes as unsigned bytes
-// (v_cvt_f32_ubyte0..3). Block scales are applied once per group; the Q4_K min
-// term is applied in factored form, dmin*m*sum(x), with the sums of x
-// precomputed per lane. F16 weights go through v_fma_mix_f32; BF16 is a
-// shift/mask into f32.
+// weight: Q4_0, Q5_0 and Q6_K codes as signed bytes holding a multiple of
+// q-8, q-16 or q-32, Q8_0 codes as they are (SDWA sign-extended
+// v_cvt_f32_i32), Q4_K codes as unsigned bytes (v_cvt_f32_ubyte0..3). Block
+// scales are applied once per group; the Q4_K min term is applied in
+// factored form, dmin*m*sum(x), with the sums of x precomputed per lane. F16
+// weights go through v_fma_mix_f32; BF16 is a shift/mask into f32.
 #include "qmv_internal.h"
 
 #include <map>
@@ -142,9 +143,25 @@ __device__ __forceinline__ void put4(float *d, f32x4 v) {
 // of its byte, where a sign-extending byte conversion yields 16*(q-8)
 // exactly. Summing signed codes keeps the rounding error proportional to
 // sum|w*x| (an all-8 block gives exactly 0).
-struct UQ4_0 {
-    struct Raw { u32x4 q0, q1; uint32_t d0, d1; };
+// x of a unit of two 32-weight blocks whose element e < 16 sits in the low
+// nibble of code byte e and e >= 16 in the high nibble of byte e-16 (Q4_0,
+// Q5_0): piece i = 8b + j of block b is lo[b][4j..] (j < 4) or hi[b][4(j-4)..].
+struct NibbleBlocksX {
     struct X { float lo[2][16], hi[2][16]; };
+    static __device__ __forceinline__ int x4_index(int u, int i, int) { return 16 * u + i; }
+    static __device__ __forceinline__ void x4_slot(int q, int, int &u, int &i) {
+        u = q >> 4;
+        i = q & 15;
+    }
+    static __device__ __forceinline__ void put_x(X &x, int i, f32x4 v) {
+        const int b = i >> 3, j = i & 7;
+        put4(j < 4 ? &x.lo[b][4 * j] : &x.hi[b][4 * (j - 4)], v);
+    }
+    static __device__ __forceinline__ void finish_x(X &) {}
+};
+
+struct UQ4_0 : NibbleBlocksX {
+    struct Raw { u32x4 q0, q1; uint32_t d0, d1; };
     // The unit starts dword aligned (rows are 36*U bytes and every batch
     // starts at a dword multiple in LDS): nine aligned dwords hold both blocks.
     static __device__ __forceinline__ void load_lds(Raw &r, const uint8_t *row, int u) {
@@ -160,16 +177,6 @@ struct UQ4_0 {
         r.d1 = e[4] >> 16;
         r.q1 = u32x4{e[5], e[6], e[7], e[8]};
     }
-    static __device__ __forceinline__ int x4_index(int u, int i, int) { return 16 * u + i; }
-    static __device__ __forceinline__ void x4_slot(int q, int, int &u, int &i) {
-        u = q >> 4;
-        i = q & 15;
-    }
-    static __device__ __forceinline__ void put_x(X &x, int i, f32x4 v) {
-        const int b = i >> 3, j = i & 7;
-        put4(j < 4 ? &x.lo[b][4 * j] : &x.hi[b][4 * (j - 4)], v);
-    }
-    static __device__ __forceinline__ void finish_x(X &) {}
     static __device__ __forceinline__ float block(u32x4 qv, uint32_t dbits, const X &x, int b) {
         const uint32_t q[4] = {qv.x, qv.y, qv.z, qv.w};
         float acc_lo = 0.f, acc_hi = 0.f;
@@ -185,6 +192,103 @@ struct UQ4_0 {
     }
     static __device__ __forceinline__ float dot(const Raw &r, const X &x, int) {
         return block(r.q0, r.d0, x, 0) + block(r.q1, r.d1, x, 1);
+    }
+};
+
+// ------------------------------------------------------------ Q8_0 units
+// A unit is two consecutive 34-byte blocks: f16 d, then 32 signed code bytes
+// in element order; value d*q. Rows are 68*U bytes, so the unit starts dword
+// aligned and 17 aligned dwords hold both blocks (the first block's codes sit
+// 2 bytes off a dword boundary, the second block's on one). The code bytes
+// convert directly with the sign-extending byte conversion.
+struct UQ8_0 {
+    struct Raw { uint32_t q0[8], q1[8]; uint32_t d0, d1; };
+    struct X { float v[2][32]; };
+    static __device__ __forceinline__ void load_lds(Raw &r, const uint8_t *row, int u) {
+        const uint32_t *w = (const uint32_t *)(row + 68 * u);
+        uint32_t e[17];
+#pragma unroll
+        for (int i = 0; i < 17; i++) e[i] = w[i];
+        r.d0 = e[0] & 0xffffu;
+#pragma unroll
+        for (int j = 0; j < 8; j++) r.q0[j] = __builtin_amdgcn_alignbyte(e[j + 1], e[j], 2);
+        r.d1 = e[8] >> 16;
+#pragma unroll
+        for (int j = 0; j < 8; j++) r.q1[j] = e[9 + j];
+    }
+    static __device__ __forceinline__ int x4_index(int u, int i, int) { return 16 * u + i; }
+    static __device__ __forceinline__ void x4_slot(int q, int, int &u, int &i) {
+        u = q >> 4;
+        i = q & 15;
+    }
+    static __device__ __forceinline__ void put_x(X &x, int i, f32x4 v) {
+        put4(&x.v[i >> 3][4 * (i & 7)], v);
+    }
+    static __device__ __forceinline__ void finish_x(X &) {}
+    static __device__ __forceinline__ float block(const uint32_t (&q)[8], uint32_t dbits,
+                                                  const X &x, int b) {
+        float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+        for (int j = 0; j < 8; j += 2) {
+            a0 = sdot4(q[j], &x.v[b][4 * j], a0);
+            a1 = sdot4(q[j + 1], &x.v[b][4 * j + 4], a1);
+        }
+        return f16lo(dbits) * (a0 + a1);
+    }
+    static __device__ __forceinline__ float dot(const Raw &r, const X &x, int) {
+        return block(r.q0, r.d0, x, 0) + block(r.q1, r.d1, x, 1);
+    }
+};
+
+// ------------------------------------------------------------ Q5_0 units
+// A unit is two consecutive 22-byte blocks: f16 d, a little-endian 32-bit
+// word qh, 16 code bytes. Element e takes its low 4 bits from the low nibble
+// of code byte e (e < 16) or the high nibble of byte e-16, and bit e of qh as
+// its fifth bit; value d*(q-16). Rows are 44*U bytes: the unit starts dword
+// aligned and 11 dwords hold both blocks. The signed code q-16 is the 5-bit
+// two's-complement reading of q^16: each nibble goes to bits 3..6 of its byte
+// and the inverted fifth bit to bit 7 (four bits of ~qh are spread to the top
+// of four bytes by one 24-bit multiply: bit i of a 4-bit field times 0x204081
+// lands on bit 8i), so a sign-extending byte conversion yields 8*(q-16).
+struct UQ5_0 : NibbleBlocksX {
+    struct Raw { u32x4 q0, q1; uint32_t h0, h1, d0, d1; };
+    static __device__ __forceinline__ void load_lds(Raw &r, const uint8_t *row, int u) {
+        const uint32_t *w = (const uint32_t *)(row + 44 * u);
+        uint32_t e[11];
+#pragma unroll
+        for (int i = 0; i < 11; i++) e[i] = w[i];
+        r.d0 = e[0] & 0xffffu;
+        r.h0 = __builtin_amdgcn_alignbyte(e[1], e[0], 2);
+        r.q0 = u32x4{__builtin_amdgcn_alignbyte(e[2], e[1], 2),
+                     __builtin_amdgcn_alignbyte(e[3], e[2], 2),
+                     __builtin_amdgcn_alignbyte(e[4], e[3], 2),
+                     __builtin_amdgcn_alignbyte(e[5], e[4], 2)};
+        r.d1 = e[5] >> 16;
+        r.h1 = e[6];
+        r.q1 = u32x4{e[7], e[8], e[9], e[10]};
+    }
+    // bits at..at+3 of nh moved to bits 7, 15, 23, 31 (the multiply is kept
+    // apart from the shift, else the two fold into a quarter-rate 32-bit one)
+    static __device__ __forceinline__ uint32_t spread4(uint32_t nh, int at) {
+        const uint32_t m = opaque(__umul24(__builtin_amdgcn_ubfe(nh, at, 4), 0x204081u));
+        return (m & 0x01010101u) << 7;
+    }
+    static __device__ __forceinline__ float block(u32x4 qv, uint32_t qh, uint32_t dbits,
+                                                  const X &x, int b) {
+        const uint32_t q[4] = {qv.x, qv.y, qv.z, qv.w};
+        const uint32_t nh = ~qh;
+        float acc_lo = 0.f, acc_hi = 0.f;
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            const uint32_t lo = opaque(((q[j] << 3) & 0x78787878u) | spread4(nh, 4 * j));
+            const uint32_t hi = opaque(((q[j] >> 1) & 0x78787878u) | spread4(nh, 16 + 4 * j));
+            acc_lo = sdot4(lo, &x.lo[b][4 * j], acc_lo);
+            acc_hi = sdot4(hi, &x.hi[b][4 * j], acc_hi);
+        }
+        return (f16lo(dbits) * 0.125f) * (acc_lo + acc_hi);
+    }
+    static __device__ __forceinline__ float dot(const Raw &r, const X &x, int) {
+        return block(r.q0, r.h0, r.d0, x, 0) + block(r.q1, r.h1, r.d1, x, 1);
     }
 };
 
@@ -781,7 +885,8 @@ static int gcd_i(int a, int b) {
 }
 
 static bool staged_format(int fmt) {
-    return fmt == FMT_Q4_0 || fmt == FMT_Q4_K || fmt == FMT_Q6_K;
+    return fmt == FMT_Q4_0 || fmt == FMT_Q4_K || fmt == FMT_Q6_K || fmt == FMT_Q8_0 ||
+           fmt == FMT_Q5_0;
 }
 
 static constexpr size_t LDS_BUDGET = 80 * 1024; // weight buffers + reductions
@@ -806,10 +911,23 @@ bool plan_gemv(int fmt, int64_t k, int64_t rows, int mt_max, int num_cu, GemvPla
     while (g.P > 1 && g.P * g.L > 64 && (rows + g.P - 1) / g.P < num_cu) g.P /= 2;
     g.T = g.P * g.L;
     g.MT = (g.UPL == 1 && mt_max >= 2) ? 2 : 1;
-    const int64_t rb = fmt == FMT_F16 || fmt == FMT_BF16 ? 2 * k
-                       : fmt == FMT_Q4_0                ? (k / 32) * 18
-                       : fmt == FMT_Q4_K                ? (k / 256) * 144
-                                                        : (k / 256) * 210;
+    int64_t rb;
+    switch (fmt) {
+    case FMT_F16:
+    case FMT_BF16: rb = 2 * k; break;
+    case FMT_Q4_0: rb = (k / 32) * 18; break;
+    case FMT_Q8_0: rb = (k / 32) * 34; break;
+    case FMT_Q5_0: rb = (k / 32) * 22; break;
+    case FMT_Q4_K:
+        if (k % 256) return false;
+        rb = (k / 256) * 144;
+        break;
+    case FMT_Q6_K:
+        if (k % 256) return false;
+        rb = (k / 256) * 210;
+        break;
+    default: return false;
+    }
     g.staged = staged_format(fmt) ? 1 : 0;
     // Rows per slot per batch: the largest of 2 and 1 that fits the register
     // budget (staged: at most 8 pieces per thread) and the LDS budget,
@@ -983,6 +1101,12 @@ hipError_t launch_gemv(const GemvPlan &p, const uint8_t *W, const float *x, floa
     case FMT_Q6_K:
         return launch_staged<UQ6_K>(p, W, x, y, k, n, row_bytes, j_start, j_end, accumulate,
                                     stream);
+    case FMT_Q8_0:
+        return launch_staged<UQ8_0>(p, W, x, y, k, n, row_bytes, j_start, j_end, accumulate,
+                                    stream);
+    case FMT_Q5_0:
+        return launch_staged<UQ5_0>(p, W, x, y, k, n, row_bytes, j_start, j_end, accumulate,
+                                    stream);
     case FMT_BF16:
         return launch_direct<UHalf<true>>(p, W, x, y, k, n, row_bytes, j_start, j_end,
                                           accumulate, stream);
@@ -994,10 +1118,15 @@ hipError_t launch_gemv(const GemvPlan &p, const uint8_t *W, const float *x, floa
 }
 
 const char *gemv_kernel_name(const GemvPlan &p) {
-    static const char *names[] = {"", "qmv_gemv_direct<f16>", "qmv_gemv_direct<bf16>",
-                                  "qmv_gemv_staged<q4_0>", "qmv_gemv_staged<q4_k>",
-                                  "qmv_gemv_staged<q6_k>"};
-    return (p.fmt >= 1 && p.fmt <= 5) ? names[p.fmt] : "";
+    static const char *names[] = {"",
+                                  "qmv_gemv_direct<f16>",
+                                  "qmv_gemv_direct<bf16>",
+                                  "qmv_gemv_staged<q4_0>",
+                                  "qmv_gemv_staged<q4_k>",
+                                  "qmv_gemv_staged<q6_k>",
+                                  "qmv_gemv_staged<q8_0>",
+                                  "qmv_gemv_staged<q5_0>"};
+    return (p.fmt >= 1 && p.fmt <= 7) ? names[p.fmt] : "";
 }
 
 } // namespace qmv

@@ -7,7 +7,15 @@
 
 namespace qmv {
 
-enum Fmt { FMT_F16 = 1, FMT_BF16 = 2, FMT_Q4_0 = 3, FMT_Q4_K = 4, FMT_Q6_K = 5 };
+enum Fmt {
+    FMT_F16 = 1,
+    FMT_BF16 = 2,
+    FMT_Q4_0 = 3,
+    FMT_Q4_K = 4,
+    FMT_Q6_K = 5,
+    FMT_Q8_0 = 6,
+    FMT_Q5_0 = 7
+};
 
 // Geometry of one streaming-GEMV launch (see qmv_gemv.hip for the mapping).
 struct GemvPlan {

@@ -8,6 +8,9 @@
 // matmul_f16, matmul_bf16): Q4_0 = f16 d + 16 code bytes per 32 weights,
 // Q4_K = f16 d, f16 dmin, 12 bytes of 6-bit scales/mins, 128 code bytes per
 // 256, Q6_K = 128 bytes low bits, 64 bytes high bits, 16 int8 scales, f16 d.
+// Q8_0 = f16 d + 32 signed code bytes per 32 weights, Q5_0 = f16 d, a 32-bit
+// word of fifth bits and 16 code bytes per 32 (the field order of the expert
+// matmul tests in src/backend/dispatch/mod.rs; element order as ggml's).
 #include "qmv_internal.h"
 
 namespace qmv {
@@ -54,6 +57,18 @@ __device__ float simple_weight(int fmt, const uint8_t *row, int64_t i) {
         const int hi = (b[128 + 32 * h + l] >> (2 * g)) & 3;
         const int sc = (int8_t)b[192 + 8 * h + 2 * g + (l >> 4)];
         return half_bits(rd16(b + 208)) * (float)sc * (float)((lo | (hi << 4)) - 32);
+    }
+    case FMT_Q8_0: {
+        const uint8_t *b = row + (i >> 5) * 34;
+        return half_bits(rd16(b)) * (float)(int8_t)b[2 + (i & 31)];
+    }
+    case FMT_Q5_0: {
+        const uint8_t *b = row + (i >> 5) * 22;
+        const int e = (int)(i & 31);
+        const uint32_t qh = rd16(b + 2) | (rd16(b + 4) << 16);
+        const int lo = e < 16 ? (b[6 + e] & 15) : (b[6 + e - 16] >> 4);
+        const int q = lo | (int)(((qh >> e) & 1u) << 4);
+        return half_bits(rd16(b)) * (float)(q - 16);
     }
     default: return 0.f;
     }

@@ -37,20 +37,25 @@ extern "C" {
 
 /* Weight formats. Block sizes: rullama 0.5.0, src/backend/matmul.rs, fns
  * matmul_f16, matmul_bf16 (2 bytes per weight), matmul_q4_0 (18 bytes per 32),
- * matmul_q4_k (144 bytes per 256), matmul_q6_k (210 bytes per 256). */
+ * matmul_q4_k (144 bytes per 256), matmul_q6_k (210 bytes per 256); Q8_0 (34
+ * bytes per 32: f16 d, 32 signed codes) and Q5_0 (22 bytes per 32: f16 d, a
+ * 32-bit word of fifth bits, 16 code bytes) as laid out in the expert-matmul
+ * tests of src/backend/dispatch/mod.rs. */
 enum qmv_format {
     QMV_FMT_F16 = 1,
     QMV_FMT_BF16 = 2,
     QMV_FMT_Q4_0 = 3,
     QMV_FMT_Q4_K = 4,
-    QMV_FMT_Q6_K = 5
+    QMV_FMT_Q6_K = 5,
+    QMV_FMT_Q8_0 = 6,
+    QMV_FMT_Q5_0 = 7
 };
 
 /* Kernel families selectable with qmv_run_ex. */
 enum qmv_algo {
     QMV_ALGO_AUTO = 0,   /* GEMV for small m_tokens, MFMA tiles for prefill-sized m */
     QMV_ALGO_GEMV = 1,   /* streaming matvec; m_tokens handled in small groups    */
-    QMV_ALGO_MFMA = 2,   /* N-token tiles on the bf16 matrix cores, exact codes    */
+    QMV_ALGO_MFMA = 2,   /* N-token tiles on the f16 matrix cores, exact codes     */
     QMV_ALGO_SIMPLE = 3  /* one wave per row, any valid shape (slow, for checks)   */
 };
 
@@ -82,9 +87,10 @@ int qmv_create(void);
  *   x           m_tokens x k f32, token-major, 4-byte aligned.
  *   y           m_tokens x n f32, token-major, 4-byte aligned; indexed by the
  *               absolute row j, not j - j_start.
- *   k           weights per row: a multiple of 32 (Q4_0), 256 (Q4_K, Q6_K) or
- *               2 (F16, BF16) (rullama 0.5.0, src/backend/matmul.rs, the shape
- *               checks of each matmul_* function).
+ *   k           weights per row: a multiple of 32 (Q4_0, Q8_0, Q5_0), 256
+ *               (Q4_K, Q6_K) or 2 (F16, BF16) (rullama 0.5.0,
+ *               src/backend/matmul.rs, the shape checks of each matmul_*
+ *               function).
  *   n           rows of W.
  *   m_tokens    number of tokens (x rows / y rows), >= 0.
  *   j_start, j_end  0 <= j_start <= j_end <= n.
@@ -122,7 +128,8 @@ void qmv_destroy(void);
 /* Bytes of W for n rows of k weights, or -1 if the format is unknown or k is
  * not a whole number of blocks (rullama 0.5.0, src/backend/matmul.rs, the
  * expected byte counts checked by each matmul_* function: k*n*2,
- * (k/32)*18*n, (k/256)*144*n, (k/256)*210*n). Host-only; needs no context. */
+ * (k/32)*18*n, (k/256)*144*n, (k/256)*210*n; and (k/32)*34*n, (k/32)*22*n for
+ * Q8_0 and Q5_0). Host-only; needs no context. */
 int64_t qmv_weight_bytes(int format, int64_t k, int64_t n);
 
 /* Message for the last failing call on this thread (empty if none). The

@@ -16,6 +16,8 @@ from block_quantized_matvec_gguf_amd import synth
 pytestmark = pytest.mark.gpu
 
 F16, BF16, Q4_0, Q4_K, Q6_K = synth.F16, synth.BF16, synth.Q4_0, synth.Q4_K, synth.Q6_K
+Q8_0, Q5_0 = synth.Q8_0, synth.Q5_0
+ALL_FORMATS = [Q4_0, Q4_K, Q6_K, BF16, F16, Q8_0, Q5_0]
 SENTINEL = np.float32(-7777.25)
 
 
@@ -84,18 +86,16 @@ def test_q4_0_small_workload(algo):
 SHAPES = [(256, 37, 1), (768, 1000, 2), (2560, 333, 3), (6400, 129, 1), (512, 1, 1)]
 
 
-@pytest.mark.parametrize("fmt", [Q4_0, Q4_K, Q6_K, BF16, F16],
-                         ids=lambda f: synth.FORMAT_NAMES[f])
+@pytest.mark.parametrize("fmt", ALL_FORMATS, ids=lambda f: synth.FORMAT_NAMES[f])
 @pytest.mark.parametrize("k,n,m", SHAPES)
 @pytest.mark.parametrize("algo", ["gemv", "simple"])
 def test_formats_ragged(fmt, k, n, m, algo):
     check_case(fmt, k, n, m, algo=algo, seed=k * 7 + n + m + fmt)
 
 
-@pytest.mark.parametrize("fmt", [Q4_0, Q4_K, Q6_K, BF16, F16],
-                         ids=lambda f: synth.FORMAT_NAMES[f])
+@pytest.mark.parametrize("fmt", ALL_FORMATS, ids=lambda f: synth.FORMAT_NAMES[f])
 def test_row_range_and_accumulate(fmt):
-    k, n, m = 1280 if fmt in (Q4_0, BF16, F16) else 1536, 777, 2
+    k, n, m = 1280 if fmt in (Q4_0, BF16, F16, Q8_0, Q5_0) else 1536, 777, 2
     check_case(fmt, k, n, m, j0=13, j1=700, seed=5)
     check_case(fmt, k, n, m, j0=100, j1=101, accumulate=True, seed=6)
     check_case(fmt, k, n, m, j0=0, j1=n, accumulate=True, seed=7)
@@ -142,6 +142,42 @@ def test_exact_small_integers(fmt, algo):
     assert np.array_equal(y.astype(np.float64), yref)
 
 
+@pytest.mark.parametrize("fmt", [Q4_0, Q8_0, Q5_0], ids=lambda f: synth.FORMAT_NAMES[f])
+@pytest.mark.parametrize("algo", ["gemv", "simple"])
+def test_exact_32_weight_blocks(fmt, algo):
+    """d = 1 in every block and dyadic x: each code times x and every partial
+    sum is exact in f32 (|sum| < 2^17 in steps of 1/8), so the GPU must equal
+    the oracle bit for bit; a dropped, doubled or misplaced element shows as
+    an exact error."""
+    k, n, m = 1024, 200, 2
+    rng = np.random.default_rng(33 + fmt)
+    W = synth.gen_weights(fmt, rng, n, k)
+    bb = synth.BLOCK[fmt][1]
+    W.reshape(-1, bb)[:, 0:2] = np.array([0x00, 0x3C], np.uint8)  # d = 1
+    x = (rng.integers(-8, 9, size=(m, k)) / 8.0).astype(np.float32)
+    y = run_gpu(fmt, W, x, k, n, np.zeros((m, n), np.float32), algo=algo)
+    yref, _ = oracle.gemv(fmt, W, x, k, n)
+    assert np.array_equal(y.astype(np.float64), yref)
+
+
+@pytest.mark.parametrize("fmt", ALL_FORMATS, ids=lambda f: synth.FORMAT_NAMES[f])
+def test_row_tiling_bit_exact(fmt):
+    """Five uneven row tiles give the untiled bits, writing or (tile 0
+    writes, the rest add) onto zeros."""
+    k, n, m = 1024 if fmt in (Q4_K, Q6_K) else 960, 1500, 2
+    W, x = gen(fmt, k, n, m, 40 + fmt)
+    Wd, xd = dev(W), dev(x)
+    y_un = run_gpu(fmt, W, x, k, n, np.zeros((m, n), np.float32), Wd=Wd, xd=xd)
+    edges = [0, 1, 300, 301, 1100, n]
+    for acc_of, init in ((lambda t: False, SENTINEL), (lambda t: t > 0, 0.0)):
+        yd = dev(np.full((m, n), init, np.float32))
+        for t in range(len(edges) - 1):
+            qb.matvec(fmt, Wd, xd, k, n, y=yd, j_start=edges[t], j_end=edges[t + 1],
+                      accumulate=acc_of(t))
+        torch.cuda.synchronize()
+        assert np.array_equal(yd.cpu().numpy().view(np.uint32), y_un.view(np.uint32))
+
+
 def test_zero_blocks():
     k, n = 512, 64
     blk = np.zeros((n * k // 32, 18), np.uint8)
@@ -153,6 +189,15 @@ def test_zero_blocks():
     W = synth.gen_q6_k(np.random.default_rng(4), n, k)
     W.reshape(-1, 210)[:, 208:210] = 0  # d = 0
     y = run_gpu(Q6_K, W, x, k, n, np.full((1, n), SENTINEL, np.float32))
+    assert not np.any(y)
+    blk = np.zeros((n * k // 32, 34), np.uint8)
+    blk[:, 0:2] = np.array([0x00, 0x3C], np.uint8)  # d = 1, every code 0
+    y = run_gpu(Q8_0, blk.reshape(-1), x, k, n, np.full((1, n), SENTINEL, np.float32))
+    assert not np.any(y)
+    blk = np.zeros((n * k // 32, 22), np.uint8)
+    blk[:, 0:2] = np.array([0x00, 0x3C], np.uint8)  # d = 1
+    blk[:, 2:6] = 0xFF  # every fifth bit set, every low nibble 0: q = 16
+    y = run_gpu(Q5_0, blk.reshape(-1), x, k, n, np.full((1, n), SENTINEL, np.float32))
     assert not np.any(y)
 
 
@@ -178,7 +223,7 @@ def test_empty_and_degenerate():
 
 
 @pytest.mark.parametrize("fmt,k,n", [(Q4_0, 96, 50), (F16, 10, 33), (BF16, 2, 5),
-                                     (F16, 72, 20)])
+                                     (F16, 72, 20), (Q8_0, 96, 21), (Q5_0, 32, 17)])
 def test_shapes_only_the_simple_kernel_covers(fmt, k, n):
     check_case(fmt, k, n, 2, algo="auto", seed=k + n)
     W, x = gen(fmt, k, n, 1, 1)
@@ -188,7 +233,9 @@ def test_shapes_only_the_simple_kernel_covers(fmt, k, n):
 
 
 @pytest.mark.parametrize("fmt,k,n,m", [(Q4_K, 65536, 40, 1), (Q6_K, 16384, 100, 2),
-                                       (BF16, 40960, 24, 1), (Q4_0, 12800, 64, 3)])
+                                       (BF16, 40960, 24, 1), (Q4_0, 12800, 64, 3),
+                                       (Q8_0, 32768, 20, 1), (Q5_0, 40960, 16, 1),
+                                       (Q5_0, 12800, 70, 2)])
 def test_long_rows(fmt, k, n, m):
     """Long rows: two units per lane and/or x loaded straight from global
     memory instead of LDS."""
@@ -219,7 +266,8 @@ def test_run_to_run_determinism():
 
 # ------------------------------------------------------- measured workloads
 
-@pytest.mark.parametrize("name", ["bf16_ffn_up", "f16_ffn_up", "q4_k_ffn_up"])
+@pytest.mark.parametrize("name", ["bf16_ffn_up", "f16_ffn_up", "q4_k_ffn_up", "q8_0_ffn_up",
+                                  "q5_0_ffn_up"])
 def test_ffn_up_workloads_full(name):
     """k=2560, n=10240, m=1, every output against the oracle."""
     f, W, x, spec = synth.workload(name)

@@ -50,7 +50,12 @@ def test_weight_bytes(lib):
     assert qb.qmv_weight_bytes(qb.QMV_FMT_Q6_K, 128, 1) == -1
     assert qb.qmv_weight_bytes(qb.QMV_FMT_F16, 3, 1) == -1
     assert qb.qmv_weight_bytes(9, 256, 1) == -1
+    assert qb.qmv_weight_bytes(8, 256, 1) == -1
     assert qb.qmv_weight_bytes(qb.QMV_FMT_Q4_0, 0, 7) == 0
+    assert qb.qmv_weight_bytes(qb.QMV_FMT_Q8_0, 2560, 10240) == 80 * 34 * 10240
+    assert qb.qmv_weight_bytes(qb.QMV_FMT_Q5_0, 2560, 10240) == 80 * 22 * 10240
+    assert qb.qmv_weight_bytes(qb.QMV_FMT_Q8_0, 48, 1) == -1
+    assert qb.qmv_weight_bytes(qb.QMV_FMT_Q5_0, 16, 1) == -1
 
 
 def test_status_strings(lib):
@@ -70,6 +75,10 @@ def test_kernel_names(lib):
     assert qb.qmv_kernel_name(qb.QMV_FMT_Q4_K, 4096, 15) == "qmv_gemv_staged<q4_k>"
     assert qb.qmv_kernel_name(qb.QMV_FMT_Q4_K, 256, 1, qb.QMV_ALGO_MFMA) == "qmv_mfma<q4_k>"
     assert qb.qmv_kernel_name(qb.QMV_FMT_BF16, 4096, 64, qb.QMV_ALGO_MFMA) == ""
+    assert qb.qmv_kernel_name(qb.QMV_FMT_Q8_0, 2560, 1) == "qmv_gemv_staged<q8_0>"
+    assert qb.qmv_kernel_name(qb.QMV_FMT_Q5_0, 2560, 1) == "qmv_gemv_staged<q5_0>"
+    assert qb.qmv_kernel_name(qb.QMV_FMT_Q5_0, 2560, 64) == "qmv_gemv_staged<q5_0>"
+    assert qb.qmv_kernel_name(qb.QMV_FMT_Q8_0, 32, 1) == "qmv_simple"
 
 
 def _run(**kw):
