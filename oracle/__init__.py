@@ -72,6 +72,10 @@ def load_library(path: str):
     lib.oracle_gemv_range.argtypes = [c_int, c_vp, c_vp, c_i64, c_i64, c_i64, c_i64, c_i64,
                                       c_vp, c_vp]
     lib.oracle_gemv_range.restype = c_int
+    if hasattr(lib, "oracle_gemv_t_cols"):
+        lib.oracle_gemv_t_cols.argtypes = [c_int, c_vp, c_vp, c_i64, c_i64, c_i64, c_i64, c_i64,
+                                           c_vp, c_i64, c_vp, c_vp]
+        lib.oracle_gemv_t_cols.restype = c_int
     return lib
 
 
@@ -192,6 +196,64 @@ def gemv(fmt: int, W: np.ndarray, x: np.ndarray, k: int, n: int, j_start: int = 
         j_end = n
     return gemv_rows(fmt, W, x, k, n, np.arange(j_start, j_end, dtype=np.int64),
                      threads=threads)
+
+
+def gemv_t_cols(fmt: int, W: np.ndarray, dy: np.ndarray, k: int, n: int, cols,
+                j_start: int = 0, j_end: int | None = None, threads: int | None = None):
+    """dx, s of the transposed product for the listed columns: arrays of shape
+    (m, len(cols)) in f64, dx[t, c] = sum_{j_start <= j < j_end} dy[t, j] *
+    w_j[cols[c]].
+
+    dy is (m, n) or (n,) float32.
+    """
+    lib = _load()
+    if j_end is None:
+        j_end = n
+    W = np.ascontiguousarray(W, dtype=np.uint8).reshape(-1)
+    dy = np.ascontiguousarray(dy, dtype=np.float32)
+    dy2 = dy.reshape(1, -1) if dy.ndim == 1 else dy
+    m = dy2.shape[0]
+    if dy2.shape[1] != n:
+        raise ValueError("dy has %d columns, expected n=%d" % (dy2.shape[1], n))
+    rb = row_bytes(fmt, k)
+    if rb < 0 or W.size < rb * n:
+        raise ValueError("bad format/k or short W")
+    cols = np.ascontiguousarray(np.asarray(cols, dtype=np.int64).reshape(-1))
+    nc = cols.size
+    dx = np.empty((m, nc), dtype=np.float64)
+    s = np.empty((m, nc), dtype=np.float64)
+    nt = min(_threads(threads), max(1, nc))
+    bounds = [nc * i // nt for i in range(nt + 1)]
+
+    def work(i):
+        a, b = bounds[i], bounds[i + 1]
+        if b <= a:
+            return 0
+        sub = np.ascontiguousarray(cols[a:b])
+        ds = np.empty((m, b - a), dtype=np.float64)
+        ss = np.empty((m, b - a), dtype=np.float64)
+        rc = lib.oracle_gemv_t_cols(fmt, _ptr(W), _ptr(dy2), k, n, m, j_start, j_end, _ptr(sub),
+                                    b - a, _ptr(ds), _ptr(ss))
+        if rc == 0:
+            dx[:, a:b] = ds
+            s[:, a:b] = ss
+        return rc
+
+    if nt == 1:
+        rcs = [work(0)]
+    else:
+        with ThreadPoolExecutor(max_workers=nt) as ex:
+            rcs = list(ex.map(work, range(nt)))
+    if any(rc != 0 for rc in rcs):
+        raise ValueError("oracle_gemv_t_cols failed: %r" % (rcs,))
+    return dx, s
+
+
+def gemv_t(fmt: int, W: np.ndarray, dy: np.ndarray, k: int, n: int, j_start: int = 0,
+           j_end: int | None = None, threads: int | None = None):
+    """dx, s of the transposed product for all k columns, each (m, k) f64."""
+    return gemv_t_cols(fmt, W, dy, k, n, np.arange(k, dtype=np.int64), j_start, j_end,
+                       threads=threads)
 
 
 def cosine(a: np.ndarray, b: np.ndarray) -> float:

@@ -13,6 +13,14 @@
  *     y[t][j] = sum_{i<k} x[t][i] * w_j[i]
  *     s[t][j] = sum_{i<k} |x[t][i] * w_j[i]|        (the tolerance scale)
  *
+ * and the transposed (backward-input) product over a row range, as the
+ * backward-input kernels of dispatch/mod.rs compute it (struct
+ * MatmulBackInputParams: j_start..j_end bounds the summed row axis; the CPU
+ * reference of its parity tests maps dy of length n to dx of length k):
+ *
+ *     dx[t][i] = sum_{j0<=j<j1} dy[t][j] * w_j[i]
+ *     s[t][i]  = sum_{j0<=j<j1} |dy[t][j] * w_j[i]|
+ *
  * Every weight is first decoded to an f32 value, element by element, then the
  * sum runs serially over i in f64. There is no blocking, no factoring of the
  * block scales and no reordering: the decode of element i of row j looks up
@@ -298,4 +306,38 @@ int oracle_gemv_range(int fmt, const uint8_t *W, const float *x, int64_t k, int6
     int rc = oracle_gemv_rows(fmt, W, x, k, n, m, rows, nr, y, s);
     free(rows);
     return rc;
+}
+
+/* ------------------------------------------------------- transposed gemv */
+
+/* For each listed column i = cols[c] and each token t < m:
+ *   dx[t*ncols + c] = sum_{j0 <= j < j1} dy[t*n + j] * w_j[i]   (f64, serial in j)
+ *   s[t*ncols + c]  = sum_{j0 <= j < j1} |dy[t*n + j] * w_j[i]|
+ * W holds n rows of row_bytes(fmt, k) bytes; dy is m rows of n f32. Every
+ * weight is decoded on its own (oracle_elem). s may be NULL. Returns 0, or -1
+ * on bad arguments. */
+int oracle_gemv_t_cols(int fmt, const uint8_t *W, const float *dy, int64_t k, int64_t n,
+                       int64_t m, int64_t j0, int64_t j1, const int64_t *cols, int64_t ncols,
+                       double *dx, double *s)
+{
+    int64_t rb = oracle_row_bytes(fmt, k);
+    if (rb < 0 || n < 0 || m < 0 || ncols < 0 || j0 < 0 || j1 < j0 || j1 > n)
+        return -1;
+    for (int64_t c = 0; c < ncols; c++) {
+        int64_t i = cols[c];
+        if (i < 0 || i >= k)
+            return -1;
+        for (int64_t t = 0; t < m; t++) {
+            double acc = 0.0, mag = 0.0;
+            for (int64_t j = j0; j < j1; j++) {
+                double p = (double)dy[t * n + j] * (double)oracle_elem(fmt, W + j * rb, i);
+                acc += p;
+                mag += fabs(p);
+            }
+            dx[t * ncols + c] = acc;
+            if (s)
+                s[t * ncols + c] = mag;
+        }
+    }
+    return 0;
 }

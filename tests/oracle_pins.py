@@ -530,4 +530,63 @@ def pin_pages_q4_0_case():
     assert np.max(np.abs(y - _factored_q4_0(W, x, k, n))) < 1e-4
 
 
+# ------------------------------------------------ transposed product pins
+
+def pin_t_adjoint_of_forward():
+    """u . (W v) = (W^T u) . v: the transposed oracle is the adjoint of the
+    (separately pinned) forward oracle, to f64 rounding."""
+    rng = np.random.default_rng(24)
+    for fmt, k, n in ((Q4_K, 512, 13), (Q6_K, 256, 9), (Q4_0, 96, 11), (Q8_0, 64, 7),
+                      (Q5_0, 128, 10), (F16, 48, 6), (BF16, 40, 5)):
+        W = _random_matrix(fmt, n, k, 800 + fmt)
+        v = rng.uniform(-1, 1, size=(1, k)).astype(np.float32)
+        u = rng.uniform(-1, 1, size=(2, n)).astype(np.float32)
+        yf, sf = oracle.gemv(fmt, W, v, k, n)                    # (1, n)
+        dx, sx = oracle.gemv_t(fmt, W, u, k, n)                  # (2, k)
+        for t in range(2):
+            lhs = float(np.dot(u[t].astype(np.float64), yf[0]))
+            rhs = float(np.dot(dx[t], v[0].astype(np.float64)))
+            bound = float(np.dot(np.abs(u[t]).astype(np.float64), sf[0]))
+            assert abs(lhs - rhs) <= 1e-12 * bound + 1e-300, (fmt, t, lhs, rhs)
+
+
+def pin_t_onehot_rows():
+    """dy = e_j gives dx = w_j (the decoded row) exactly, and zeros when j
+    lies outside the summed range."""
+    for fmt, k, n in ((Q4_K, 256, 6), (Q6_K, 256, 5), (Q4_0, 64, 7), (Q8_0, 32, 4),
+                      (Q5_0, 64, 5), (BF16, 16, 3)):
+        W = _random_matrix(fmt, n, k, 900 + fmt)
+        dense = oracle.dequant(fmt, W, k, n).astype(np.float64)
+        dy = np.eye(n, dtype=np.float32)
+        dx, s = oracle.gemv_t(fmt, W, dy, k, n)
+        assert np.array_equal(dx, dense), fmt
+        assert np.array_equal(s, np.abs(dense)), fmt
+        dx, _ = oracle.gemv_t(fmt, W, dy, k, n, 1, n - 1)
+        assert not np.any(dx[0]) and not np.any(dx[n - 1]), fmt
+        assert np.array_equal(dx[1:n - 1], dense[1:n - 1]), fmt
+
+
+def pin_t_dense_route_and_ranges():
+    """A library f64 product of the decoded matrix agrees with the oracle; a
+    split of the row range adds up; an empty range is zero."""
+    rng = np.random.default_rng(25)
+    for fmt, k, n in ((Q4_K, 512, 21), (Q6_K, 256, 33), (Q5_0, 96, 17)):
+        W = _random_matrix(fmt, n, k, 1000 + fmt)
+        dy = rng.uniform(-1, 1, size=(3, n)).astype(np.float32)
+        dense = oracle.dequant(fmt, W, k, n).astype(np.float64)
+        dx, s = oracle.gemv_t(fmt, W, dy, k, n)
+        want = dy.astype(np.float64) @ dense
+        assert np.all(np.abs(dx - want) <= 1e-12 * s + 1e-300), fmt
+        a, _ = oracle.gemv_t(fmt, W, dy, k, n, 0, 7)
+        b, _ = oracle.gemv_t(fmt, W, dy, k, n, 7, n)
+        assert np.all(np.abs(a + b - dx) <= 1e-12 * s + 1e-300), fmt
+        want_a = dy[:, 0:7].astype(np.float64) @ dense[0:7]
+        assert np.all(np.abs(a - want_a) <= 1e-12 * s + 1e-300), fmt
+        e, es = oracle.gemv_t(fmt, W, dy, k, n, 5, 5)
+        assert not np.any(e) and not np.any(es)
+        cols = [k - 1, 0, 3, 3]
+        c, cs = oracle.gemv_t_cols(fmt, W, dy, k, n, cols)
+        assert np.array_equal(c, dx[:, cols]) and np.array_equal(cs, s[:, cols])
+
+
 ALL_PINS = [v for name, v in sorted(globals().items()) if name.startswith("pin_")]

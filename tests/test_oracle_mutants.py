@@ -36,7 +36,10 @@ MUTANTS = {
                               "for (int64_t i = 1; i < k; i++) {\n                double p"),
     "gemv_x_index_transposed": ("(double)x[t * k + i] * (double)w[i]",
                                 "(double)x[i * m + t] * (double)w[i]"),
-    "gemv_bound_signed": ("mag += fabs(p);", "mag += p;"),
+    "gemv_bound_signed": ("mag += fabs(p);\n            }\n            y[t * nrows + r]",
+                          "mag += p;\n            }\n            y[t * nrows + r]"),
+    "gemv_t_bound_signed": ("mag += fabs(p);\n            }\n            dx[t * ncols + c]",
+                            "mag += p;\n            }\n            dx[t * ncols + c]"),
     "q6_k_d_offset": ("rd_u16(blk + 208)", "rd_u16(blk + 206)"),
     "q8_0_unsigned_codes": ("int q = (int)(int8_t)blk[2 + e];", "int q = (int)blk[2 + e];"),
     "q8_0_code_offset": ("int q = (int)(int8_t)blk[2 + e];", "int q = (int)(int8_t)blk[1 + e];"),
@@ -48,6 +51,13 @@ MUTANTS = {
     "q5_0_qh_big_endian": ("uint32_t qh = (uint32_t)blk[2] | ((uint32_t)blk[3] << 8)",
                            "uint32_t qh = (uint32_t)blk[5] | ((uint32_t)blk[3] << 8)"),
     "q5_0_codes_at_byte_2": ("const uint8_t *qs = blk + 6;", "const uint8_t *qs = blk + 2;"),
+    "gemv_t_dy_index_transposed": ("(double)dy[t * n + j] * (double)oracle_elem",
+                                   "(double)dy[j * m + t] * (double)oracle_elem"),
+    "gemv_t_range_inclusive": ("for (int64_t j = j0; j < j1; j++) {\n                double p = (double)dy",
+                               "for (int64_t j = j0; j <= j1 && j < n; j++) {\n                double p = (double)dy"),
+    "gemv_t_skips_first_row": ("for (int64_t j = j0; j < j1; j++) {\n                double p = (double)dy",
+                               "for (int64_t j = j0 + 1; j < j1; j++) {\n                double p = (double)dy"),
+    "gemv_t_row_as_column": ("oracle_elem(fmt, W + j * rb, i)", "oracle_elem(fmt, W + i * rb, j % k)"),
 }
 
 
