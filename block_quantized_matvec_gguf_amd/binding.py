@@ -68,6 +68,12 @@ def load(path: str | None = None):
         lib.qmv_status_string.restype = ctypes.c_char_p
         lib.qmv_kernel_name.argtypes = [ci, i64, i64, ci]
         lib.qmv_kernel_name.restype = ctypes.c_char_p
+        lib.qmv_run_t.argtypes = run_args
+        lib.qmv_run_t.restype = ci
+        lib.qmv_run_t_ex.argtypes = run_args + [ci]
+        lib.qmv_run_t_ex.restype = ci
+        lib.qmv_t_kernel_name.argtypes = [ci, i64, ci]
+        lib.qmv_t_kernel_name.restype = ctypes.c_char_p
         _lib = lib
         return lib
 
@@ -93,6 +99,23 @@ def qmv_run_ex(format: int, W: int, x: int, y: int, k: int, n: int, m_tokens: in
                algo: int) -> int:
     return int(load().qmv_run_ex(format, W, x, y, k, n, m_tokens, j_start, j_end, accumulate,
                                  stream, algo))
+
+
+def qmv_run_t(format: int, W: int, dy: int, dx: int, k: int, n: int, m_tokens: int,
+              j_start: int, j_end: int, accumulate: int, stream: int | None) -> int:
+    return int(load().qmv_run_t(format, W, dy, dx, k, n, m_tokens, j_start, j_end, accumulate,
+                                stream))
+
+
+def qmv_run_t_ex(format: int, W: int, dy: int, dx: int, k: int, n: int, m_tokens: int,
+                 j_start: int, j_end: int, accumulate: int, stream: int | None,
+                 algo: int) -> int:
+    return int(load().qmv_run_t_ex(format, W, dy, dx, k, n, m_tokens, j_start, j_end,
+                                   accumulate, stream, algo))
+
+
+def qmv_t_kernel_name(format: int, k: int, algo: int = QMV_ALGO_AUTO) -> str:
+    return load().qmv_t_kernel_name(format, k, algo).decode()
 
 
 def qmv_weight_bytes(format: int, k: int, n: int) -> int:
@@ -132,6 +155,51 @@ def _fmt(fmt) -> int:
     return fmt_id(fmt)
 
 
+def _check_w(f, W, k, n):
+    import torch
+    if W.dtype != torch.uint8 or not W.is_cuda or not W.is_contiguous():
+        raise ValueError("W must be a contiguous uint8 CUDA tensor")
+    want = qmv_weight_bytes(f, k, n)
+    if want < 0 or W.numel() != want:
+        raise ValueError("W has %d bytes, expected %d for format %d k=%d n=%d"
+                         % (W.numel(), want, f, k, n))
+
+
+def matvec_t(fmt, W, dy, k: int, n: int, dx=None, j_start: int = 0, j_end: int | None = None,
+             accumulate: bool = False, algo="auto", stream=None):
+    """dx (=|+=) dy @ W[j_start:j_end] on the GPU (the transposed product).
+
+    W as for matvec; dy: float32 CUDA tensor (m, n) or (n,); dx: float32 CUDA
+    tensor (m, k) (allocated when None). Enqueued on `stream` (default:
+    torch's current stream); returns dx.
+    """
+    import torch
+    f = _fmt(fmt)
+    a = ALGOS[algo] if isinstance(algo, str) else int(algo)
+    if j_end is None:
+        j_end = n
+    _check_w(f, W, k, n)
+    if dy.dtype != torch.float32 or not dy.is_cuda or not dy.is_contiguous():
+        raise ValueError("dy must be a contiguous float32 CUDA tensor")
+    dy2 = dy.reshape(1, -1) if dy.dim() == 1 else dy
+    if dy2.shape[1] != n:
+        raise ValueError("dy has %d columns, expected n=%d" % (dy2.shape[1], n))
+    m = dy2.shape[0]
+    if dx is None:
+        dx = torch.empty((m, k), dtype=torch.float32, device=dy.device)
+    if dx.dtype != torch.float32 or not dx.is_cuda or not dx.is_contiguous() or \
+            dx.numel() != m * k:
+        raise ValueError("dx must be a contiguous float32 CUDA tensor of m*k elements")
+    ensure_context()
+    s = stream if stream is not None else torch.cuda.current_stream(dy.device)
+    with torch.cuda.device(dy.device):
+        rc = qmv_run_t_ex(f, W.data_ptr(), dy2.data_ptr(), dx.data_ptr(), k, n, m, j_start,
+                          j_end, 1 if accumulate else 0, s.cuda_stream, a)
+    if rc != QMV_OK:
+        raise QmvError(rc, qmv_last_error())
+    return dx
+
+
 def matvec(fmt, W, x, k: int, n: int, y=None, j_start: int = 0, j_end: int | None = None,
            accumulate: bool = False, algo="auto", stream=None):
     """y (=|+=) x @ W on the GPU for rows [j_start, j_end).
@@ -145,12 +213,7 @@ def matvec(fmt, W, x, k: int, n: int, y=None, j_start: int = 0, j_end: int | Non
     a = ALGOS[algo] if isinstance(algo, str) else int(algo)
     if j_end is None:
         j_end = n
-    if W.dtype != torch.uint8 or not W.is_cuda or not W.is_contiguous():
-        raise ValueError("W must be a contiguous uint8 CUDA tensor")
-    want = qmv_weight_bytes(f, k, n)
-    if want < 0 or W.numel() != want:
-        raise ValueError("W has %d bytes, expected %d for format %d k=%d n=%d"
-                         % (W.numel(), want, f, k, n))
+    _check_w(f, W, k, n)
     if x.dtype != torch.float32 or not x.is_cuda or not x.is_contiguous():
         raise ValueError("x must be a contiguous float32 CUDA tensor")
     x2 = x.reshape(1, -1) if x.dim() == 1 else x

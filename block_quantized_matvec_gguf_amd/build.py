@@ -15,7 +15,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libqmv.so")
-SOURCES = ["qmv_api.cpp", "qmv_gemv.hip", "qmv_simple.hip", "qmv_mfma.hip"]
+SOURCES = ["qmv_api.cpp", "qmv_gemv.hip", "qmv_gemv_t.hip", "qmv_simple.hip", "qmv_mfma.hip"]
 ARCH = "gfx950"
 
 

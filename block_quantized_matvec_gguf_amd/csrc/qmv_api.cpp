@@ -94,6 +94,19 @@ int resolve_algo(int fmt, int64_t k, int64_t m, int algo) {
     }
 }
 
+// Kernel family of a transposed request; -1 when the explicit choice cannot
+// serve the shape.
+int resolve_algo_t(int fmt, int64_t k, int algo) {
+    qmv::GemvTPlan tp;
+    const bool stream_ok = qmv::plan_gemv_t(fmt, k, 1 << 20, 256, &tp);
+    switch (algo) {
+    case QMV_ALGO_AUTO: return stream_ok ? QMV_ALGO_GEMV : QMV_ALGO_SIMPLE;
+    case QMV_ALGO_GEMV: return stream_ok ? QMV_ALGO_GEMV : -1;
+    case QMV_ALGO_SIMPLE: return QMV_ALGO_SIMPLE;
+    default: return -1;
+    }
+}
+
 } // namespace
 
 extern "C" {
@@ -272,6 +285,99 @@ int qmv_run(int format, const void *W, const float *x, float *y, int64_t k, int6
             int64_t m_tokens, int64_t j_start, int64_t j_end, int accumulate, void *stream) {
     return qmv_run_ex(format, W, x, y, k, n, m_tokens, j_start, j_end, accumulate, stream,
                       QMV_ALGO_AUTO);
+}
+
+} // extern "C"
+
+extern "C" {
+
+const char *qmv_t_kernel_name(int format, int64_t k, int algo) {
+    thread_local std::string name;
+    if (block_elems(format) <= 0 || k <= 0 || k % block_elems(format) != 0) return "";
+    const int a = resolve_algo_t(format, k, algo);
+    if (a == QMV_ALGO_GEMV) {
+        qmv::GemvTPlan p;
+        qmv::plan_gemv_t(format, k, 1 << 20, 256, &p);
+        name = qmv::gemv_t_kernel_name(p);
+    } else if (a == QMV_ALGO_SIMPLE) {
+        name = "qmv_simple_t";
+    } else {
+        name = "";
+    }
+    return name.c_str();
+}
+
+int qmv_run_t_ex(int format, const void *W, const float *dy, float *dx, int64_t k, int64_t n,
+                 int64_t m_tokens, int64_t j_start, int64_t j_end, int accumulate,
+                 void *stream, int algo) {
+    t_err.clear();
+    const int64_t qk = block_elems(format);
+    if (qk <= 0) return fail(QMV_ERR_INVALID_ARGUMENT, "unknown format %d", format);
+    if (k < 0 || n < 0 || m_tokens < 0)
+        return fail(QMV_ERR_INVALID_ARGUMENT, "negative shape k=%lld n=%lld m=%lld",
+                    (long long)k, (long long)n, (long long)m_tokens);
+    if (k % qk != 0)
+        return fail(QMV_ERR_INVALID_ARGUMENT, "k %lld must be a multiple of %lld for %s",
+                    (long long)k, (long long)qk, fmt_name(format));
+    if (j_start < 0 || j_end < j_start || j_end > n)
+        return fail(QMV_ERR_INVALID_ARGUMENT, "row range [%lld, %lld) outside [0, %lld)",
+                    (long long)j_start, (long long)j_end, (long long)n);
+    if (accumulate != 0 && accumulate != 1)
+        return fail(QMV_ERR_INVALID_ARGUMENT, "accumulate must be 0 or 1, got %d", accumulate);
+    if (algo != QMV_ALGO_AUTO && algo != QMV_ALGO_GEMV && algo != QMV_ALGO_SIMPLE)
+        return fail(QMV_ERR_INVALID_ARGUMENT, "algo %d has no transposed form", algo);
+    // every dx entry is written (or, with accumulate, added to) unless the
+    // sum is empty and accumulating, or there is no output at all
+    const bool sum = j_end > j_start;
+    const bool work = m_tokens > 0 && k > 0 && (sum || !accumulate);
+    if (work) {
+        if (!dx) return fail(QMV_ERR_INVALID_ARGUMENT, "dx is NULL");
+        if (sum && (!W || !dy)) return fail(QMV_ERR_INVALID_ARGUMENT, "W or dy is NULL");
+        if (((uintptr_t)W & 15) != 0)
+            return fail(QMV_ERR_MISALIGNED, "W must be 16-byte aligned");
+        if (((uintptr_t)dy & 3) != 0 || ((uintptr_t)dx & 3) != 0)
+            return fail(QMV_ERR_MISALIGNED, "dy and dx must be 4-byte aligned");
+    }
+    if (g_refs.load() <= 0)
+        return fail(QMV_ERR_NOT_INITIALIZED, "qmv_run_t before qmv_create");
+    if (!work) return QMV_OK;
+
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(QMV_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+    if (dev < 0 || (size_t)dev >= g_dev.size() || !g_dev[(size_t)dev].gfx950)
+        return fail(QMV_ERR_UNSUPPORTED_ARCH, "device %d is not gfx950", dev);
+    const int num_cu = g_dev[(size_t)dev].num_cu;
+    hipStream_t s = (hipStream_t)stream;
+    if (!sum) {
+        e = qmv::launch_fill_zero_all(dx, m_tokens * k, s);
+        if (e != hipSuccess) return fail(QMV_ERR_HIP, "fill launch: %s", hipGetErrorString(e));
+        return QMV_OK;
+    }
+    const int a = resolve_algo_t(format, k, algo);
+    if (a < 0)
+        return fail(QMV_ERR_UNSUPPORTED, "algo %d cannot serve the transposed %s with k=%lld",
+                    algo, fmt_name(format), (long long)k);
+    const uint8_t *Wb = (const uint8_t *)W;
+    const int64_t rb = row_bytes_of(format, k);
+    if (a == QMV_ALGO_SIMPLE) {
+        e = qmv::launch_simple_t(format, Wb, dy, dx, k, n, m_tokens, rb, j_start, j_end,
+                                 accumulate, s);
+        if (e != hipSuccess) return fail(QMV_ERR_HIP, "simple launch: %s", hipGetErrorString(e));
+        return QMV_OK;
+    }
+    qmv::GemvTPlan p;
+    if (!qmv::plan_gemv_t(format, k, j_end - j_start, num_cu, &p))
+        return fail(QMV_ERR_UNSUPPORTED, "transposed plan failed");
+    e = qmv::launch_gemv_t(p, Wb, dy, dx, k, n, m_tokens, rb, j_start, j_end, accumulate, s);
+    if (e != hipSuccess) return fail(QMV_ERR_HIP, "transposed launch: %s", hipGetErrorString(e));
+    return QMV_OK;
+}
+
+int qmv_run_t(int format, const void *W, const float *dy, float *dx, int64_t k, int64_t n,
+              int64_t m_tokens, int64_t j_start, int64_t j_end, int accumulate, void *stream) {
+    return qmv_run_t_ex(format, W, dy, dx, k, n, m_tokens, j_start, j_end, accumulate, stream,
+                        QMV_ALGO_AUTO);
 }
 
 } // extern "C"

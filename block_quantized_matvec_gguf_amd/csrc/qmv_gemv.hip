@@ -38,447 +38,13 @@
 // factored form, dmin*m*sum(x), with the sums of x precomputed per lane. F16
 // weights go through v_fma_mix_f32; BF16 is a shift/mask into f32.
 #include "qmv_internal.h"
+#include "qmv_units.h"
 
 #include <map>
 #include <mutex>
 #include <utility>
 
 namespace qmv {
-
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-// LDS reads at 2-byte alignment (block fields): single ds_read_b128/b64.
-typedef uint32_t u32x4h __attribute__((ext_vector_type(4), aligned(2)));
-typedef uint32_t u32x2h __attribute__((ext_vector_type(2), aligned(2)));
-
-__device__ __forceinline__ u32x4 ld16(const uint8_t *p) {
-    return __builtin_nontemporal_load((const u32x4 *)p);
-}
-__device__ __forceinline__ u32x4 lds16(const uint8_t *p) {
-    const u32x4h v = *(const u32x4h *)p;
-    return u32x4{v.x, v.y, v.z, v.w};
-}
-__device__ __forceinline__ u32x2 lds8(const uint8_t *p) {
-    const u32x2h v = *(const u32x2h *)p;
-    return u32x2{v.x, v.y};
-}
-__device__ __forceinline__ uint32_t lds2(const uint8_t *p) { return *(const uint16_t *)p; }
-// LDS serves 16- and 8-byte reads that are not naturally aligned, but only
-// with a large stall, so fields of the 2-byte aligned block formats are read
-// as the dwords covering them (ds_read2_b32) and shifted into place with
-// v_alignbyte_b32. The dword after a field is read even when the field is
-// dword aligned; it lies inside the LDS allocation and is then not used.
-__device__ __forceinline__ u32x4 lds16u(const uint8_t *p) {
-    const uint32_t sh = (uint32_t)(uintptr_t)p & 3u;
-    const uint32_t *d = (const uint32_t *)(p - sh);
-    const uint32_t w0 = d[0], w1 = d[1], w2 = d[2], w3 = d[3], w4 = d[4];
-    return u32x4{__builtin_amdgcn_alignbyte(w1, w0, sh), __builtin_amdgcn_alignbyte(w2, w1, sh),
-                 __builtin_amdgcn_alignbyte(w3, w2, sh), __builtin_amdgcn_alignbyte(w4, w3, sh)};
-}
-__device__ __forceinline__ u32x2 lds8u(const uint8_t *p) {
-    const uint32_t sh = (uint32_t)(uintptr_t)p & 3u;
-    const uint32_t *d = (const uint32_t *)(p - sh);
-    const uint32_t w0 = d[0], w1 = d[1], w2 = d[2];
-    return u32x2{__builtin_amdgcn_alignbyte(w1, w0, sh), __builtin_amdgcn_alignbyte(w2, w1, sh)};
-}
-
-// Keeps the compiler from folding a byte mask into per-element bit-field
-// extracts, so that the byte conversions select v_cvt_f32_{ubyte,i32 sdwa}.
-__device__ __forceinline__ uint32_t opaque(uint32_t v) {
-    asm("" : "+v"(v));
-    return v;
-}
-__device__ __forceinline__ float ub0(uint32_t v) { return (float)(v & 0xffu); }
-__device__ __forceinline__ float ub1(uint32_t v) { return (float)((v >> 8) & 0xffu); }
-__device__ __forceinline__ float ub2(uint32_t v) { return (float)((v >> 16) & 0xffu); }
-__device__ __forceinline__ float ub3(uint32_t v) { return (float)(v >> 24); }
-__device__ __forceinline__ float sb0(uint32_t v) { return (float)(int)(int8_t)(v & 0xffu); }
-__device__ __forceinline__ float sb1(uint32_t v) { return (float)(int)(int8_t)((v >> 8) & 0xffu); }
-__device__ __forceinline__ float sb2(uint32_t v) { return (float)(int)(int8_t)((v >> 16) & 0xffu); }
-__device__ __forceinline__ float sb3(uint32_t v) { return (float)((int)v >> 24); }
-__device__ __forceinline__ float f16lo(uint32_t v) {
-    return (float)__builtin_bit_cast(_Float16, (uint16_t)(v & 0xffffu));
-}
-__device__ __forceinline__ float f16hi(uint32_t v) {
-    return (float)__builtin_bit_cast(_Float16, (uint16_t)(v >> 16));
-}
-// acc + sum_b byte_b(q) * x[b]
-__device__ __forceinline__ float dot4(uint32_t q, const float *x, float acc) {
-    acc = fmaf(ub0(q), x[0], acc);
-    acc = fmaf(ub1(q), x[1], acc);
-    acc = fmaf(ub2(q), x[2], acc);
-    acc = fmaf(ub3(q), x[3], acc);
-    return acc;
-}
-// acc + sum_b signed_byte_b(q) * x[b]
-__device__ __forceinline__ float sdot4(uint32_t q, const float *x, float acc) {
-    acc = fmaf(sb0(q), x[0], acc);
-    acc = fmaf(sb1(q), x[1], acc);
-    acc = fmaf(sb2(q), x[2], acc);
-    acc = fmaf(sb3(q), x[3], acc);
-    return acc;
-}
-__device__ __forceinline__ void put4(float *d, f32x4 v) {
-    d[0] = v.x;
-    d[1] = v.y;
-    d[2] = v.z;
-    d[3] = v.w;
-}
-
-// Each unit type below provides
-//   Raw                 registers holding one unit of one row
-//   load_lds / load     read them from the staged row in LDS / from global memory
-//   X, x4_index, x4_slot, put_x, finish_x
-//                       the unit's 64 x values as 16 float4 pieces: piece i of
-//                       unit u is float4 number x4_index(u, i) of x; x4_slot
-//                       is the inverse
-//   dot                 the unit's contribution to the row's dot product
-
-// ------------------------------------------------------------ Q4_0 units
-// A unit is two consecutive 18-byte blocks. Block layout: f16 d, 16 code
-// bytes; element e < 16 is the low nibble of byte e, e >= 16 the high nibble
-// of byte e-16; value d*(q-8). The signed code q-8 is the 4-bit two's
-// complement reading of q^8: each nibble is XORed with 8 and moved to the top
-// of its byte, where a sign-extending byte conversion yields 16*(q-8)
-// exactly. Summing signed codes keeps the rounding error proportional to
-// sum|w*x| (an all-8 block gives exactly 0).
-// x of a unit of two 32-weight blocks whose element e < 16 sits in the low
-// nibble of code byte e and e >= 16 in the high nibble of byte e-16 (Q4_0,
-// Q5_0): piece i = 8b + j of block b is lo[b][4j..] (j < 4) or hi[b][4(j-4)..].
-struct NibbleBlocksX {
-    struct X { float lo[2][16], hi[2][16]; };
-    static __device__ __forceinline__ int x4_index(int u, int i, int) { return 16 * u + i; }
-    static __device__ __forceinline__ void x4_slot(int q, int, int &u, int &i) {
-        u = q >> 4;
-        i = q & 15;
-    }
-    static __device__ __forceinline__ void put_x(X &x, int i, f32x4 v) {
-        const int b = i >> 3, j = i & 7;
-        put4(j < 4 ? &x.lo[b][4 * j] : &x.hi[b][4 * (j - 4)], v);
-    }
-    static __device__ __forceinline__ void finish_x(X &) {}
-};
-
-struct UQ4_0 : NibbleBlocksX {
-    struct Raw { u32x4 q0, q1; uint32_t d0, d1; };
-    // The unit starts dword aligned (rows are 36*U bytes and every batch
-    // starts at a dword multiple in LDS): nine aligned dwords hold both blocks.
-    static __device__ __forceinline__ void load_lds(Raw &r, const uint8_t *row, int u) {
-        const uint32_t *w = (const uint32_t *)(row + 36 * u);
-        uint32_t e[9];
-#pragma unroll
-        for (int i = 0; i < 9; i++) e[i] = w[i];
-        r.d0 = e[0] & 0xffffu;
-        r.q0 = u32x4{__builtin_amdgcn_alignbyte(e[1], e[0], 2),
-                     __builtin_amdgcn_alignbyte(e[2], e[1], 2),
-                     __builtin_amdgcn_alignbyte(e[3], e[2], 2),
-                     __builtin_amdgcn_alignbyte(e[4], e[3], 2)};
-        r.d1 = e[4] >> 16;
-        r.q1 = u32x4{e[5], e[6], e[7], e[8]};
-    }
-    static __device__ __forceinline__ float block(u32x4 qv, uint32_t dbits, const X &x, int b) {
-        const uint32_t q[4] = {qv.x, qv.y, qv.z, qv.w};
-        float acc_lo = 0.f, acc_hi = 0.f;
-#pragma unroll
-        for (int j = 0; j < 4; j++) {
-            // bytes of 16*(q-8): low nibbles moved up, then both XOR 8 in the top nibble
-            const uint32_t lo = opaque(((q[j] << 4) ^ 0x80808080u) & 0xf0f0f0f0u);
-            const uint32_t hi = opaque((q[j] ^ 0x80808080u) & 0xf0f0f0f0u);
-            acc_lo = sdot4(lo, &x.lo[b][4 * j], acc_lo);
-            acc_hi = sdot4(hi, &x.hi[b][4 * j], acc_hi);
-        }
-        return (f16lo(dbits) * 0.0625f) * (acc_lo + acc_hi);
-    }
-    static __device__ __forceinline__ float dot(const Raw &r, const X &x, int) {
-        return block(r.q0, r.d0, x, 0) + block(r.q1, r.d1, x, 1);
-    }
-};
-
-// ------------------------------------------------------------ Q8_0 units
-// A unit is two consecutive 34-byte blocks: f16 d, then 32 signed code bytes
-// in element order; value d*q. Rows are 68*U bytes, so the unit starts dword
-// aligned and 17 aligned dwords hold both blocks (the first block's codes sit
-// 2 bytes off a dword boundary, the second block's on one). The code bytes
-// convert directly with the sign-extending byte conversion.
-struct UQ8_0 {
-    struct Raw { uint32_t q0[8], q1[8]; uint32_t d0, d1; };
-    struct X { float v[2][32]; };
-    static __device__ __forceinline__ void load_lds(Raw &r, const uint8_t *row, int u) {
-        const uint32_t *w = (const uint32_t *)(row + 68 * u);
-        uint32_t e[17];
-#pragma unroll
-        for (int i = 0; i < 17; i++) e[i] = w[i];
-        r.d0 = e[0] & 0xffffu;
-#pragma unroll
-        for (int j = 0; j < 8; j++) r.q0[j] = __builtin_amdgcn_alignbyte(e[j + 1], e[j], 2);
-        r.d1 = e[8] >> 16;
-#pragma unroll
-        for (int j = 0; j < 8; j++) r.q1[j] = e[9 + j];
-    }
-    static __device__ __forceinline__ int x4_index(int u, int i, int) { return 16 * u + i; }
-    static __device__ __forceinline__ void x4_slot(int q, int, int &u, int &i) {
-        u = q >> 4;
-        i = q & 15;
-    }
-    static __device__ __forceinline__ void put_x(X &x, int i, f32x4 v) {
-        put4(&x.v[i >> 3][4 * (i & 7)], v);
-    }
-    static __device__ __forceinline__ void finish_x(X &) {}
-    static __device__ __forceinline__ float block(const uint32_t (&q)[8], uint32_t dbits,
-                                                  const X &x, int b) {
-        float a0 = 0.f, a1 = 0.f;
-#pragma unroll
-        for (int j = 0; j < 8; j += 2) {
-            a0 = sdot4(q[j], &x.v[b][4 * j], a0);
-            a1 = sdot4(q[j + 1], &x.v[b][4 * j + 4], a1);
-        }
-        return f16lo(dbits) * (a0 + a1);
-    }
-    static __device__ __forceinline__ float dot(const Raw &r, const X &x, int) {
-        return block(r.q0, r.d0, x, 0) + block(r.q1, r.d1, x, 1);
-    }
-};
-
-// ------------------------------------------------------------ Q5_0 units
-// A unit is two consecutive 22-byte blocks: f16 d, a little-endian 32-bit
-// word qh, 16 code bytes. Element e takes its low 4 bits from the low nibble
-// of code byte e (e < 16) or the high nibble of byte e-16, and bit e of qh as
-// its fifth bit; value d*(q-16). Rows are 44*U bytes: the unit starts dword
-// aligned and 11 dwords hold both blocks. The signed code q-16 is the 5-bit
-// two's-complement reading of q^16: each nibble goes to bits 3..6 of its byte
-// and the inverted fifth bit to bit 7 (four bits of ~qh are spread to the top
-// of four bytes by one 24-bit multiply: bit i of a 4-bit field times 0x204081
-// lands on bit 8i), so a sign-extending byte conversion yields 8*(q-16).
-struct UQ5_0 : NibbleBlocksX {
-    struct Raw { u32x4 q0, q1; uint32_t h0, h1, d0, d1; };
-    static __device__ __forceinline__ void load_lds(Raw &r, const uint8_t *row, int u) {
-        const uint32_t *w = (const uint32_t *)(row + 44 * u);
-        uint32_t e[11];
-#pragma unroll
-        for (int i = 0; i < 11; i++) e[i] = w[i];
-        r.d0 = e[0] & 0xffffu;
-        r.h0 = __builtin_amdgcn_alignbyte(e[1], e[0], 2);
-        r.q0 = u32x4{__builtin_amdgcn_alignbyte(e[2], e[1], 2),
-                     __builtin_amdgcn_alignbyte(e[3], e[2], 2),
-                     __builtin_amdgcn_alignbyte(e[4], e[3], 2),
-                     __builtin_amdgcn_alignbyte(e[5], e[4], 2)};
-        r.d1 = e[5] >> 16;
-        r.h1 = e[6];
-        r.q1 = u32x4{e[7], e[8], e[9], e[10]};
-    }
-    // bits at..at+3 of nh moved to bits 7, 15, 23, 31 (the multiply is kept
-    // apart from the shift, else the two fold into a quarter-rate 32-bit one)
-    static __device__ __forceinline__ uint32_t spread4(uint32_t nh, int at) {
-        const uint32_t m = opaque(__umul24(__builtin_amdgcn_ubfe(nh, at, 4), 0x204081u));
-        return (m & 0x01010101u) << 7;
-    }
-    static __device__ __forceinline__ float block(u32x4 qv, uint32_t qh, uint32_t dbits,
-                                                  const X &x, int b) {
-        const uint32_t q[4] = {qv.x, qv.y, qv.z, qv.w};
-        const uint32_t nh = ~qh;
-        float acc_lo = 0.f, acc_hi = 0.f;
-#pragma unroll
-        for (int j = 0; j < 4; j++) {
-            const uint32_t lo = opaque(((q[j] << 3) & 0x78787878u) | spread4(nh, 4 * j));
-            const uint32_t hi = opaque(((q[j] >> 1) & 0x78787878u) | spread4(nh, 16 + 4 * j));
-            acc_lo = sdot4(lo, &x.lo[b][4 * j], acc_lo);
-            acc_hi = sdot4(hi, &x.hi[b][4 * j], acc_hi);
-        }
-        return (f16lo(dbits) * 0.125f) * (acc_lo + acc_hi);
-    }
-    static __device__ __forceinline__ float dot(const Raw &r, const X &x, int) {
-        return block(r.q0, r.h0, r.d0, x, 0) + block(r.q1, r.h1, r.d1, x, 1);
-    }
-};
-
-// ------------------------------------------------------------ Q4_K units
-// A unit is one 64-weight chunk c of a 144-byte super-block: its 32 code
-// bytes (low nibbles = sub-block 2c, high nibbles = sub-block 2c+1) plus the
-// 16-byte head (f16 d, f16 dmin, 12 bytes of packed 6-bit scales/mins).
-struct UQ4_K {
-    struct Raw { u32x4 hd, q0, q1; };
-    struct X { float lo[32], hi[32]; float slo, shi; };
-    static __device__ __forceinline__ void load_lds(Raw &r, const uint8_t *row, int u) {
-        const uint8_t *sb = row + 144 * (u >> 2);
-        const int c = u & 3;
-        r.hd = lds16(sb);
-        r.q0 = lds16(sb + 16 + 32 * c);
-        r.q1 = lds16(sb + 32 + 32 * c);
-    }
-    static __device__ __forceinline__ int x4_index(int u, int i, int) { return 16 * u + i; }
-    static __device__ __forceinline__ void x4_slot(int q, int, int &u, int &i) {
-        u = q >> 4;
-        i = q & 15;
-    }
-    static __device__ __forceinline__ void put_x(X &x, int i, f32x4 v) {
-        put4(i < 8 ? &x.lo[4 * i] : &x.hi[4 * (i - 8)], v);
-    }
-    static __device__ __forceinline__ void finish_x(X &x) {
-        float a = 0.f, b = 0.f;
-        for (int i = 0; i < 32; i++) a += x.lo[i];
-        for (int i = 0; i < 32; i++) b += x.hi[i];
-        x.slo = a;
-        x.shi = b;
-    }
-    // 6-bit scale and min of sub-block s from the packed dwords d1..d3
-    // (head bytes 4..15). s < 4: low 6 bits of byte s (scale) and byte s+4
-    // (min). s >= 4: low 4 bits from the nibbles of byte s+4, top 2 bits
-    // from the top bits of byte s-4 (scale) and byte s (min).
-    static __device__ __forceinline__ void scale_min(uint32_t d1, uint32_t d2, uint32_t d3,
-                                                     int s, uint32_t &sc, uint32_t &mn) {
-        const bool low = s < 4;
-        const int t = 8 * (s & 3);
-        const uint32_t a = low ? d1 : d3, b = low ? d2 : d3;
-        const int sa = t, sb = low ? t : t + 4, hs = low ? t + 4 : t + 6;
-        sc = ((a >> sa) & 15u) | (((d1 >> hs) & 3u) << 4);
-        mn = ((b >> sb) & 15u) | (((d2 >> hs) & 3u) << 4);
-    }
-    static __device__ __forceinline__ float dot(const Raw &r, const X &x, int u) {
-        const uint32_t q[8] = {r.q0.x, r.q0.y, r.q0.z, r.q0.w, r.q1.x, r.q1.y, r.q1.z, r.q1.w};
-        float acc_lo = 0.f, acc_hi = 0.f;
-#pragma unroll
-        for (int i = 0; i < 8; i++) {
-            const uint32_t lo = opaque(q[i] & 0x0f0f0f0fu), hi = opaque(q[i] & 0xf0f0f0f0u);
-            acc_lo = dot4(lo, &x.lo[4 * i], acc_lo);
-            acc_hi = dot4(hi, &x.hi[4 * i], acc_hi); // 16x the high nibble
-        }
-        const int s0 = 2 * (u & 3);
-        uint32_t sc0, mn0, sc1, mn1;
-        scale_min(r.hd.y, r.hd.z, r.hd.w, s0, sc0, mn0);
-        scale_min(r.hd.y, r.hd.z, r.hd.w, s0 + 1, sc1, mn1);
-        const float d = f16lo(r.hd.x), dmin = f16hi(r.hd.x);
-        const float f0 = d * (float)sc0;
-        const float f1 = (d * 0.0625f) * (float)sc1;
-        const float mt = dmin * fmaf((float)mn1, x.shi, (float)mn0 * x.slo);
-        return fmaf(f1, acc_hi, fmaf(f0, acc_lo, -mt));
-    }
-};
-
-// ------------------------------------------------------------ Q6_K units
-// A unit is (super-block, half h, lane block lq): the 64 weights
-// 128h + 32g + 16lq + i (g < 4, i < 16). Their low 4 bits are bytes
-// ql[64h + 16lq + i] (g = 0 low nibble, g = 2 high nibble) and
-// ql[64h + 32 + 16lq + i] (g = 1, 3), their top 2 bits are bits 2g..2g+1 of
-// qh[32h + 16lq + i], and their scales are the int8 scales[8h + 2g + lq].
-// Super-blocks are 210 bytes, so fields may sit 2 bytes off a dword
-// boundary (read through lds16u/lds8u). The signed code q-32 is the 6-bit
-// two's-complement reading of q^32: the high 2-bit fields are XORed with
-// 0b10, the 6-bit code is assembled in the top of its byte, and a
-// sign-extending byte conversion yields 4*(q-32).
-struct UQ6_K {
-    struct Raw { u32x4 a, b, h; u32x2 s; uint32_t d; };
-    struct X { float v[4][16]; };
-    static __device__ __forceinline__ void load_lds(Raw &r, const uint8_t *row, int u) {
-        const uint8_t *o = row + 210 * (u >> 2);
-        const int h = (u >> 1) & 1, lq = u & 1;
-        r.a = lds16u(o + 64 * h + 16 * lq);
-        r.b = lds16u(o + 64 * h + 32 + 16 * lq);
-        r.h = lds16u(o + 128 + 32 * h + 16 * lq);
-        r.s = lds8u(o + 192 + 8 * h);
-        r.d = lds2(o + 208);
-    }
-    // piece i = 4g + i4 holds weights 128h + 32g + 16lq + 4i4 .. +3
-    static __device__ __forceinline__ int x4_index(int u, int i, int) {
-        return 64 * (u >> 2) + 32 * ((u >> 1) & 1) + 8 * (i >> 2) + 4 * (u & 1) + (i & 3);
-    }
-    static __device__ __forceinline__ void x4_slot(int q, int, int &u, int &i) {
-        u = 4 * (q >> 6) + 2 * ((q >> 5) & 1) + ((q >> 2) & 1);
-        i = 4 * ((q >> 3) & 3) + (q & 3);
-    }
-    static __device__ __forceinline__ void put_x(X &x, int i, f32x4 v) {
-        put4(&x.v[i >> 2][4 * (i & 3)], v);
-    }
-    static __device__ __forceinline__ void finish_x(X &) {}
-    static __device__ __forceinline__ float dot(const Raw &r, const X &x, int u) {
-        const uint32_t A[4] = {r.a.x, r.a.y, r.a.z, r.a.w};
-        const uint32_t B[4] = {r.b.x, r.b.y, r.b.z, r.b.w};
-        const uint32_t H[4] = {r.h.x, r.h.y, r.h.z, r.h.w};
-        float acc[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int j = 0; j < 4; j++) {
-            const uint32_t h = H[j] ^ 0xaaaaaaaau; // top bit of every 2-bit field flipped
-            // bytes of 4*(q-32) for quarters g = 0..3
-            const uint32_t q0 = opaque(((A[j] << 2) & 0x3c3c3c3cu) | ((h << 6) & 0xc0c0c0c0u));
-            const uint32_t q1 = opaque(((B[j] << 2) & 0x3c3c3c3cu) | ((h << 4) & 0xc0c0c0c0u));
-            const uint32_t q2 = opaque(((A[j] >> 2) & 0x3c3c3c3cu) | ((h << 2) & 0xc0c0c0c0u));
-            const uint32_t q3 = opaque(((B[j] >> 2) & 0x3c3c3c3cu) | (h & 0xc0c0c0c0u));
-            acc[0] = sdot4(q0, &x.v[0][4 * j], acc[0]);
-            acc[1] = sdot4(q1, &x.v[1][4 * j], acc[1]);
-            acc[2] = sdot4(q2, &x.v[2][4 * j], acc[2]);
-            acc[3] = sdot4(q3, &x.v[3][4 * j], acc[3]);
-        }
-        const int lq8 = 8 * (u & 1);
-        const float d = f16lo(r.d) * 0.25f;
-        // the scale bytes are signed: extract with sign extension, convert as int
-        const float s0 = (float)(int)__builtin_amdgcn_sbfe((int)r.s.x, lq8, 8);
-        const float s1 = (float)(int)__builtin_amdgcn_sbfe((int)r.s.x, lq8 + 16, 8);
-        const float s2 = (float)(int)__builtin_amdgcn_sbfe((int)r.s.y, lq8, 8);
-        const float s3 = (float)(int)__builtin_amdgcn_sbfe((int)r.s.y, lq8 + 16, 8);
-        float r0 = (d * s0) * acc[0];
-        r0 = fmaf(d * s1, acc[1], r0);
-        r0 = fmaf(d * s2, acc[2], r0);
-        return fmaf(d * s3, acc[3], r0);
-    }
-};
-
-// ------------------------------------------------------- F16 / BF16 units
-// A unit is the eight 8-weight chunks u, u+U, ..., u+7U of the row (16 bytes
-// each), so that for a fixed chunk index the lanes of a slot read one
-// contiguous span straight from global memory.
-template <bool BF>
-struct UHalf {
-    struct Raw { u32x4 c[8]; };
-    struct X { float v[8][8]; };
-    static __device__ __forceinline__ void load(Raw &r, const uint8_t *row, int u, int U) {
-#pragma unroll
-        for (int c = 0; c < 8; c++) r.c[c] = ld16(row + 16 * (u + U * c));
-    }
-    // piece i = 2c + hf holds weights 8(u + cU) + 4hf .. +3
-    static __device__ __forceinline__ int x4_index(int u, int i, int U) {
-        return 2 * (u + U * (i >> 1)) + (i & 1);
-    }
-    static __device__ __forceinline__ void x4_slot(int q, int U, int &u, int &i) {
-        const int chunk = q >> 1;
-        const int c = chunk / U;
-        u = chunk - c * U;
-        i = 2 * c + (q & 1);
-    }
-    static __device__ __forceinline__ void put_x(X &x, int i, f32x4 v) {
-        put4(&x.v[i >> 1][4 * (i & 1)], v);
-    }
-    static __device__ __forceinline__ void finish_x(X &) {}
-    static __device__ __forceinline__ float dot(const Raw &r, const X &x, int) {
-        float acc0 = 0.f, acc1 = 0.f;
-#pragma unroll
-        for (int c = 0; c < 8; c++) {
-            const uint32_t w[4] = {r.c[c].x, r.c[c].y, r.c[c].z, r.c[c].w};
-#pragma unroll
-            for (int j = 0; j < 4; j++) {
-                float lo, hi;
-                if (BF) {
-                    lo = __builtin_bit_cast(float, w[j] << 16);
-                    hi = __builtin_bit_cast(float, w[j] & 0xffff0000u);
-                } else {
-                    lo = f16lo(w[j]);
-                    hi = f16hi(w[j]);
-                }
-                acc0 = fmaf(lo, x.v[c][2 * j], acc0);
-                acc1 = fmaf(hi, x.v[c][2 * j + 1], acc1);
-            }
-        }
-        return acc0 + acc1;
-    }
-};
-
-// ------------------------------------------------------ shared device code
-// Workgroup barrier that orders LDS only: global loads in flight (the next
-// batch of weights) are not drained, unlike __syncthreads().
-__device__ __forceinline__ void lds_barrier() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
 
 // Sum over aligned groups of G lanes (G a power of two <= 16); every lane of
 // a group ends with the group sum. Order of additions is fixed.
@@ -494,28 +60,6 @@ __device__ __forceinline__ float group_sum(float v, int G) {
     if (G >= 16) v += dpp_mov<0x140>(v); // row_mirror
     return v;
 }
-
-// Lane geometry common to both kernels.
-template <int UPL>
-struct Lanes {
-    int tid, T, slot, lane, NG;
-    int uid[UPL];  // units owned by this lane
-    int ulod[UPL]; // unit actually read: padding lanes re-read a valid unit
-    bool uvalid[UPL];
-    __device__ __forceinline__ Lanes(int U, int L, int G) {
-        tid = threadIdx.x;
-        T = blockDim.x;
-        slot = tid / L;
-        lane = tid - slot * L;
-        NG = L / G;
-#pragma unroll
-        for (int i = 0; i < UPL; i++) {
-            uid[i] = lane + i * L;
-            uvalid[i] = uid[i] < U;
-            ulod[i] = uvalid[i] ? uid[i] : U - 1;
-        }
-    }
-};
 
 // x, first part: coalesced float4 loads into registers (4 per thread; the
 // index is clamped so the loads are unconditional and their count is known).
@@ -766,9 +310,6 @@ __global__ __launch_bounds__(512) void qmv_gemv_direct(const uint8_t *__restrict
 // descriptor's range check is a second guard), so a buffer holds exactly the
 // largest batch. The copy of batch i+1 runs while batch i is decoded and is
 // waited for at the end-of-batch barrier. XL: x goes through LDS.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t batch_rsrc(const uint8_t *p, int bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc((void *)p, (short)0, bytes, 0x00020000);
-}
 
 // Single-token, one-row-per-slot instances fit in 128 registers without
 // spilling, i.e. 4 waves per SIMD; the others are left to the compiler.
@@ -856,7 +397,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(
 #pragma unroll
             for (int i = 0; i < UPL; i++) {
                 typename F::Raw raw;
-                F::load_lds(raw, row, ln.ulod[i]);
+                F::load_lds(raw, row, ln.ulod[i], U);
 #pragma unroll
                 for (int t = 0; t < MT; t++)
                     if (live && ln.uvalid[i]) part[r][t] += F::dot(raw, xu[t][i], ln.uid[i]);
@@ -978,25 +519,6 @@ bool plan_gemv(int fmt, int64_t k, int64_t rows, int mt_max, int num_cu, GemvPla
     if (g.lds_bytes > 160 * 1024) return false;
     *p = g;
     return true;
-}
-
-// Resident workgroups per compute unit for one kernel at a given block size
-// and LDS size (cached: the query only reads kernel metadata).
-template <typename K>
-static int resident_per_cu(K kernel, int T, size_t lds) {
-    static std::mutex mu;
-    static std::map<std::pair<int, size_t>, int> cache;
-    std::lock_guard<std::mutex> lk(mu);
-    auto it = cache.find({T, lds});
-    if (it != cache.end()) return it->second;
-    int nb = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, kernel, T, lds) != hipSuccess ||
-        nb < 1) {
-        (void)hipGetLastError();
-        nb = 1;
-    }
-    cache[{T, lds}] = nb;
-    return nb;
 }
 
 template <typename K>

@@ -46,6 +46,19 @@ struct MfmaPlan {
     size_t lds_bytes;
 };
 
+// Geometry of one transposed-product launch (see qmv_gemv_t.hip).
+struct GemvTPlan {
+    int fmt;
+    int U, UPL, L; // as in GemvPlan
+    int P;         // row slots per workgroup (a power of two)
+    int T;         // threads per workgroup (P * L)
+    int npt;       // 16-byte weight pieces per thread per batch
+    int buf_bytes; // bytes of one LDS weight buffer
+    int grid;      // workgroups wanted; the launch caps it at residency
+    int num_cu;
+    size_t lds_bytes;
+};
+
 // Fill the geometry for a GEMV launch of up to mt_max tokens over `rows` rows.
 // Returns false when the shape is outside what the streaming kernel covers.
 bool plan_gemv(int fmt, int64_t k, int64_t rows, int mt_max, int num_cu, GemvPlan *p);
@@ -61,6 +74,17 @@ hipError_t launch_simple(int fmt, const uint8_t *W, const float *x, float *y, in
 
 hipError_t launch_fill_zero(float *y, int64_t n, int64_t m, int64_t j_start, int64_t j_end,
                             hipStream_t stream);
+
+// Transposed product dx (=|+=) W^T dy over rows [j_start, j_end), per token.
+bool plan_gemv_t(int fmt, int64_t k, int64_t rows, int num_cu, GemvTPlan *p);
+hipError_t launch_gemv_t(const GemvTPlan &p, const uint8_t *W, const float *dy, float *dx,
+                         int64_t k, int64_t n, int64_t m, int64_t row_bytes, int64_t j_start,
+                         int64_t j_end, int accumulate, hipStream_t stream);
+const char *gemv_t_kernel_name(const GemvTPlan &p);
+hipError_t launch_simple_t(int fmt, const uint8_t *W, const float *dy, float *dx, int64_t k,
+                           int64_t n, int64_t m, int64_t row_bytes, int64_t j_start,
+                           int64_t j_end, int accumulate, hipStream_t stream);
+hipError_t launch_fill_zero_all(float *v, int64_t count, hipStream_t stream);
 
 bool plan_mfma(int fmt, int64_t k, int64_t rows, int64_t m, int num_cu, MfmaPlan *p);
 hipError_t launch_mfma(const MfmaPlan &p, const uint8_t *W, const float *x, float *y,

@@ -109,6 +109,46 @@ hipError_t launch_simple(int fmt, const uint8_t *W, const float *x, float *y, in
     return hipGetLastError();
 }
 
+// Transposed product, one thread per output (t, i): the rows of the range
+// in order, every weight decoded on its own, the sum kept in f64.
+__global__ __launch_bounds__(256) void qmv_simple_t(const uint8_t *__restrict__ W,
+                                                     const float *__restrict__ dy,
+                                                     float *__restrict__ dx, int64_t k, int64_t n,
+                                                     int64_t m, int64_t row_bytes, int64_t j0,
+                                                     int64_t j1, int accumulate, int fmt) {
+    const int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (q >= m * k) return;
+    const int64_t t = q / k, i = q - t * k;
+    double acc = 0.0;
+    for (int64_t j = j0; j < j1; j++)
+        acc += (double)dy[t * n + j] * (double)simple_weight(fmt, W + j * row_bytes, i);
+    dx[q] = accumulate ? dx[q] + (float)acc : (float)acc;
+}
+
+hipError_t launch_simple_t(int fmt, const uint8_t *W, const float *dy, float *dx, int64_t k,
+                           int64_t n, int64_t m, int64_t row_bytes, int64_t j_start,
+                           int64_t j_end, int accumulate, hipStream_t stream) {
+    const int64_t blocks = (m * k + 255) / 256;
+    if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(qmv_simple_t, dim3((unsigned)blocks), dim3(256), 0, stream, W, dy, dx, k,
+                       n, m, row_bytes, j_start, j_end, accumulate, fmt);
+    return hipGetLastError();
+}
+
+__global__ __launch_bounds__(256) void qmv_fill_zero_all(float *__restrict__ v, int64_t count) {
+    for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < count;
+         q += (int64_t)gridDim.x * blockDim.x)
+        v[q] = 0.f;
+}
+
+hipError_t launch_fill_zero_all(float *v, int64_t count, hipStream_t stream) {
+    int64_t blocks = (count + 255) / 256;
+    if (blocks > 4096) blocks = 4096;
+    if (blocks < 1) blocks = 1;
+    hipLaunchKernelGGL(qmv_fill_zero_all, dim3((unsigned)blocks), dim3(256), 0, stream, v, count);
+    return hipGetLastError();
+}
+
 __global__ __launch_bounds__(256) void qmv_fill_zero(float *__restrict__ y, int64_t n,
                                                       int64_t m, int64_t j0, int64_t j1) {
     const int64_t rows = j1 - j0;

@@ -121,6 +121,44 @@ int qmv_run_ex(int format, const void *W, const float *x, float *y, int64_t k, i
                int64_t m_tokens, int64_t j_start, int64_t j_end, int accumulate,
                void *stream, int algo);
 
+/* Enqueue the transposed (backward-input) product over a row range on
+ * `stream`, kernel family chosen automatically:
+ *
+ *     dx[t*k + i] (=|+=) sum_{j_start <= j < j_end} dy[t*n + j] * w_j[i]
+ *
+ * for every token t < m_tokens and every i < k (rullama 0.5.0,
+ * src/backend/dispatch/mod.rs, struct MatmulBackInputParams: the range bounds
+ * the summed row axis so that a vocabulary-sized product can be cut into
+ * several calls, the first with accumulate = 0, the others with accumulate =
+ * 1; the CPU reference of the backward-input parity tests maps dy of length n
+ * to dx of length k).
+ *
+ *   format, W, k, n  as for qmv_run.
+ *   dy          m_tokens x n f32, token-major, 4-byte aligned; indexed by the
+ *               absolute row j.
+ *   dx          m_tokens x k f32, token-major, 4-byte aligned; every entry is
+ *               written (accumulate = 0) or added to (accumulate = 1).
+ *   j_start, j_end  0 <= j_start <= j_end <= n; an empty range is an empty
+ *               sum (dx = 0, or unchanged when accumulating).
+ *
+ * Returns QMV_OK after a successful enqueue, else the same codes as qmv_run.
+ * The streaming family takes stream-ordered scratch of at most 4 MiB * k /
+ * 1024 (one partial dx per workgroup, hipMallocAsync / hipFreeAsync on
+ * `stream`; QMV_ERR_HIP if that fails) and is deterministic run to run; a
+ * split of the range into tiles changes the rounding, not the accuracy
+ * contract (|error| <= 1e-4 * sum_j |dy_j * w_j[i]|). */
+int qmv_run_t(int format, const void *W, const float *dy, float *dx, int64_t k, int64_t n,
+              int64_t m_tokens, int64_t j_start, int64_t j_end, int accumulate,
+              void *stream);
+
+/* qmv_run_t with an explicit kernel family: QMV_ALGO_GEMV (streaming; k a
+ * multiple of 64 up to 65536, else QMV_ERR_UNSUPPORTED) or QMV_ALGO_SIMPLE
+ * (one thread per output, any valid shape, f64 sums; slow, for checks).
+ * QMV_ALGO_MFMA is QMV_ERR_INVALID_ARGUMENT here. */
+int qmv_run_t_ex(int format, const void *W, const float *dy, float *dx, int64_t k,
+                 int64_t n, int64_t m_tokens, int64_t j_start, int64_t j_end,
+                 int accumulate, void *stream, int algo);
+
 /* Release one reference to the context; the last one frees it. Safe to call
  * when not initialised. Must not race with qmv_run or qmv_create. */
 void qmv_destroy(void);
@@ -143,6 +181,9 @@ const char *qmv_status_string(int status);
  * when the request is invalid. Host-only; needs no context or device. Used
  * to find the launch in profiler output. */
 const char *qmv_kernel_name(int format, int64_t k, int64_t m_tokens, int algo);
+
+/* The same for qmv_run_t_ex. */
+const char *qmv_t_kernel_name(int format, int64_t k, int algo);
 
 #ifdef __cplusplus
 }

@@ -29,7 +29,7 @@ def declared_functions():
 def test_header_declares_the_boundary():
     names = declared_functions()
     for need in ("qmv_create", "qmv_run", "qmv_destroy", "qmv_run_ex", "qmv_weight_bytes",
-                 "qmv_last_error"):
+                 "qmv_last_error", "qmv_run_t", "qmv_run_t_ex", "qmv_t_kernel_name"):
         assert need in names
 
 
@@ -79,6 +79,42 @@ def test_kernel_names(lib):
     assert qb.qmv_kernel_name(qb.QMV_FMT_Q5_0, 2560, 1) == "qmv_gemv_staged<q5_0>"
     assert qb.qmv_kernel_name(qb.QMV_FMT_Q5_0, 2560, 64) == "qmv_gemv_staged<q5_0>"
     assert qb.qmv_kernel_name(qb.QMV_FMT_Q8_0, 32, 1) == "qmv_simple"
+
+
+def test_transposed_kernel_names(lib):
+    assert qb.qmv_t_kernel_name(qb.QMV_FMT_Q6_K, 2560) == "qmv_gemv_t_staged<q6_k>"
+    assert qb.qmv_t_kernel_name(qb.QMV_FMT_BF16, 2560) == "qmv_gemv_t_staged<bf16>"
+    assert qb.qmv_t_kernel_name(qb.QMV_FMT_Q5_0, 4096) == "qmv_gemv_t_staged<q5_0>"
+    assert qb.qmv_t_kernel_name(qb.QMV_FMT_Q4_0, 96) == "qmv_simple_t"
+    assert qb.qmv_t_kernel_name(qb.QMV_FMT_Q4_0, 96, qb.QMV_ALGO_GEMV) == ""
+    assert qb.qmv_t_kernel_name(qb.QMV_FMT_Q4_K, 4096, qb.QMV_ALGO_MFMA) == ""
+    assert qb.qmv_t_kernel_name(qb.QMV_FMT_Q4_K, 300) == ""
+
+
+def _run_t(**kw):
+    a = dict(format=qb.QMV_FMT_Q6_K, W=0x1000, dy=0x2000, dx=0x3000, k=256, n=8, m_tokens=1,
+             j_start=0, j_end=8, accumulate=0, stream=None, algo=0)
+    a.update(kw)
+    return qb.qmv_run_t_ex(a["format"], a["W"], a["dy"], a["dx"], a["k"], a["n"],
+                           a["m_tokens"], a["j_start"], a["j_end"], a["accumulate"],
+                           a["stream"], a["algo"])
+
+
+def test_transposed_argument_errors_are_host_side(lib):
+    E = qb.QMV_ERR_INVALID_ARGUMENT
+    assert _run_t(format=0) == E
+    assert _run_t(k=300) == E
+    assert _run_t(j_start=5, j_end=4) == E
+    assert _run_t(j_end=9) == E
+    assert _run_t(accumulate=2) == E
+    assert _run_t(algo=qb.QMV_ALGO_MFMA) == E
+    assert _run_t(dx=0) == E
+    assert _run_t(dy=0) == E
+    assert _run_t(W=0x1001) == qb.QMV_ERR_MISALIGNED
+    assert _run_t(dx=0x3002) == qb.QMV_ERR_MISALIGNED
+    # an empty sum still writes dx (zeros) unless accumulating
+    assert _run_t(j_start=3, j_end=3, W=0, dy=0) == qb.QMV_ERR_NOT_INITIALIZED
+    assert _run_t(j_start=3, j_end=3, accumulate=1, dx=0) == qb.QMV_ERR_NOT_INITIALIZED
 
 
 def _run(**kw):
