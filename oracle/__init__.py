@@ -256,6 +256,40 @@ def gemv_t(fmt: int, W: np.ndarray, dy: np.ndarray, k: int, n: int, j_start: int
                        threads=threads)
 
 
+def moe(fmt: int, W: np.ndarray, ids, x: np.ndarray, k: int, n: int, n_experts: int,
+        top_k: int, threads: int | None = None):
+    """y, s of the expert-indexed product, each (n_pos * top_k, n) f64.
+
+    W stacks n_experts weight matrices of n rows ([E][n][row bytes]); ids holds
+    n_pos * top_k expert numbers; x is (n_pos, k). Output row p*top_k + slot is
+    x[p] @ W_e with e = ids[p*top_k + slot] (rullama 0.5.0,
+    src/backend/dispatch/mod.rs, the batched expert-matmul test: each
+    (position, slot) applies its own expert to x[pos]). An expert number
+    outside [0, n_experts) gives a row of NaN.
+    """
+    rb = row_bytes(fmt, k)
+    W = np.ascontiguousarray(W, dtype=np.uint8).reshape(-1)
+    ids = np.asarray(ids, dtype=np.int64).reshape(-1)
+    x2 = np.ascontiguousarray(x, dtype=np.float32)
+    x2 = x2.reshape(1, -1) if x2.ndim == 1 else x2
+    if rb < 0 or W.size < rb * n * n_experts:
+        raise ValueError("bad format/k or short W")
+    if ids.size != x2.shape[0] * top_k:
+        raise ValueError("ids must hold n_pos * top_k entries")
+    slab = rb * n
+    y = np.empty((ids.size, n), dtype=np.float64)
+    s = np.empty((ids.size, n), dtype=np.float64)
+    for r, e in enumerate(ids):
+        if e < 0 or e >= n_experts:
+            y[r] = np.nan
+            s[r] = np.nan
+            continue
+        yr, sr = gemv(fmt, W[e * slab:(e + 1) * slab], x2[r // top_k], k, n, threads=threads)
+        y[r] = yr[0]
+        s[r] = sr[0]
+    return y, s
+
+
 def cosine(a: np.ndarray, b: np.ndarray) -> float:
     """Cosine similarity accumulated in f64; a zero norm gives 0 (a failure
     against any positive floor), as in the moeflux graph_diff_oracle tests."""

@@ -589,4 +589,42 @@ def pin_t_dense_route_and_ranges():
         assert np.array_equal(c, dx[:, cols]) and np.array_equal(cs, s[:, cols])
 
 
+# ------------------------------------------------ expert-indexed pins
+
+def pin_moe_dense_route():
+    """Each output row is x[pos] times the decoded matrix of the expert its
+    (position, slot) names: a library f64 product of the decoded slices."""
+    rng = np.random.default_rng(26)
+    for fmt, k, n, E in ((Q5_0, 64, 4, 5), (Q8_0, 64, 5, 6), (Q4_K, 256, 7, 3)):
+        W = _random_matrix(fmt, n * E, k, 1100 + fmt)
+        n_pos, top_k = 3, 2
+        ids = rng.permutation(E)[:top_k].tolist() + rng.permutation(E)[:top_k].tolist() + \
+            rng.permutation(E)[:top_k].tolist()
+        x = rng.uniform(-1, 1, size=(n_pos, k)).astype(np.float32)
+        y, s = oracle.moe(fmt, W, ids, x, k, n, E, top_k)
+        dense = oracle.dequant(fmt, W, k, n * E).astype(np.float64).reshape(E, n, k)
+        for r, e in enumerate(ids):
+            want = dense[e] @ x[r // top_k].astype(np.float64)
+            assert np.all(np.abs(y[r] - want) <= 1e-12 * s[r] + 1e-300), (fmt, r)
+
+
+def pin_moe_expert_relabeling():
+    """Permuting the stacked experts and renumbering ids to match leaves every
+    output bit unchanged; an out-of-range id gives a NaN row."""
+    rng = np.random.default_rng(27)
+    fmt, k, n, E, top_k = Q4_0, 96, 6, 4, 2
+    W = _random_matrix(fmt, n * E, k, 1200)
+    x = rng.uniform(-1, 1, size=(2, k)).astype(np.float32)
+    ids = [3, 1, 0, 3]
+    y, _ = oracle.moe(fmt, W, ids, x, k, n, E, top_k)
+    perm = [2, 0, 3, 1]                  # new slab i holds old expert perm[i]
+    slab = oracle.row_bytes(fmt, k) * n
+    W2 = np.concatenate([W[p * slab:(p + 1) * slab] for p in perm])
+    ids2 = [perm.index(e) for e in ids]
+    y2, _ = oracle.moe(fmt, W2, ids2, x, k, n, E, top_k)
+    assert np.array_equal(y, y2)
+    y3, _ = oracle.moe(fmt, W, [3, 7, 0, 1], x, k, n, E, top_k)
+    assert np.all(np.isnan(y3[1])) and np.array_equal(y3[0], y[0])
+
+
 ALL_PINS = [v for name, v in sorted(globals().items()) if name.startswith("pin_")]
