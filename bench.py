@@ -8,6 +8,9 @@ all rows. W is rotated over enough copies that HBM, not the 256 MB
 last-level cache, serves it. The same rows as 8 row-range tiles accumulating
 into y are timed as well and reported under "tiled".
 
+--op t times the transposed (backward-input) product dx = dy @ W over the
+same weights instead (dy of length n in, dx of length k out).
+
 Prints ONE JSON line. Extra modes:
   --summarize-pmc CSV...   turn rocprofv3 counter CSVs of this script into
                            the traffic summary under profiles/
@@ -27,20 +30,34 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
-MFMA_BF16_PEAK_TFS = 2500.0   # dense bf16 matrix-core peak of MI355X
+MFMA_F16_PEAK_TFS = 2500.0    # dense f16/bf16 matrix-core peak of MI355X
 # Sources of each kernel family (the traffic summary of a workload is valid
 # only for the sources it was measured on).
 COMMON_SOURCES = ["block_quantized_matvec_gguf_amd/csrc/qmv_api.cpp",
                   "block_quantized_matvec_gguf_amd/csrc/qmv_internal.h"]
-FAMILY_SOURCES = {"gemv": ["block_quantized_matvec_gguf_amd/csrc/qmv_gemv.hip"],
+FAMILY_SOURCES = {"gemv": ["block_quantized_matvec_gguf_amd/csrc/qmv_gemv.hip",
+                           "block_quantized_matvec_gguf_amd/csrc/qmv_units.h"],
+                  "gemv_t": ["block_quantized_matvec_gguf_amd/csrc/qmv_gemv_t.hip",
+                             "block_quantized_matvec_gguf_amd/csrc/qmv_units.h"],
                   "mfma": ["block_quantized_matvec_gguf_amd/csrc/qmv_mfma.hip"],
                   "simple": ["block_quantized_matvec_gguf_amd/csrc/qmv_simple.hip"]}
+# the dispatches whose counters and durations are the family's (not x staging
+# or the partial-sum reduction)
+MAIN_KERNEL = {"gemv": "qmv_gemv", "gemv_t": "qmv_gemv_t_staged", "mfma": "qmv_mfma_q4_k",
+               "simple": "qmv_simple"}
 METRIC = "effective weight-read GB/s and % of MI355X HBM peak for quantized GEMV"
 
 
 def kernel_family(kernel_name: str) -> str:
     return ("mfma" if kernel_name.startswith("qmv_mfma") else
-            "simple" if kernel_name.startswith("qmv_simple") else "gemv")
+            "simple" if kernel_name.startswith("qmv_simple") else
+            "gemv_t" if kernel_name.startswith("qmv_gemv_t") else "gemv")
+
+
+def kernel_name_of(qb, fmt: int, k: int, m: int, algo: int, op: str) -> str:
+    if op == "t":
+        return qb.qmv_t_kernel_name(fmt, k, algo)
+    return qb.qmv_kernel_name(fmt, k, m, algo)
 
 
 def kernel_source_hash(family: str) -> str:
@@ -51,14 +68,15 @@ def kernel_source_hash(family: str) -> str:
     return h.hexdigest()
 
 
-def traffic_path(workload: str) -> str:
-    return os.path.join(ROOT, "profiles", "traffic_%s.json" % workload)
+def traffic_path(workload: str, op: str = "fwd") -> str:
+    return os.path.join(ROOT, "profiles", "traffic_%s%s.json" % (workload,
+                                                                "_t" if op == "t" else ""))
 
 
-def load_traffic(workload: str, family: str):
+def load_traffic(workload: str, family: str, op: str = "fwd"):
     """HBM bytes per launch from committed counter runs, or None when absent
     or taken on a different kernel source."""
-    p = traffic_path(workload)
+    p = traffic_path(workload, op)
     if not os.path.exists(p):
         return None
     with open(p) as f:
@@ -76,10 +94,9 @@ def summarize_pmc(args):
     from block_quantized_matvec_gguf_amd import binding as qb
     from block_quantized_matvec_gguf_amd import synth
     spec = synth.WORKLOADS[args.workload]
-    family = kernel_family(qb.qmv_kernel_name(synth.fmt_id(spec["fmt"]), spec["k"], spec["m"],
-                                              qb.ALGOS[args.algo]))
-    # the dispatches counted: the main kernel of the family (not x staging)
-    main_kernel = {"gemv": "qmv_gemv", "mfma": "qmv_mfma_q4_k", "simple": "qmv_simple"}[family]
+    family = kernel_family(kernel_name_of(qb, synth.fmt_id(spec["fmt"]), spec["k"], spec["m"],
+                                          qb.ALGOS[args.algo], args.op))
+    main_kernel = MAIN_KERNEL[family]
     per = {}
     for path in args.summarize_pmc:
         for r in csv.DictReader(open(path)):
@@ -98,7 +115,7 @@ def summarize_pmc(args):
     copy_bytes = args.calib_bytes
     cf, cw = avg("copy", "FETCH_SIZE"), avg("copy", "WRITE_SIZE")
     gf, gw = avg("gemv", "FETCH_SIZE"), avg("gemv", "WRITE_SIZE")
-    out = {"workload": args.workload, "kernel_family": family,
+    out = {"workload": args.workload, "op": args.op, "kernel_family": family,
            "kernel_source_sha256": kernel_source_hash(family),
            "gemv_fetch_kib_per_dispatch": gf, "gemv_write_kib_per_dispatch": gw,
            "copy_bytes": copy_bytes, "copy_fetch_kib": cf, "copy_write_kib": cw}
@@ -110,8 +127,8 @@ def summarize_pmc(args):
         out["write_bytes_per_launch"] = gw * 1024.0 * out["write_factor"]
     if "fetch_bytes_per_launch" in out and "write_bytes_per_launch" in out:
         out["bytes_per_launch"] = out["fetch_bytes_per_launch"] + out["write_bytes_per_launch"]
-    os.makedirs(os.path.dirname(traffic_path(args.workload)), exist_ok=True)
-    with open(traffic_path(args.workload), "w") as f:
+    os.makedirs(os.path.dirname(traffic_path(args.workload, args.op)), exist_ok=True)
+    with open(traffic_path(args.workload, args.op), "w") as f:
         json.dump(out, f, indent=1)
     print(json.dumps(out))
 
@@ -123,6 +140,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="q6_k_vocab_outproj")
     ap.add_argument("--algo", default="auto")
+    ap.add_argument("--op", choices=["fwd", "t"], default="fwd",
+                    help="fwd: y = x @ W; t: the transposed product dx = dy @ W")
     ap.add_argument("--tiles", type=int, default=None, help="tiles of the auxiliary run")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-tiled", action="store_true",
@@ -149,6 +168,9 @@ def main():
 
     fmt, W, x, spec = synth.workload(args.workload)
     k, n, m = spec["k"], spec["n"], spec["m"]
+    op_t = args.op == "t"
+    if op_t:  # the transposed product reads dy (m x n) and writes dx (m x k)
+        x = synth.gen_x(np.random.default_rng(0x51A72000 + spec["id"]), m, n)
     tiles = args.tiles if args.tiles is not None else spec.get("tiles", 8)
     algo = qb.ALGOS[args.algo]
     wbytes = W.nbytes
@@ -158,7 +180,7 @@ def main():
     for _ in range(copies - 1):
         Wd.append(Wd[0].clone())
     xd = torch.from_numpy(x).to(dev)
-    yd = torch.zeros((m, n), dtype=torch.float32, device=dev)
+    yd = torch.zeros((m, k if op_t else n), dtype=torch.float32, device=dev)
     qb.ensure_context()
     lib = qb.load()
     stream = torch.cuda.current_stream(dev)
@@ -166,11 +188,12 @@ def main():
     wp = [w.data_ptr() for w in Wd]
     xp, yp = xd.data_ptr(), yd.data_ptr()
 
+    entry = lib.qmv_run_t_ex if op_t else lib.qmv_run_ex
+
     def run(i, j0=0, j1=n, acc=0):
-        rc = lib.qmv_run_ex(fmt, wp[i % copies], xp, yp, k, n, m, j0, j1, acc, sp, algo)
+        rc = entry(fmt, wp[i % copies], xp, yp, k, n, m, j0, j1, acc, sp, algo)
         if rc != 0:
-            raise RuntimeError("qmv_run_ex: %s %s" % (qb.qmv_status_string(rc),
-                                                      qb.qmv_last_error()))
+            raise RuntimeError("qmv run: %s %s" % (qb.qmv_status_string(rc), qb.qmv_last_error()))
 
     # ---- main timed region: one launch over all rows per step
     for i in range(args.warmup):
@@ -195,9 +218,14 @@ def main():
     tstep = None
     if not args.no_tiled:
         yd.zero_()
+        # forward: every tile adds into y; transposed: tile 0 writes dx and
+        # tiles 1.. add (the partial-sum convention of the backward pass)
+        def tacc(t):
+            return (1 if t > 0 else 0) if op_t else 1
+
         for i in range(max(1, args.warmup // 4)):
             for t in range(tiles):
-                run(i, edges[t], edges[t + 1], 1)
+                run(i, edges[t], edges[t + 1], tacc(t))
         torch.cuda.synchronize()
         tsteps = max(1, args.steps // 2)
         e2, e3 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -205,7 +233,7 @@ def main():
         e2.record(stream)
         for i in range(tsteps):
             for t in range(tiles):
-                run(i, edges[t], edges[t + 1], 1)
+                run(i, edges[t], edges[t + 1], tacc(t))
         e3.record(stream)
         torch.cuda.synchronize()
         twall = time.perf_counter() - t0
@@ -220,23 +248,23 @@ def main():
         torch.cuda.synchronize()
         del a, b
 
-    alg_bytes = wbytes + m * k * 4 + m * n * 4       # W + x + y written once
+    alg_bytes = wbytes + m * k * 4 + m * n * 4       # W + x + y (dy + dx) once
     achieved = alg_bytes / launch_s / 1e9
     value = wbytes / step_s / 1e9
-    kname = qb.qmv_kernel_name(fmt, k, m, algo)
-    traffic = load_traffic(args.workload, kernel_family(kname))
+    kname = kernel_name_of(qb, fmt, k, m, algo, args.op)
+    traffic = load_traffic(args.workload, kernel_family(kname), args.op)
     traffic_bytes = (round(traffic["bytes_per_launch"])
                      if traffic and "bytes_per_launch" in traffic else None)
     hbm = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
            "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic_bytes,
            "algorithmic_bytes_per_launch": alg_bytes, "launch_us": round(launch_s * 1e6, 3)}
     if kname.startswith("qmv_mfma"):
-        # matrix-core kernel: 2*m*k*n algorithmic flops against the dense bf16
-        # peak (x enters as two bf16 terms, so the units execute twice that)
+        # matrix-core kernel: 2*m*k*n algorithmic flops against the dense f16
+        # peak (x enters as two f16 terms, so the units execute twice that)
         flops = 2.0 * m * k * n
         tf = flops / launch_s / 1e12
-        roofline = {"bound": "mfma", "achieved": round(tf, 2), "peak": MFMA_BF16_PEAK_TFS,
-                    "unit": "TFLOP/s", "frac": round(tf / MFMA_BF16_PEAK_TFS, 4),
+        roofline = {"bound": "mfma", "achieved": round(tf, 2), "peak": MFMA_F16_PEAK_TFS,
+                    "unit": "TFLOP/s", "frac": round(tf / MFMA_F16_PEAK_TFS, 4),
                     "traffic": traffic_bytes, "algorithmic_flops_per_launch": flops,
                     "executed_mfma_flops_per_launch": 2 * flops,
                     "launch_us": round(launch_s * 1e6, 3),
@@ -257,7 +285,8 @@ def main():
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic (seeded; value distributions of the measured workload)",
-        "config": {"workload": args.workload, "format": synth.FORMAT_NAMES[fmt], "k": k,
+        "config": {"workload": args.workload + ("_transposed" if op_t else ""),
+                   "format": synth.FORMAT_NAMES[fmt], "k": k,
                    "n": n, "m_tokens": m, "accumulate": 0, "weight_bytes": wbytes,
                    "weight_copies_rotated": copies,
                    "kernel": kname},
@@ -266,11 +295,29 @@ def main():
         "roofline": roofline,
     }
     if tstep is not None:
-        out["tiled"] = {"tiles": tiles, "accumulate": 1, "ms_per_step": round(tstep * 1e3, 5),
+        out["tiled"] = {"tiles": tiles, "accumulate": "tiles 1.. add" if op_t else 1,
+                        "ms_per_step": round(tstep * 1e3, 5),
                         "value": round(wbytes / tstep / 1e9, 1),
                         "pct_hbm_peak": round(100.0 * wbytes / tstep / 1e9 / HBM_PEAK_GBS, 2)}
 
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and op_t:
+        import oracle
+        threads = max(1, min(os.cpu_count() or 1, 16))
+        # a bounded sample of columns (each needs every row of the range)
+        ncols = max(1, min(k, 400_000_000 // max(1, n * m)))
+        cols = np.linspace(0, k - 1, ncols).astype(np.int64)
+        t0 = time.perf_counter()
+        dref, sref = oracle.gemv_t_cols(fmt, W, x, k, n, cols, threads=threads)
+        dt = time.perf_counter() - t0
+        out["cpu_baseline"] = {
+            "value": round(wbytes * ncols / k / dt / 1e9, 3), "unit": "GB/s",
+            "cores": threads, "kind": "oracle",
+            "sample": "%d of %d columns (evenly spaced), all %d rows, m=%d, f64 accumulation; "
+                      "%.2f s" % (ncols, k, n, m, dt)}
+        res = oracle.check_parity(y_main[:, cols], dref, sref)
+        out["parity"] = {"ok": res["ok"], "max_err_over_tol": round(res["max_ratio"], 5),
+                         "cosine": res["cosine"], "outputs": res["n"]}
+    elif not args.no_cpu_baseline:
         import oracle
         threads = max(1, min(os.cpu_count() or 1, 16))
         # the whole workload when it is small enough, else a bounded row sample

@@ -74,6 +74,13 @@ def load(path: str | None = None):
         lib.qmv_run_t_ex.restype = ci
         lib.qmv_t_kernel_name.argtypes = [ci, i64, ci]
         lib.qmv_t_kernel_name.restype = ctypes.c_char_p
+        moe_args = [ci, vp, vp, vp, vp, i64, i64, i64, i64, i64, ci, vp]
+        lib.qmv_run_moe.argtypes = moe_args
+        lib.qmv_run_moe.restype = ci
+        lib.qmv_run_moe_ex.argtypes = moe_args + [ci]
+        lib.qmv_run_moe_ex.restype = ci
+        lib.qmv_moe_kernel_name.argtypes = [ci, i64, ci]
+        lib.qmv_moe_kernel_name.restype = ctypes.c_char_p
         _lib = lib
         return lib
 
@@ -116,6 +123,24 @@ def qmv_run_t_ex(format: int, W: int, dy: int, dx: int, k: int, n: int, m_tokens
 
 def qmv_t_kernel_name(format: int, k: int, algo: int = QMV_ALGO_AUTO) -> str:
     return load().qmv_t_kernel_name(format, k, algo).decode()
+
+
+def qmv_run_moe(format: int, W: int, ids: int, x: int, y: int, k: int, n: int,
+                n_experts: int, n_pos: int, top_k: int, accumulate: int,
+                stream: int | None) -> int:
+    return int(load().qmv_run_moe(format, W, ids, x, y, k, n, n_experts, n_pos, top_k,
+                                  accumulate, stream))
+
+
+def qmv_run_moe_ex(format: int, W: int, ids: int, x: int, y: int, k: int, n: int,
+                   n_experts: int, n_pos: int, top_k: int, accumulate: int,
+                   stream: int | None, algo: int) -> int:
+    return int(load().qmv_run_moe_ex(format, W, ids, x, y, k, n, n_experts, n_pos, top_k,
+                                     accumulate, stream, algo))
+
+
+def qmv_moe_kernel_name(format: int, k: int, algo: int = QMV_ALGO_AUTO) -> str:
+    return load().qmv_moe_kernel_name(format, k, algo).decode()
 
 
 def qmv_weight_bytes(format: int, k: int, n: int) -> int:
@@ -198,6 +223,46 @@ def matvec_t(fmt, W, dy, k: int, n: int, dx=None, j_start: int = 0, j_end: int |
     if rc != QMV_OK:
         raise QmvError(rc, qmv_last_error())
     return dx
+
+
+def matvec_moe(fmt, W, ids, x, k: int, n: int, n_experts: int, top_k: int, y=None,
+               accumulate: bool = False, algo="auto", stream=None):
+    """y (=|+=) the expert-indexed product on the GPU.
+
+    W: uint8 CUDA tensor of n_experts * qmv_weight_bytes(fmt, k, n) bytes;
+    ids: int32 or uint32-valued int32 CUDA tensor of n_pos * top_k expert
+    numbers; x: float32 CUDA tensor (n_pos, k); y: float32 CUDA tensor
+    (n_pos * top_k, n) (allocated when None). Returns y.
+    """
+    import torch
+    f = _fmt(fmt)
+    a = ALGOS[algo] if isinstance(algo, str) else int(algo)
+    want = qmv_weight_bytes(f, k, n)
+    if W.dtype != torch.uint8 or not W.is_cuda or not W.is_contiguous() or want < 0 or \
+            W.numel() != want * n_experts:
+        raise ValueError("W must be a contiguous uint8 CUDA tensor of n_experts * %d bytes"
+                         % want)
+    if ids.dtype != torch.int32 or not ids.is_cuda or not ids.is_contiguous():
+        raise ValueError("ids must be a contiguous int32 CUDA tensor")
+    if x.dtype != torch.float32 or not x.is_cuda or not x.is_contiguous():
+        raise ValueError("x must be a contiguous float32 CUDA tensor")
+    x2 = x.reshape(1, -1) if x.dim() == 1 else x
+    n_pos = x2.shape[0]
+    if x2.shape[1] != k or ids.numel() != n_pos * top_k:
+        raise ValueError("x must be (n_pos, k) and ids hold n_pos * top_k entries")
+    if y is None:
+        y = torch.empty((n_pos * top_k, n), dtype=torch.float32, device=x.device)
+    if y.dtype != torch.float32 or not y.is_cuda or not y.is_contiguous() or \
+            y.numel() != n_pos * top_k * n:
+        raise ValueError("y must be a contiguous float32 CUDA tensor of n_pos*top_k*n elements")
+    ensure_context()
+    s = stream if stream is not None else torch.cuda.current_stream(x.device)
+    with torch.cuda.device(x.device):
+        rc = qmv_run_moe_ex(f, W.data_ptr(), ids.data_ptr(), x2.data_ptr(), y.data_ptr(), k, n,
+                            n_experts, n_pos, top_k, 1 if accumulate else 0, s.cuda_stream, a)
+    if rc != QMV_OK:
+        raise QmvError(rc, qmv_last_error())
+    return y
 
 
 def matvec(fmt, W, x, k: int, n: int, y=None, j_start: int = 0, j_end: int | None = None,

@@ -381,3 +381,96 @@ int qmv_run_t(int format, const void *W, const float *dy, float *dx, int64_t k, 
 }
 
 } // extern "C"
+
+extern "C" {
+
+const char *qmv_moe_kernel_name(int format, int64_t k, int algo) {
+    thread_local std::string name;
+    if (block_elems(format) <= 0 || k <= 0 || k % block_elems(format) != 0) return "";
+    qmv::GemvPlan p;
+    const bool stream_ok = qmv::plan_gemv(format, k, 1, 1, 256, &p);
+    const int a = algo == QMV_ALGO_AUTO ? (stream_ok ? QMV_ALGO_GEMV : QMV_ALGO_SIMPLE) : algo;
+    if (a == QMV_ALGO_GEMV && stream_ok)
+        name = qmv::gemv_moe_kernel_name(p);
+    else if (a == QMV_ALGO_SIMPLE)
+        name = "qmv_simple_moe";
+    else
+        name = "";
+    return name.c_str();
+}
+
+int qmv_run_moe_ex(int format, const void *W, const uint32_t *ids, const float *x, float *y,
+                   int64_t k, int64_t n, int64_t n_experts, int64_t n_pos, int64_t top_k,
+                   int accumulate, void *stream, int algo) {
+    t_err.clear();
+    const int64_t qk = block_elems(format);
+    if (qk <= 0) return fail(QMV_ERR_INVALID_ARGUMENT, "unknown format %d", format);
+    if (k < 0 || n < 0 || n_experts < 0 || n_pos < 0 || top_k < 0)
+        return fail(QMV_ERR_INVALID_ARGUMENT,
+                    "negative shape k=%lld n=%lld experts=%lld positions=%lld top_k=%lld",
+                    (long long)k, (long long)n, (long long)n_experts, (long long)n_pos,
+                    (long long)top_k);
+    if (k % qk != 0)
+        return fail(QMV_ERR_INVALID_ARGUMENT, "k %lld must be a multiple of %lld for %s",
+                    (long long)k, (long long)qk, fmt_name(format));
+    if (accumulate != 0 && accumulate != 1)
+        return fail(QMV_ERR_INVALID_ARGUMENT, "accumulate must be 0 or 1, got %d", accumulate);
+    if (algo != QMV_ALGO_AUTO && algo != QMV_ALGO_GEMV && algo != QMV_ALGO_SIMPLE)
+        return fail(QMV_ERR_INVALID_ARGUMENT, "algo %d has no expert-indexed form", algo);
+    const int64_t pairs = n_pos * top_k;
+    const bool work = pairs > 0 && n > 0;
+    if (work) {
+        if (pairs > 65535)
+            return fail(QMV_ERR_UNSUPPORTED, "n_pos * top_k = %lld exceeds 65535",
+                        (long long)pairs);
+        if (!y || !ids) return fail(QMV_ERR_INVALID_ARGUMENT, "y or ids is NULL");
+        if (k > 0 && (!x || (n_experts > 0 && !W)))
+            return fail(QMV_ERR_INVALID_ARGUMENT, "W or x is NULL");
+        if (((uintptr_t)W & 15) != 0)
+            return fail(QMV_ERR_MISALIGNED, "W must be 16-byte aligned");
+        if (((uintptr_t)x & 3) != 0 || ((uintptr_t)y & 3) != 0 || ((uintptr_t)ids & 3) != 0)
+            return fail(QMV_ERR_MISALIGNED, "x, y and ids must be 4-byte aligned");
+    }
+    if (g_refs.load() <= 0)
+        return fail(QMV_ERR_NOT_INITIALIZED, "qmv_run_moe before qmv_create");
+    if (!work) return QMV_OK;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(QMV_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+    if (dev < 0 || (size_t)dev >= g_dev.size() || !g_dev[(size_t)dev].gfx950)
+        return fail(QMV_ERR_UNSUPPORTED_ARCH, "device %d is not gfx950", dev);
+    const int num_cu = g_dev[(size_t)dev].num_cu;
+    hipStream_t s = (hipStream_t)stream;
+    if (k == 0) {
+        if (accumulate) return QMV_OK;
+        e = qmv::launch_fill_zero_all(y, pairs * n, s);
+        if (e != hipSuccess) return fail(QMV_ERR_HIP, "fill launch: %s", hipGetErrorString(e));
+        return QMV_OK;
+    }
+    const uint8_t *Wb = (const uint8_t *)W;
+    const int64_t rb = row_bytes_of(format, k);
+    qmv::GemvPlan p;
+    const bool stream_ok = qmv::plan_gemv(format, k, n, 1, num_cu, &p);
+    if (algo == QMV_ALGO_GEMV && !stream_ok)
+        return fail(QMV_ERR_UNSUPPORTED, "algo %d cannot serve %s with k=%lld", algo,
+                    fmt_name(format), (long long)k);
+    if (algo == QMV_ALGO_SIMPLE || !stream_ok) {
+        e = qmv::launch_simple_moe(format, Wb, ids, x, y, k, n, rb, n_experts, n_pos,
+                                   (int)top_k, accumulate, s);
+        if (e != hipSuccess) return fail(QMV_ERR_HIP, "simple launch: %s", hipGetErrorString(e));
+        return QMV_OK;
+    }
+    e = qmv::launch_gemv_moe(p, Wb, ids, x, y, k, n, rb, n_experts, n_pos, (int)top_k,
+                             accumulate, s);
+    if (e != hipSuccess) return fail(QMV_ERR_HIP, "expert launch: %s", hipGetErrorString(e));
+    return QMV_OK;
+}
+
+int qmv_run_moe(int format, const void *W, const uint32_t *ids, const float *x, float *y,
+                int64_t k, int64_t n, int64_t n_experts, int64_t n_pos, int64_t top_k,
+                int accumulate, void *stream) {
+    return qmv_run_moe_ex(format, W, ids, x, y, k, n, n_experts, n_pos, top_k, accumulate,
+                          stream, QMV_ALGO_AUTO);
+}
+
+} // extern "C"

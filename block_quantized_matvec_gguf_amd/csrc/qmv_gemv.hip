@@ -214,13 +214,11 @@ __device__ __forceinline__ void reduce_batch(float (&part)[RB][MT], const Lanes<
 // batch's loads are issued before the current batch is reduced. XL: x goes
 // through LDS (else each lane reads its x units from global memory).
 template <class F, int MT, int UPL, int RB, bool XL>
-__global__ __launch_bounds__(512) void qmv_gemv_direct(const uint8_t *__restrict__ W,
-                                                        const float *__restrict__ x,
-                                                        float *__restrict__ y, int64_t k,
-                                                        int64_t n, int64_t row_bytes,
-                                                        int64_t j_start, int64_t j_end,
-                                                        int accumulate, int U, int L, int P,
-                                                        int G, int) {
+__device__ __forceinline__ void direct_body(const uint8_t *__restrict__ W,
+                                            const float *__restrict__ x, float *__restrict__ y,
+                                            int64_t k, int64_t n, int64_t row_bytes,
+                                            int64_t j_start, int64_t j_end, int accumulate,
+                                            int U, int L, int P, int G) {
     extern __shared__ float smem[];
     const Lanes<UPL> ln(U, L, G);
     const int64_t rows_per_batch = (int64_t)P * RB;
@@ -319,15 +317,11 @@ struct StagedOccupancy {
 };
 
 template <class F, int MT, int UPL, int RB, int NPT, bool XL>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(
-    StagedOccupancy<MT, UPL, RB, NPT>::waves))) void qmv_gemv_staged(const uint8_t *__restrict__ W,
-                                                                  const float *__restrict__ x,
-                                                                  float *__restrict__ y,
-                                                                  int64_t k, int64_t n,
-                                                                  int64_t row_bytes,
-                                                                  int64_t j_start, int64_t j_end,
-                                                                  int accumulate, int U, int L,
-                                                                  int P, int G, int buf_bytes) {
+__device__ __forceinline__ void staged_body(const uint8_t *__restrict__ W,
+                                            const float *__restrict__ x, float *__restrict__ y,
+                                            int64_t k, int64_t n, int64_t row_bytes,
+                                            int64_t j_start, int64_t j_end, int accumulate,
+                                            int U, int L, int P, int G, int buf_bytes) {
     extern __shared__ float smem[];
     const Lanes<UPL> ln(U, L, G);
     const int64_t rows_per_batch = (int64_t)P * RB;
@@ -413,6 +407,80 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(
     if (ln.NG > 1 && prev >= 0)
         finish_batch<MT, RB>(red + (cur ^ 1) * nq * ln.NG, ybuf + (cur ^ 1) * nq, ln.NG, P,
                              ln.tid, ln.T, prev, j_end, y, n, accumulate);
+}
+
+// --------------------------------------------------------------- kernels
+template <class F, int MT, int UPL, int RB, bool XL>
+__global__ __launch_bounds__(512) void qmv_gemv_direct(const uint8_t *__restrict__ W,
+                                                        const float *__restrict__ x,
+                                                        float *__restrict__ y, int64_t k,
+                                                        int64_t n, int64_t row_bytes,
+                                                        int64_t j_start, int64_t j_end,
+                                                        int accumulate, int U, int L, int P,
+                                                        int G, int) {
+    direct_body<F, MT, UPL, RB, XL>(W, x, y, k, n, row_bytes, j_start, j_end, accumulate, U, L,
+                                    P, G);
+}
+
+template <class F, int MT, int UPL, int RB, int NPT, bool XL>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(
+    StagedOccupancy<MT, UPL, RB, NPT>::waves))) void qmv_gemv_staged(const uint8_t *__restrict__ W,
+                                                                  const float *__restrict__ x,
+                                                                  float *__restrict__ y,
+                                                                  int64_t k, int64_t n,
+                                                                  int64_t row_bytes,
+                                                                  int64_t j_start, int64_t j_end,
+                                                                  int accumulate, int U, int L,
+                                                                  int P, int G, int buf_bytes) {
+    staged_body<F, MT, UPL, RB, NPT, XL>(W, x, y, k, n, row_bytes, j_start, j_end, accumulate,
+                                         U, L, P, G, buf_bytes);
+}
+
+// Expert-indexed product (rullama 0.5.0, src/backend/dispatch/mod.rs, the
+// batched expert-matmul test): output row `pair` = blockIdx.y is
+// x[pair / top_k] @ W_e over all n rows of expert e = ids[pair], where W
+// stacks the experts' matrices ([E][n][row bytes]). The blockIdx.x workgroups
+// of a pair stream its expert's rows exactly as the plain kernels do. An
+// expert number outside [0, n_experts) turns the pair's outputs into NaN.
+__device__ __forceinline__ bool moe_pair(const uint32_t *ids, int64_t n_experts, int64_t n,
+                                         float *y, uint32_t &e) {
+    e = __builtin_amdgcn_readfirstlane(ids[blockIdx.y]);
+    if ((int64_t)e < n_experts) return true;
+    if (blockIdx.x == 0)
+        for (int64_t j = threadIdx.x; j < n; j += blockDim.x)
+            y[(int64_t)blockIdx.y * n + j] = __builtin_nanf("");
+    return false;
+}
+
+template <class F, int UPL, int RB, bool XL>
+__global__ __launch_bounds__(512) void qmv_gemv_moe_direct(const uint8_t *__restrict__ W,
+                                                            const uint32_t *__restrict__ ids,
+                                                            const float *__restrict__ x,
+                                                            float *__restrict__ y, int64_t k,
+                                                            int64_t n, int64_t row_bytes,
+                                                            int64_t n_experts, int top_k,
+                                                            int accumulate, int U, int L, int P,
+                                                            int G, int) {
+    uint32_t e;
+    if (!moe_pair(ids, n_experts, n, y, e)) return;
+    direct_body<F, 1, UPL, RB, XL>(W + (int64_t)e * n * row_bytes,
+                                   x + (int64_t)(blockIdx.y / top_k) * k,
+                                   y + (int64_t)blockIdx.y * n, k, n, row_bytes, 0, n,
+                                   accumulate, U, L, P, G);
+}
+
+template <class F, int UPL, int RB, int NPT, bool XL>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(
+    StagedOccupancy<1, UPL, RB, NPT>::waves))) void qmv_gemv_moe_staged(
+    const uint8_t *__restrict__ W, const uint32_t *__restrict__ ids, const float *__restrict__ x,
+    float *__restrict__ y, int64_t k, int64_t n, int64_t row_bytes, int64_t n_experts, int top_k,
+    int accumulate, int U, int L, int P, int G, int buf_bytes) {
+    uint32_t e;
+    if (!moe_pair(ids, n_experts, n, y, e)) return;
+    staged_body<F, 1, UPL, RB, NPT, XL>(W + (int64_t)e * n * row_bytes,
+                                        x + (int64_t)(blockIdx.y / top_k) * k,
+                                        y + (int64_t)blockIdx.y * n, k, n, row_bytes, 0, n,
+                                        accumulate, U, L, P, G, buf_bytes);
 }
 
 // -------------------------------------------------------------- planning
@@ -608,6 +676,108 @@ static hipError_t launch_direct(const GemvPlan &p0, const uint8_t *W, const floa
     if (p.UPL == 2) return launch_direct_rb<F, 1, 2, false>(p, W, x, y, k, n, rb, j0, j1, acc, s);
     if (p.MT == 2) return launch_direct_rb<F, 2, 1, false>(p, W, x, y, k, n, rb, j0, j1, acc, s);
     return launch_direct_rb<F, 1, 1, false>(p, W, x, y, k, n, rb, j0, j1, acc, s);
+}
+
+// ------------------------------------------------ expert-indexed launches
+struct MoeArgs {
+    const uint32_t *ids;
+    int64_t n_experts;
+    int top_k, pairs;
+};
+
+// blockIdx.y = pair; the residency cap is shared by the pairs
+template <typename K>
+static hipError_t launch_moe_k(K kernel, const GemvPlan &p, const uint8_t *W, const MoeArgs &a,
+                               const float *x, float *y, int64_t k, int64_t n, int64_t rb,
+                               int acc, hipStream_t s) {
+    if (p.lds_bytes > 64 * 1024 &&
+        hipFuncSetAttribute((const void *)kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)p.lds_bytes) != hipSuccess)
+        return hipGetLastError();
+    const int64_t cap = (int64_t)p.num_cu * resident_per_cu(kernel, p.T, p.lds_bytes);
+    int64_t per = cap / a.pairs;
+    if (per > p.grid) per = p.grid;
+    if (per < 1) per = 1;
+    hipLaunchKernelGGL(kernel, dim3((unsigned)per, (unsigned)a.pairs), dim3(p.T), p.lds_bytes, s,
+                       W, a.ids, x, y, k, n, rb, a.n_experts, a.top_k, acc, p.U, p.L, p.P, p.G,
+                       p.buf_bytes);
+    return hipGetLastError();
+}
+
+template <class F, int UPL, bool XL>
+static hipError_t launch_moe_staged_x(const GemvPlan &p, const uint8_t *W, const MoeArgs &a,
+                                      const float *x, float *y, int64_t k, int64_t n, int64_t rb,
+                                      int acc, hipStream_t s) {
+    switch (p.npt) { // the staged plan always has one row per slot per batch
+    case 2:
+        return launch_moe_k(qmv_gemv_moe_staged<F, UPL, 1, 2, XL>, p, W, a, x, y, k, n, rb, acc, s);
+    case 4:
+        return launch_moe_k(qmv_gemv_moe_staged<F, UPL, 1, 4, XL>, p, W, a, x, y, k, n, rb, acc, s);
+    default:
+        return launch_moe_k(qmv_gemv_moe_staged<F, UPL, 1, 8, XL>, p, W, a, x, y, k, n, rb, acc, s);
+    }
+}
+
+template <class F, int UPL, bool XL>
+static hipError_t launch_moe_direct_x(const GemvPlan &p, const uint8_t *W, const MoeArgs &a,
+                                      const float *x, float *y, int64_t k, int64_t n, int64_t rb,
+                                      int acc, hipStream_t s) {
+    if (p.RB == 2)
+        return launch_moe_k(qmv_gemv_moe_direct<F, UPL, 2, XL>, p, W, a, x, y, k, n, rb, acc, s);
+    return launch_moe_k(qmv_gemv_moe_direct<F, UPL, 1, XL>, p, W, a, x, y, k, n, rb, acc, s);
+}
+
+template <class F, bool STAGED>
+static hipError_t launch_moe_f(const GemvPlan &p0, const uint8_t *W, const MoeArgs &a,
+                               const float *x, float *y, int64_t k, int64_t n, int64_t rb,
+                               int acc, hipStream_t s) {
+    GemvPlan p = p0;
+    const bool xl = use_x_lds(p, x, k);
+    if constexpr (STAGED) {
+        if (p.UPL == 2)
+            return xl ? launch_moe_staged_x<F, 2, true>(p, W, a, x, y, k, n, rb, acc, s)
+                      : launch_moe_staged_x<F, 2, false>(p, W, a, x, y, k, n, rb, acc, s);
+        return xl ? launch_moe_staged_x<F, 1, true>(p, W, a, x, y, k, n, rb, acc, s)
+                  : launch_moe_staged_x<F, 1, false>(p, W, a, x, y, k, n, rb, acc, s);
+    } else {
+        if (p.UPL == 2)
+            return xl ? launch_moe_direct_x<F, 2, true>(p, W, a, x, y, k, n, rb, acc, s)
+                      : launch_moe_direct_x<F, 2, false>(p, W, a, x, y, k, n, rb, acc, s);
+        return xl ? launch_moe_direct_x<F, 1, true>(p, W, a, x, y, k, n, rb, acc, s)
+                  : launch_moe_direct_x<F, 1, false>(p, W, a, x, y, k, n, rb, acc, s);
+    }
+}
+
+hipError_t launch_gemv_moe(const GemvPlan &p, const uint8_t *W, const uint32_t *ids,
+                           const float *x, float *y, int64_t k, int64_t n, int64_t row_bytes,
+                           int64_t n_experts, int64_t n_pos, int top_k, int accumulate,
+                           hipStream_t s) {
+    const MoeArgs a = {ids, n_experts, top_k, (int)(n_pos * top_k)};
+    const int64_t rb = row_bytes;
+    switch (p.fmt) {
+    case FMT_Q4_0: return launch_moe_f<UQ4_0, true>(p, W, a, x, y, k, n, rb, accumulate, s);
+    case FMT_Q4_K: return launch_moe_f<UQ4_K, true>(p, W, a, x, y, k, n, rb, accumulate, s);
+    case FMT_Q6_K: return launch_moe_f<UQ6_K, true>(p, W, a, x, y, k, n, rb, accumulate, s);
+    case FMT_Q8_0: return launch_moe_f<UQ8_0, true>(p, W, a, x, y, k, n, rb, accumulate, s);
+    case FMT_Q5_0: return launch_moe_f<UQ5_0, true>(p, W, a, x, y, k, n, rb, accumulate, s);
+    case FMT_BF16:
+        return launch_moe_f<UHalf<true>, false>(p, W, a, x, y, k, n, rb, accumulate, s);
+    case FMT_F16:
+        return launch_moe_f<UHalf<false>, false>(p, W, a, x, y, k, n, rb, accumulate, s);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+const char *gemv_moe_kernel_name(const GemvPlan &p) {
+    static const char *names[] = {"",
+                                  "qmv_gemv_moe_direct<f16>",
+                                  "qmv_gemv_moe_direct<bf16>",
+                                  "qmv_gemv_moe_staged<q4_0>",
+                                  "qmv_gemv_moe_staged<q4_k>",
+                                  "qmv_gemv_moe_staged<q6_k>",
+                                  "qmv_gemv_moe_staged<q8_0>",
+                                  "qmv_gemv_moe_staged<q5_0>"};
+    return (p.fmt >= 1 && p.fmt <= 7) ? names[p.fmt] : "";
 }
 
 hipError_t launch_gemv(const GemvPlan &p, const uint8_t *W, const float *x, float *y,

@@ -75,6 +75,17 @@ hipError_t launch_simple(int fmt, const uint8_t *W, const float *x, float *y, in
 hipError_t launch_fill_zero(float *y, int64_t n, int64_t m, int64_t j_start, int64_t j_end,
                             hipStream_t stream);
 
+// Expert-indexed product: pair r = p*top_k + slot of n_pos*top_k computes
+// y[r] (=|+=) x[p] @ W_{ids[r]} over all n rows of that expert.
+hipError_t launch_gemv_moe(const GemvPlan &p, const uint8_t *W, const uint32_t *ids,
+                           const float *x, float *y, int64_t k, int64_t n, int64_t row_bytes,
+                           int64_t n_experts, int64_t n_pos, int top_k, int accumulate,
+                           hipStream_t stream);
+const char *gemv_moe_kernel_name(const GemvPlan &p);
+hipError_t launch_simple_moe(int fmt, const uint8_t *W, const uint32_t *ids, const float *x,
+                             float *y, int64_t k, int64_t n, int64_t row_bytes, int64_t n_experts,
+                             int64_t n_pos, int top_k, int accumulate, hipStream_t stream);
+
 // Transposed product dx (=|+=) W^T dy over rows [j_start, j_end), per token.
 bool plan_gemv_t(int fmt, int64_t k, int64_t rows, int num_cu, GemvTPlan *p);
 hipError_t launch_gemv_t(const GemvTPlan &p, const uint8_t *W, const float *dy, float *dx,

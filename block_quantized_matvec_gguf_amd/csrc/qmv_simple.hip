@@ -109,6 +109,44 @@ hipError_t launch_simple(int fmt, const uint8_t *W, const float *x, float *y, in
     return hipGetLastError();
 }
 
+// Expert-indexed product, one wave per (row, pair): pair r applies expert
+// ids[r] to x[r / top_k]; an expert number out of range gives NaN outputs.
+__global__ __launch_bounds__(256) void qmv_simple_moe(const uint8_t *__restrict__ W,
+                                                       const uint32_t *__restrict__ ids,
+                                                       const float *__restrict__ x,
+                                                       float *__restrict__ y, int64_t k,
+                                                       int64_t n, int64_t row_bytes,
+                                                       int64_t n_experts, int top_k,
+                                                       int accumulate, int fmt) {
+    const int lane = threadIdx.x & 63;
+    const int64_t pair = blockIdx.y;
+    const int64_t j = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+    if (j >= n) return;
+    const uint32_t e = ids[pair];
+    float *dst = y + pair * n + j;
+    if ((int64_t)e >= n_experts) {
+        if (lane == 0) *dst = __builtin_nanf("");
+        return;
+    }
+    const uint8_t *row = W + ((int64_t)e * n + j) * row_bytes;
+    const float *xp = x + (pair / top_k) * k;
+    float acc = 0.f;
+    for (int64_t i = lane; i < k; i += 64) acc = fmaf(simple_weight(fmt, row, i), xp[i], acc);
+    for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
+    if (lane == 0) *dst = accumulate ? *dst + acc : acc;
+}
+
+hipError_t launch_simple_moe(int fmt, const uint8_t *W, const uint32_t *ids, const float *x,
+                             float *y, int64_t k, int64_t n, int64_t row_bytes, int64_t n_experts,
+                             int64_t n_pos, int top_k, int accumulate, hipStream_t stream) {
+    const int64_t bx = (n + 3) / 4;
+    if (bx > 0x7fffffff) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(qmv_simple_moe, dim3((unsigned)bx, (unsigned)(n_pos * top_k)), dim3(256),
+                       0, stream, W, ids, x, y, k, n, row_bytes, n_experts, top_k, accumulate,
+                       fmt);
+    return hipGetLastError();
+}
+
 // Transposed product, one thread per output (t, i): the rows of the range
 // in order, every weight decoded on its own, the sum kept in f64.
 __global__ __launch_bounds__(256) void qmv_simple_t(const uint8_t *__restrict__ W,

@@ -153,6 +153,8 @@ WORKLOADS = {
     "q5_0_ffn_up": dict(id=7, fmt="q5_0", k=2560, n=10240, m=1),
     "q6_k_vocab_outproj": dict(id=4, fmt="q6_k", k=2560, n=262144, m=1, tiles=8),
     "q4_k_prefill": dict(id=5, fmt="q4_k", k=4096, n=14336, m=64),
+    # expert-indexed decode: 64 stacked experts of n rows, 8 chosen per position
+    "q4_k_moe_decode": dict(id=8, fmt="q4_k", k=2048, n=1536, m=1, experts=64, top_k=8),
 }
 
 
@@ -166,6 +168,14 @@ def workload(name: str, n: int | None = None):
     f = fmt_id(spec["fmt"])
     rw = np.random.default_rng(0x51A70000 + spec["id"] + (0 if n is None else 7919 * n))
     rx = np.random.default_rng(0x51A71000 + spec["id"])
-    W = gen_weights(f, rw, spec["n"], spec["k"])
+    W = gen_weights(f, rw, spec["n"] * spec.get("experts", 1), spec["k"])
     x = gen_x(rx, spec["m"], spec["k"])
     return f, W, x, spec
+
+
+def moe_ids(spec) -> np.ndarray:
+    """Seeded expert numbers of an expert-indexed workload: top_k distinct
+    experts per position, int32 (n_pos * top_k,)."""
+    r = np.random.default_rng(0x51A73000 + spec["id"])
+    return np.concatenate([r.permutation(spec["experts"])[:spec["top_k"]]
+                           for _ in range(spec["m"])]).astype(np.int32)

@@ -159,6 +159,41 @@ int qmv_run_t_ex(int format, const void *W, const float *dy, float *dx, int64_t 
                  int64_t n, int64_t m_tokens, int64_t j_start, int64_t j_end,
                  int accumulate, void *stream, int algo);
 
+/* Enqueue the expert-indexed product of a mixture-of-experts layer on
+ * `stream`, kernel family chosen automatically:
+ *
+ *     y[r*n + j] (=|+=) sum_{i<k} x[p*k + i] * w_{e,j}[i],
+ *     r = p*top_k + slot,  e = ids[r],
+ *
+ * for every position p < n_pos, slot < top_k and row j < n, where W stacks
+ * n_experts weight matrices of n rows each ([E][n][row bytes], expert e at
+ * byte e * qmv_weight_bytes(format, k, n)) (rullama 0.5.0,
+ * src/backend/dispatch/mod.rs, the expert-matmul tests: stacked experts,
+ * ids[pos*top_k + slot] selecting each slot's expert, x[pos] the position's
+ * input).
+ *
+ *   ids         n_pos * top_k uint32 device values, 4-byte aligned. They are
+ *               read on the device only: a value >= n_experts is not an error
+ *               the host can see; it turns that slot's n outputs into NaN.
+ *   x           n_pos x k f32; y: (n_pos * top_k) x n f32 (4-byte aligned).
+ *   W           16-byte aligned; n_pos * top_k <= 65535.
+ *   accumulate  0: y = result; 1: y += result.
+ *
+ * Returns QMV_OK after a successful enqueue (nothing to do when n_pos, top_k
+ * or n is 0; with k == 0, y is zeroed unless accumulating and ids are not
+ * read), else the codes of qmv_run. Allocates nothing. Each output row's
+ * arithmetic matches qmv_run on the same expert's matrix. */
+int qmv_run_moe(int format, const void *W, const uint32_t *ids, const float *x, float *y,
+                int64_t k, int64_t n, int64_t n_experts, int64_t n_pos, int64_t top_k,
+                int accumulate, void *stream);
+
+/* qmv_run_moe with an explicit kernel family: QMV_ALGO_GEMV (streaming; the
+ * shapes qmv_run_ex serves with it) or QMV_ALGO_SIMPLE (one wave per output,
+ * any valid shape). QMV_ALGO_MFMA is QMV_ERR_INVALID_ARGUMENT here. */
+int qmv_run_moe_ex(int format, const void *W, const uint32_t *ids, const float *x, float *y,
+                   int64_t k, int64_t n, int64_t n_experts, int64_t n_pos, int64_t top_k,
+                   int accumulate, void *stream, int algo);
+
 /* Release one reference to the context; the last one frees it. Safe to call
  * when not initialised. Must not race with qmv_run or qmv_create. */
 void qmv_destroy(void);
@@ -182,8 +217,9 @@ const char *qmv_status_string(int status);
  * to find the launch in profiler output. */
 const char *qmv_kernel_name(int format, int64_t k, int64_t m_tokens, int algo);
 
-/* The same for qmv_run_t_ex. */
+/* The same for qmv_run_t_ex and qmv_run_moe_ex. */
 const char *qmv_t_kernel_name(int format, int64_t k, int algo);
+const char *qmv_moe_kernel_name(int format, int64_t k, int algo);
 
 #ifdef __cplusplus
 }

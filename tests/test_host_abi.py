@@ -29,7 +29,8 @@ def declared_functions():
 def test_header_declares_the_boundary():
     names = declared_functions()
     for need in ("qmv_create", "qmv_run", "qmv_destroy", "qmv_run_ex", "qmv_weight_bytes",
-                 "qmv_last_error", "qmv_run_t", "qmv_run_t_ex", "qmv_t_kernel_name"):
+                 "qmv_last_error", "qmv_run_t", "qmv_run_t_ex", "qmv_t_kernel_name",
+                 "qmv_run_moe", "qmv_run_moe_ex", "qmv_moe_kernel_name"):
         assert need in names
 
 
@@ -89,6 +90,32 @@ def test_transposed_kernel_names(lib):
     assert qb.qmv_t_kernel_name(qb.QMV_FMT_Q4_0, 96, qb.QMV_ALGO_GEMV) == ""
     assert qb.qmv_t_kernel_name(qb.QMV_FMT_Q4_K, 4096, qb.QMV_ALGO_MFMA) == ""
     assert qb.qmv_t_kernel_name(qb.QMV_FMT_Q4_K, 300) == ""
+
+
+def test_moe_kernel_names_and_errors(lib):
+    assert qb.qmv_moe_kernel_name(qb.QMV_FMT_Q4_K, 2048) == "qmv_gemv_moe_staged<q4_k>"
+    assert qb.qmv_moe_kernel_name(qb.QMV_FMT_F16, 2048) == "qmv_gemv_moe_direct<f16>"
+    assert qb.qmv_moe_kernel_name(qb.QMV_FMT_Q8_0, 32) == "qmv_simple_moe"
+    assert qb.qmv_moe_kernel_name(qb.QMV_FMT_Q8_0, 32, qb.QMV_ALGO_GEMV) == ""
+
+    def run(**kw):
+        a = dict(format=qb.QMV_FMT_Q4_K, W=0x1000, ids=0x4000, x=0x2000, y=0x3000, k=256, n=8,
+                 E=4, n_pos=2, top_k=2, accumulate=0, stream=None, algo=0)
+        a.update(kw)
+        return qb.qmv_run_moe_ex(a["format"], a["W"], a["ids"], a["x"], a["y"], a["k"], a["n"],
+                                 a["E"], a["n_pos"], a["top_k"], a["accumulate"], a["stream"],
+                                 a["algo"])
+    E = qb.QMV_ERR_INVALID_ARGUMENT
+    assert run(format=0) == E
+    assert run(k=100) == E
+    assert run(top_k=-1) == E
+    assert run(ids=0) == E
+    assert run(algo=qb.QMV_ALGO_MFMA) == E
+    assert run(ids=0x4002) == qb.QMV_ERR_MISALIGNED
+    assert run(W=0x1008) == qb.QMV_ERR_MISALIGNED
+    assert run(n_pos=70000, top_k=1) == qb.QMV_ERR_UNSUPPORTED
+    assert run() == qb.QMV_ERR_NOT_INITIALIZED
+    assert run(n_pos=0, ids=0, x=0, y=0) == qb.QMV_ERR_NOT_INITIALIZED
 
 
 def _run_t(**kw):
