@@ -9,7 +9,10 @@ last-level cache, serves it. The same rows as 8 row-range tiles accumulating
 into y are timed as well and reported under "tiled".
 
 --op t times the transposed (backward-input) product dx = dy @ W over the
-same weights instead (dy of length n in, dx of length k out).
+same weights instead (dy of length n in, dx of length k out); --op moe the
+expert-indexed product of an expert workload (top_k of the stacked experts per
+position; the expert sets rotate with the weight copies so that HBM serves
+them).
 
 Prints ONE JSON line. Extra modes:
   --summarize-pmc CSV...   turn rocprofv3 counter CSVs of this script into
@@ -57,6 +60,8 @@ def kernel_family(kernel_name: str) -> str:
 def kernel_name_of(qb, fmt: int, k: int, m: int, algo: int, op: str) -> str:
     if op == "t":
         return qb.qmv_t_kernel_name(fmt, k, algo)
+    if op == "moe":
+        return qb.qmv_moe_kernel_name(fmt, k, algo)
     return qb.qmv_kernel_name(fmt, k, m, algo)
 
 
@@ -140,8 +145,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="q6_k_vocab_outproj")
     ap.add_argument("--algo", default="auto")
-    ap.add_argument("--op", choices=["fwd", "t"], default="fwd",
-                    help="fwd: y = x @ W; t: the transposed product dx = dy @ W")
+    ap.add_argument("--op", choices=["fwd", "t", "moe"], default=None,
+                    help="fwd: y = x @ W; t: the transposed product dx = dy @ W; moe: the "
+                         "expert-indexed product (default: moe for expert workloads, else fwd)")
     ap.add_argument("--tiles", type=int, default=None, help="tiles of the auxiliary run")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-tiled", action="store_true",
@@ -152,6 +158,9 @@ def main():
     ap.add_argument("--summarize-pmc", nargs="*", default=None)
     args = ap.parse_args()
 
+    if args.op is None:
+        from block_quantized_matvec_gguf_amd import synth as _s
+        args.op = "moe" if "experts" in _s.WORKLOADS[args.workload] else "fwd"
     if args.summarize_pmc:
         summarize_pmc(args)
         return
@@ -169,18 +178,31 @@ def main():
     fmt, W, x, spec = synth.workload(args.workload)
     k, n, m = spec["k"], spec["n"], spec["m"]
     op_t = args.op == "t"
+    op_moe = args.op == "moe"
     if op_t:  # the transposed product reads dy (m x n) and writes dx (m x k)
         x = synth.gen_x(np.random.default_rng(0x51A72000 + spec["id"]), m, n)
     tiles = args.tiles if args.tiles is not None else spec.get("tiles", 8)
     algo = qb.ALGOS[args.algo]
     wbytes = W.nbytes
     copies = max(1, int(np.ceil(1.1e9 / wbytes)))
+    if op_moe:
+        E, top_k = spec["experts"], spec["top_k"]
+        slab = W.nbytes // E
+        # disjoint expert sets, one per step in turn (each set: top_k experts
+        # per position, all positions drawn from the set's experts)
+        perm = np.random.default_rng(0x51A73000 + spec["id"]).permutation(E)
+        nsets = max(1, E // (top_k * m))
+        id_sets = [perm[s_ * top_k * m:(s_ + 1) * top_k * m].astype(np.int32)
+                   for s_ in range(nsets)]
+        wbytes = len(np.unique(id_sets[0])) * slab       # weight bytes one call reads
+        copies = max(1, int(np.ceil(1.1e9 / (wbytes * nsets))))
     dev = torch.device("cuda:0")
     Wd = [torch.from_numpy(W).to(dev)]
     for _ in range(copies - 1):
         Wd.append(Wd[0].clone())
     xd = torch.from_numpy(x).to(dev)
-    yd = torch.zeros((m, k if op_t else n), dtype=torch.float32, device=dev)
+    yd = torch.zeros((m * (top_k if op_moe else 1), k if op_t else n), dtype=torch.float32,
+                     device=dev)
     qb.ensure_context()
     lib = qb.load()
     stream = torch.cuda.current_stream(dev)
@@ -189,9 +211,17 @@ def main():
     xp, yp = xd.data_ptr(), yd.data_ptr()
 
     entry = lib.qmv_run_t_ex if op_t else lib.qmv_run_ex
+    if op_moe:
+        idd = [torch.from_numpy(a).to(dev) for a in id_sets]
+        idp = [t.data_ptr() for t in idd]
 
     def run(i, j0=0, j1=n, acc=0):
-        rc = entry(fmt, wp[i % copies], xp, yp, k, n, m, j0, j1, acc, sp, algo)
+        if op_moe:
+            # step i: weight copy i % copies, expert set (i // copies) % nsets
+            rc = lib.qmv_run_moe_ex(fmt, wp[i % copies], idp[(i // copies) % nsets], xp, yp, k,
+                                    n, E, m, top_k, acc, sp, algo)
+        else:
+            rc = entry(fmt, wp[i % copies], xp, yp, k, n, m, j0, j1, acc, sp, algo)
         if rc != 0:
             raise RuntimeError("qmv run: %s %s" % (qb.qmv_status_string(rc), qb.qmv_last_error()))
 
@@ -212,11 +242,12 @@ def main():
     step_s = max(wall, gpu_s) / args.steps
     launch_s = gpu_s / args.steps
     y_main = yd.cpu().numpy()
+    last_ids = id_sets[((args.steps - 1) // copies) % nsets] if op_moe else None
 
     # ---- auxiliary: the same rows as row-range tiles accumulating into y
     edges = [t * n // tiles for t in range(tiles + 1)]
     tstep = None
-    if not args.no_tiled:
+    if not args.no_tiled and not op_moe:
         yd.zero_()
         # forward: every tile adds into y; transposed: tile 0 writes dx and
         # tiles 1.. add (the partial-sum convention of the backward pass)
@@ -248,7 +279,8 @@ def main():
         torch.cuda.synchronize()
         del a, b
 
-    alg_bytes = wbytes + m * k * 4 + m * n * 4       # W + x + y (dy + dx) once
+    # W read + x + y (dy + dx) once
+    alg_bytes = wbytes + m * k * 4 + m * (top_k if op_moe else 1) * n * 4
     achieved = alg_bytes / launch_s / 1e9
     value = wbytes / step_s / 1e9
     kname = kernel_name_of(qb, fmt, k, m, algo, args.op)
@@ -286,12 +318,14 @@ def main():
         "dtype": "f32",
         "data": "synthetic (seeded; value distributions of the measured workload)",
         "config": {"workload": args.workload + ("_transposed" if op_t else ""),
+                   **({"experts": E, "top_k": top_k, "expert_sets_rotated": nsets}
+                      if op_moe else {}),
                    "format": synth.FORMAT_NAMES[fmt], "k": k,
                    "n": n, "m_tokens": m, "accumulate": 0, "weight_bytes": wbytes,
                    "weight_copies_rotated": copies,
                    "kernel": kname},
         "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
-        "rows_per_s": round(m * n / step_s, 1),
+        "rows_per_s": round(m * (top_k if op_moe else 1) * n / step_s, 1),
         "roofline": roofline,
     }
     if tstep is not None:
@@ -300,7 +334,21 @@ def main():
                         "value": round(wbytes / tstep / 1e9, 1),
                         "pct_hbm_peak": round(100.0 * wbytes / tstep / 1e9 / HBM_PEAK_GBS, 2)}
 
-    if not args.no_cpu_baseline and op_t:
+    if not args.no_cpu_baseline and op_moe:
+        import oracle
+        threads = max(1, min(os.cpu_count() or 1, 16))
+        t0 = time.perf_counter()
+        yref, sref = oracle.moe(fmt, W, last_ids, x, k, n, E, top_k, threads=threads)
+        dt = time.perf_counter() - t0
+        out["cpu_baseline"] = {
+            "value": round(wbytes / dt / 1e9, 3), "unit": "GB/s", "cores": threads,
+            "kind": "oracle",
+            "sample": "the whole call (%d expert rows x %d), f64 accumulation; %.2f s"
+                      % (len(last_ids) * n, k, dt)}
+        res = oracle.check_parity(y_main, yref, sref)
+        out["parity"] = {"ok": res["ok"], "max_err_over_tol": round(res["max_ratio"], 5),
+                         "cosine": res["cosine"], "outputs": res["n"]}
+    elif not args.no_cpu_baseline and op_t:
         import oracle
         threads = max(1, min(os.cpu_count() or 1, 16))
         # a bounded sample of columns (each needs every row of the range)
