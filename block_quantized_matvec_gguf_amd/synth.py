@@ -21,6 +21,9 @@ Q8_0 and Q5_0 draws mirror Q4_0's, as no measured workload uses them):
   0..31).
 * F16 / BF16: weights ~ N(0, 0.02), rounded to nearest-even in the storage
   type (f64 draw -> f32 -> storage type).
+* Affine 4-bit / 8-bit group-64 rows: uniform u32 code words, bf16 scales ~
+  U[0.01, 0.06] and biases ~ U[-0.1, 0.1] per group (the spans of the pages'
+  4-bit fixture; rounded to nearest even).
 * x: f32 ~ U[-1, 1].
 
 All generators take a numpy Generator; the named workloads use fixed seeds.
@@ -135,6 +138,20 @@ def gen_q5_0(rng, n, k, d_range=(0.001, 0.02)) -> np.ndarray:
     blk[:, 0:2] = _f16_bytes(rng.uniform(d_range[0], d_range[1], size=nb))
     blk[:, 2:22] = rng.integers(0, 256, size=(nb, 20), dtype=np.uint8)
     return blk.reshape(-1)
+
+
+def gen_affine(rng, bits, n, k, scale_range=(0.01, 0.06), bias_range=(-0.1, 0.1)):
+    """Affine group-quantized rows: uniform random u32 code words (k*bits/32
+    per row), bf16 scales ~ U[0.01, 0.06] and biases ~ U[-0.1, 0.1] per group
+    of 64 (the spans of the pages' 4-bit fixture). Returns (words, scales,
+    biases) as uint32 (n, k*bits/32), uint16 (n, k/64), uint16 (n, k/64)."""
+    if bits not in (4, 8) or k % 64:
+        raise ValueError("affine rows need bits 4 or 8 and k % 64 == 0")
+    words = rng.integers(0, 2 ** 32, size=(n, k * bits // 32), dtype=np.uint64).astype(np.uint32)
+    g = k // 64
+    scales = bf16_bits(rng.uniform(scale_range[0], scale_range[1], size=(n, g)).astype(np.float32))
+    biases = bf16_bits(rng.uniform(bias_range[0], bias_range[1], size=(n, g)).astype(np.float32))
+    return words, scales, biases
 
 
 def gen_weights(fmt, rng, n, k) -> np.ndarray:

@@ -72,6 +72,12 @@ def load_library(path: str):
     lib.oracle_gemv_range.argtypes = [c_int, c_vp, c_vp, c_i64, c_i64, c_i64, c_i64, c_i64,
                                       c_vp, c_vp]
     lib.oracle_gemv_range.restype = c_int
+    if hasattr(lib, "oracle_affine_gemv_rows"):
+        lib.oracle_affine_elem.argtypes = [c_int, c_vp, c_vp, c_vp, c_i64]
+        lib.oracle_affine_elem.restype = ctypes.c_float
+        lib.oracle_affine_gemv_rows.argtypes = [c_int, c_vp, c_vp, c_vp, c_vp, c_i64, c_i64,
+                                                c_i64, c_vp, c_i64, c_vp, c_vp]
+        lib.oracle_affine_gemv_rows.restype = c_int
     if hasattr(lib, "oracle_gemv_t_cols"):
         lib.oracle_gemv_t_cols.argtypes = [c_int, c_vp, c_vp, c_i64, c_i64, c_i64, c_i64, c_i64,
                                            c_vp, c_i64, c_vp, c_vp]
@@ -287,6 +293,72 @@ def moe(fmt: int, W: np.ndarray, ids, x: np.ndarray, k: int, n: int, n_experts: 
         yr, sr = gemv(fmt, W[e * slab:(e + 1) * slab], x2[r // top_k], k, n, threads=threads)
         y[r] = yr[0]
         s[r] = sr[0]
+    return y, s
+
+
+def _affine_arrays(bits, words, scales, biases, k, n):
+    words = np.ascontiguousarray(words, dtype=np.uint32).reshape(-1)
+    scales = np.ascontiguousarray(scales, dtype=np.uint16).reshape(-1)
+    biases = np.ascontiguousarray(biases, dtype=np.uint16).reshape(-1)
+    if bits not in (4, 8) or k % 64 or words.size < n * k * bits // 32 or \
+            scales.size < n * (k // 64) or biases.size < n * (k // 64):
+        raise ValueError("bad affine shapes")
+    return words, scales, biases
+
+
+def affine_dequant(bits, words, scales, biases, k, n):
+    """Decode affine group-quantized rows to an (n, k) f32 array."""
+    lib = _load()
+    words, scales, biases = _affine_arrays(bits, words, scales, biases, k, n)
+    out = np.empty((n, k), dtype=np.float32)
+    wpr, gpr = k * bits // 32, k // 64
+    for j in range(n):
+        wj, sj, bj = words[j * wpr:], scales[j * gpr:], biases[j * gpr:]
+        for i in range(k):
+            out[j, i] = lib.oracle_affine_elem(bits, _ptr(wj), _ptr(sj), _ptr(bj), i)
+    return out
+
+
+def affine_gemv(bits, words, scales, biases, x, k, n, j_start=0, j_end=None,
+                threads: int | None = None):
+    """y, s of the forward product over affine group-quantized weights for rows
+    j_start <= j < j_end, each (m, j_end - j_start) f64."""
+    lib = _load()
+    if j_end is None:
+        j_end = n
+    words, scales, biases = _affine_arrays(bits, words, scales, biases, k, n)
+    x2 = np.ascontiguousarray(x, dtype=np.float32)
+    x2 = x2.reshape(1, -1) if x2.ndim == 1 else x2
+    m = x2.shape[0]
+    rows = np.arange(j_start, j_end, dtype=np.int64)
+    nr = rows.size
+    y = np.empty((m, nr), dtype=np.float64)
+    s = np.empty((m, nr), dtype=np.float64)
+    nt = min(_threads(threads), max(1, nr))
+    bounds = [nr * i // nt for i in range(nt + 1)]
+
+    def work(i):
+        a, b = bounds[i], bounds[i + 1]
+        if b <= a:
+            return 0
+        sub = np.ascontiguousarray(rows[a:b])
+        ys = np.empty((m, b - a), dtype=np.float64)
+        ss = np.empty((m, b - a), dtype=np.float64)
+        rc = lib.oracle_affine_gemv_rows(bits, _ptr(words), _ptr(scales), _ptr(biases),
+                                         _ptr(x2), k, n, m, _ptr(sub), b - a, _ptr(ys),
+                                         _ptr(ss))
+        if rc == 0:
+            y[:, a:b] = ys
+            s[:, a:b] = ss
+        return rc
+
+    if nt == 1:
+        rcs = [work(0)]
+    else:
+        with ThreadPoolExecutor(max_workers=nt) as ex:
+            rcs = list(ex.map(work, range(nt)))
+    if any(rc != 0 for rc in rcs):
+        raise ValueError("oracle_affine_gemv_rows failed: %r" % (rcs,))
     return y, s
 
 

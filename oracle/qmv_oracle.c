@@ -21,6 +21,11 @@
  *     dx[t][i] = sum_{j0<=j<j1} dy[t][j] * w_j[i]
  *     s[t][i]  = sum_{j0<=j<j1} |dy[t][j] * w_j[i]|
  *
+ * and the same forward product over affine group-quantized weights (moeflux,
+ * tests/graph_diff_oracle.rs: 4-bit or 8-bit codes packed in u32 words, one
+ * bf16 scale and one bf16 bias per group of 64 weights, value
+ * code * scale + bias).
+ *
  * Every weight is first decoded to an f32 value, element by element, then the
  * sum runs serially over i in f64. There is no blocking, no factoring of the
  * block scales and no reordering: the decode of element i of row j looks up
@@ -339,5 +344,65 @@ int oracle_gemv_t_cols(int fmt, const uint8_t *W, const float *dy, int64_t k, in
                 s[t * ncols + c] = mag;
         }
     }
+    return 0;
+}
+
+/* ------------------------------------------------------- affine weights */
+
+/* Weight i of one row of affine group-quantized weights (moeflux,
+ * tests/graph_diff_oracle.rs, the 4-bit embedding fixture: codes packed into
+ * u32 words, k*bits/32 words per row; bf16 scales and biases, k/64 per row).
+ * Element i is code number i mod (32/bits) of word i / (32/bits), counted
+ * from the least significant bits (the pages do not print the order inside
+ * a word; lowest first is this reading). Value code * scale + bias, with
+ * scale and bias of group i / 64: the product is exact in f32 (an 8-bit bf16
+ * significand times a code of at most 8 bits), the addition rounds once. */
+float oracle_affine_elem(int bits, const uint32_t *words, const uint16_t *scales,
+                         const uint16_t *biases, int64_t i)
+{
+    int per = 32 / bits;
+    uint32_t mask = (bits == 8) ? 0xffu : 0x0fu;
+    uint32_t w = words[i / per];
+    uint32_t q = (w >> (bits * (int)(i % per))) & mask;
+    float sc = oracle_bf16_to_f32(scales[i / 64]);
+    float bi = oracle_bf16_to_f32(biases[i / 64]);
+    return (float)q * sc + bi;
+}
+
+/* y, s of the forward product for the listed rows (as oracle_gemv_rows), W
+ * given as words [n][k*bits/32], scales and biases [n][k/64]. bits is 4 or 8
+ * and k a multiple of 64. Returns 0, -1 on bad arguments, -2 if out of
+ * memory. */
+int oracle_affine_gemv_rows(int bits, const uint32_t *words, const uint16_t *scales,
+                            const uint16_t *biases, const float *x, int64_t k, int64_t n,
+                            int64_t m, const int64_t *rows, int64_t nrows, double *y, double *s)
+{
+    if ((bits != 4 && bits != 8) || k < 0 || k % 64 != 0 || n < 0 || m < 0 || nrows < 0)
+        return -1;
+    int64_t wpr = k * bits / 32, gpr = k / 64;
+    float *w = (float *)malloc((size_t)(k > 0 ? k : 1) * sizeof(float));
+    if (!w)
+        return -2;
+    for (int64_t r = 0; r < nrows; r++) {
+        int64_t j = rows[r];
+        if (j < 0 || j >= n) {
+            free(w);
+            return -1;
+        }
+        for (int64_t i = 0; i < k; i++)
+            w[i] = oracle_affine_elem(bits, words + j * wpr, scales + j * gpr, biases + j * gpr, i);
+        for (int64_t t = 0; t < m; t++) {
+            double sum = 0.0, bound = 0.0;
+            for (int64_t e = 0; e < k; e++) {
+                double prod = (double)x[t * k + e] * (double)w[e];
+                sum += prod;
+                bound += fabs(prod);
+            }
+            y[t * nrows + r] = sum;
+            if (s)
+                s[t * nrows + r] = bound;
+        }
+    }
+    free(w);
     return 0;
 }

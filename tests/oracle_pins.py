@@ -627,4 +627,72 @@ def pin_moe_expert_relabeling():
     assert np.all(np.isnan(y3[1])) and np.array_equal(y3[0], y[0])
 
 
+# ------------------------------------------------ affine group-64 pins
+
+def pack_affine(bits, codes):
+    """codes: k ints in element order -> u32 words, least significant first."""
+    per = 32 // bits
+    words = []
+    for w in range(len(codes) // per):
+        v = 0
+        for p in range(per):
+            v |= int(codes[w * per + p]) << (bits * p)
+        words.append(v)
+    return np.array(words, dtype=np.uint32)
+
+
+def pin_affine_golden():
+    g = read_golden("affine_hand_rows.txt")
+    assert len(g["words"]) == len(g["values"]) == 3
+    for b, w, sc, bi, v in zip(g["bits"], g["words"], g["scale"], g["bias"], g["values"]):
+        words = np.array([int(t, 16) for t in w.split()], dtype=np.uint32)
+        got = oracle.affine_dequant(int(b), words, np.array([int(sc, 16)], np.uint16),
+                                    np.array([int(bi, 16)], np.uint16), 64, 1)[0]
+        want = np.array([float(t) for t in v.split()], dtype=np.float32)
+        assert np.array_equal(got, want), (b, got, want)
+    codes4 = [e % 16 if e < 32 else 15 - e % 16 for e in range(64)]
+    assert pack_affine(4, codes4).tolist() == [int(t, 16) for t in g["words"][0].split()]
+    assert pack_affine(8, [4 * e for e in range(64)]).tolist() == \
+        [int(t, 16) for t in g["words"][2].split()]
+
+
+def pin_affine_roundtrip_and_groups():
+    """Random codes, scales and biases through the packer: every element is
+    code * scale + bias of its own group; a scale of zero leaves the bias."""
+    rng = np.random.default_rng(28)
+    for bits in (4, 8):
+        k, n = 256, 3
+        codes = rng.integers(0, 2 ** bits, size=(n, k))
+        sc = synth.bf16_bits(rng.uniform(-0.1, 0.1, size=(n, k // 64)).astype(np.float32))
+        bi = synth.bf16_bits(rng.uniform(-0.5, 0.5, size=(n, k // 64)).astype(np.float32))
+        words = np.stack([pack_affine(bits, codes[j]) for j in range(n)])
+        w = oracle.affine_dequant(bits, words, sc, bi, k, n)
+        scf = (sc.astype(np.uint32) << 16).view(np.float32)
+        bif = (bi.astype(np.uint32) << 16).view(np.float32)
+        for j in range(n):
+            for i in range(k):
+                want = np.float32(codes[j, i]) * scf[j, i // 64] + bif[j, i // 64]
+                assert w[j, i] == want, (bits, j, i)
+        sc0 = sc.copy()
+        sc0[:, 1] = 0
+        w0 = oracle.affine_dequant(bits, words, sc0, bi, k, n)
+        assert np.array_equal(w0[:, 64:128], np.repeat(bif[:, 1:2], 64, axis=1))
+        assert np.array_equal(w0[:, :64], w[:, :64]) and np.array_equal(w0[:, 128:], w[:, 128:])
+
+
+def pin_affine_dense_route_and_onehot():
+    rng = np.random.default_rng(29)
+    for bits in (4, 8):
+        k, n = 192, 7
+        words, sc, bi = synth.gen_affine(rng, bits, n, k)
+        dense = oracle.affine_dequant(bits, words, sc, bi, k, n).astype(np.float64)
+        x = synth.gen_x(rng, 2, k)
+        y, s = oracle.affine_gemv(bits, words, sc, bi, x, k, n)
+        assert np.all(np.abs(y - x.astype(np.float64) @ dense.T) <= 1e-12 * s + 1e-300)
+        y1, s1 = oracle.affine_gemv(bits, words, sc, bi, np.eye(k, dtype=np.float32), k, n)
+        assert np.array_equal(y1, dense.T) and np.array_equal(s1, np.abs(dense.T))
+        yr, _ = oracle.affine_gemv(bits, words, sc, bi, x, k, n, 2, 5)
+        assert np.array_equal(yr, y[:, 2:5])
+
+
 ALL_PINS = [v for name, v in sorted(globals().items()) if name.startswith("pin_")]

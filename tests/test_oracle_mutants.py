@@ -58,6 +58,15 @@ MUTANTS = {
     "gemv_t_skips_first_row": ("for (int64_t j = j0; j < j1; j++) {\n                double p = (double)dy",
                                "for (int64_t j = j0 + 1; j < j1; j++) {\n                double p = (double)dy"),
     "gemv_t_row_as_column": ("oracle_elem(fmt, W + j * rb, i)", "oracle_elem(fmt, W + i * rb, j % k)"),
+    "affine_codes_high_first": ("uint32_t q = (w >> (bits * (int)(i % per))) & mask;",
+                                "uint32_t q = (w >> (bits * (per - 1 - (int)(i % per)))) & mask;"),
+    "affine_group_of_32": ("float sc = oracle_bf16_to_f32(scales[i / 64]);",
+                           "float sc = oracle_bf16_to_f32(scales[i / 32 % (64 / 32)]);"),
+    "affine_bias_sign": ("return (float)q * sc + bi;", "return (float)q * sc - bi;"),
+    "affine_scale_bias_swapped": ("float sc = oracle_bf16_to_f32(scales[i / 64]);\n    float bi = oracle_bf16_to_f32(biases[i / 64]);",
+                                  "float sc = oracle_bf16_to_f32(biases[i / 64]);\n    float bi = oracle_bf16_to_f32(scales[i / 64]);"),
+    "affine_nibble_mask_wide": ("uint32_t mask = (bits == 8) ? 0xffu : 0x0fu;",
+                                "uint32_t mask = (bits == 8) ? 0xffu : 0x1fu;"),
 }
 
 
