@@ -42,22 +42,27 @@ FAMILY_SOURCES = {"gemv": ["block_quantized_matvec_gguf_amd/csrc/qmv_gemv.hip",
                            "block_quantized_matvec_gguf_amd/csrc/qmv_units.h"],
                   "gemv_t": ["block_quantized_matvec_gguf_amd/csrc/qmv_gemv_t.hip",
                              "block_quantized_matvec_gguf_amd/csrc/qmv_units.h"],
+                  "affine": ["block_quantized_matvec_gguf_amd/csrc/qmv_gemv.hip",
+                             "block_quantized_matvec_gguf_amd/csrc/qmv_units.h"],
                   "mfma": ["block_quantized_matvec_gguf_amd/csrc/qmv_mfma.hip"],
                   "simple": ["block_quantized_matvec_gguf_amd/csrc/qmv_simple.hip"]}
 # the dispatches whose counters and durations are the family's (not x staging
 # or the partial-sum reduction)
 MAIN_KERNEL = {"gemv": "qmv_gemv", "gemv_t": "qmv_gemv_t_staged", "mfma": "qmv_mfma_q4_k",
-               "simple": "qmv_simple"}
+               "simple": "qmv_simple", "affine": "qmv_affine_gemv"}
 METRIC = "effective weight-read GB/s and % of MI355X HBM peak for quantized GEMV"
 
 
 def kernel_family(kernel_name: str) -> str:
     return ("mfma" if kernel_name.startswith("qmv_mfma") else
+            "affine" if kernel_name.startswith("qmv_affine") else
             "simple" if kernel_name.startswith("qmv_simple") else
             "gemv_t" if kernel_name.startswith("qmv_gemv_t") else "gemv")
 
 
-def kernel_name_of(qb, fmt: int, k: int, m: int, algo: int, op: str) -> str:
+def kernel_name_of(qb, fmt, k: int, m: int, algo: int, op: str) -> str:
+    if op == "affine":
+        return qb.qmv_affine_kernel_name(fmt, k)
     if op == "t":
         return qb.qmv_t_kernel_name(fmt, k, algo)
     if op == "moe":
@@ -99,8 +104,9 @@ def summarize_pmc(args):
     from block_quantized_matvec_gguf_amd import binding as qb
     from block_quantized_matvec_gguf_amd import synth
     spec = synth.WORKLOADS[args.workload]
-    family = kernel_family(kernel_name_of(qb, synth.fmt_id(spec["fmt"]), spec["k"], spec["m"],
-                                          qb.ALGOS[args.algo], args.op))
+    fmt_ = spec["bits"] if args.op == "affine" else synth.fmt_id(spec["fmt"])
+    family = kernel_family(kernel_name_of(qb, fmt_, spec["k"], spec["m"], qb.ALGOS[args.algo],
+                                          args.op))
     main_kernel = MAIN_KERNEL[family]
     per = {}
     for path in args.summarize_pmc:
@@ -145,7 +151,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="q6_k_vocab_outproj")
     ap.add_argument("--algo", default="auto")
-    ap.add_argument("--op", choices=["fwd", "t", "moe"], default=None,
+    ap.add_argument("--op", choices=["fwd", "t", "moe", "affine"], default=None,
                     help="fwd: y = x @ W; t: the transposed product dx = dy @ W; moe: the "
                          "expert-indexed product (default: moe for expert workloads, else fwd)")
     ap.add_argument("--tiles", type=int, default=None, help="tiles of the auxiliary run")
@@ -160,7 +166,8 @@ def main():
 
     if args.op is None:
         from block_quantized_matvec_gguf_amd import synth as _s
-        args.op = "moe" if "experts" in _s.WORKLOADS[args.workload] else "fwd"
+        spec_ = _s.WORKLOADS[args.workload]
+        args.op = "moe" if "experts" in spec_ else "affine" if "bits" in spec_ else "fwd"
     if args.summarize_pmc:
         summarize_pmc(args)
         return
@@ -175,10 +182,18 @@ def main():
     from block_quantized_matvec_gguf_amd import binding as qb
     from block_quantized_matvec_gguf_amd import synth
 
-    fmt, W, x, spec = synth.workload(args.workload)
-    k, n, m = spec["k"], spec["n"], spec["m"]
     op_t = args.op == "t"
     op_moe = args.op == "moe"
+    op_aff = args.op == "affine"
+    if op_aff:  # three arrays: code words, bf16 scales, bf16 biases
+        spec = synth.WORKLOADS[args.workload]
+        words, scales, biases, x = synth.affine_workload(args.workload)
+        fmt = spec["bits"]
+        W = np.concatenate([words.view(np.uint8).reshape(-1), scales.view(np.uint8).reshape(-1),
+                            biases.view(np.uint8).reshape(-1)])
+    else:
+        fmt, W, x, spec = synth.workload(args.workload)
+    k, n, m = spec["k"], spec["n"], spec["m"]
     if op_t:  # the transposed product reads dy (m x n) and writes dx (m x k)
         x = synth.gen_x(np.random.default_rng(0x51A72000 + spec["id"]), m, n)
     tiles = args.tiles if args.tiles is not None else spec.get("tiles", 8)
@@ -211,12 +226,17 @@ def main():
     xp, yp = xd.data_ptr(), yd.data_ptr()
 
     entry = lib.qmv_run_t_ex if op_t else lib.qmv_run_ex
+    if op_aff:  # the three arrays sit back to back in each weight copy
+        o_s, o_b = words.nbytes, words.nbytes + scales.nbytes
     if op_moe:
         idd = [torch.from_numpy(a).to(dev) for a in id_sets]
         idp = [t.data_ptr() for t in idd]
 
     def run(i, j0=0, j1=n, acc=0):
-        if op_moe:
+        if op_aff:
+            wb = wp[i % copies]
+            rc = lib.qmv_run_affine(fmt, wb, wb + o_s, wb + o_b, xp, yp, k, n, m, j0, j1, acc, sp)
+        elif op_moe:
             # step i: weight copy i % copies, expert set (i // copies) % nsets
             rc = lib.qmv_run_moe_ex(fmt, wp[i % copies], idp[(i // copies) % nsets], xp, yp, k,
                                     n, E, m, top_k, acc, sp, algo)
@@ -320,7 +340,8 @@ def main():
         "config": {"workload": args.workload + ("_transposed" if op_t else ""),
                    **({"experts": E, "top_k": top_k, "expert_sets_rotated": nsets}
                       if op_moe else {}),
-                   "format": synth.FORMAT_NAMES[fmt], "k": k,
+                   "format": ("affine%d_group64" % fmt) if op_aff else synth.FORMAT_NAMES[fmt],
+                   "k": k,
                    "n": n, "m_tokens": m, "accumulate": 0, "weight_bytes": wbytes,
                    "weight_copies_rotated": copies,
                    "kernel": kname},
@@ -334,7 +355,20 @@ def main():
                         "value": round(wbytes / tstep / 1e9, 1),
                         "pct_hbm_peak": round(100.0 * wbytes / tstep / 1e9 / HBM_PEAK_GBS, 2)}
 
-    if not args.no_cpu_baseline and op_moe:
+    if not args.no_cpu_baseline and op_aff:
+        import oracle
+        threads = max(1, min(os.cpu_count() or 1, 16))
+        t0 = time.perf_counter()
+        yref, sref = oracle.affine_gemv(fmt, words, scales, biases, x, k, n, threads=threads)
+        dt = time.perf_counter() - t0
+        out["cpu_baseline"] = {
+            "value": round(wbytes / dt / 1e9, 3), "unit": "GB/s", "cores": threads,
+            "kind": "oracle", "sample": "all %d rows, m=%d, f64 accumulation; %.2f s"
+                                        % (n, m, dt)}
+        res = oracle.check_parity(y_main, yref, sref)
+        out["parity"] = {"ok": res["ok"], "max_err_over_tol": round(res["max_ratio"], 5),
+                         "cosine": res["cosine"], "outputs": res["n"]}
+    elif not args.no_cpu_baseline and op_moe:
         import oracle
         threads = max(1, min(os.cpu_count() or 1, 16))
         t0 = time.perf_counter()

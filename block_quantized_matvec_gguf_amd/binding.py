@@ -81,6 +81,10 @@ def load(path: str | None = None):
         lib.qmv_run_moe_ex.restype = ci
         lib.qmv_moe_kernel_name.argtypes = [ci, i64, ci]
         lib.qmv_moe_kernel_name.restype = ctypes.c_char_p
+        lib.qmv_run_affine.argtypes = [ci, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, ci, vp]
+        lib.qmv_run_affine.restype = ci
+        lib.qmv_affine_kernel_name.argtypes = [ci, i64]
+        lib.qmv_affine_kernel_name.restype = ctypes.c_char_p
         _lib = lib
         return lib
 
@@ -141,6 +145,17 @@ def qmv_run_moe_ex(format: int, W: int, ids: int, x: int, y: int, k: int, n: int
 
 def qmv_moe_kernel_name(format: int, k: int, algo: int = QMV_ALGO_AUTO) -> str:
     return load().qmv_moe_kernel_name(format, k, algo).decode()
+
+
+def qmv_run_affine(bits: int, codes: int, scales: int, biases: int, x: int, y: int, k: int,
+                   n: int, m_tokens: int, j_start: int, j_end: int, accumulate: int,
+                   stream: int | None) -> int:
+    return int(load().qmv_run_affine(bits, codes, scales, biases, x, y, k, n, m_tokens,
+                                     j_start, j_end, accumulate, stream))
+
+
+def qmv_affine_kernel_name(bits: int, k: int) -> str:
+    return load().qmv_affine_kernel_name(bits, k).decode()
 
 
 def qmv_weight_bytes(format: int, k: int, n: int) -> int:
@@ -260,6 +275,40 @@ def matvec_moe(fmt, W, ids, x, k: int, n: int, n_experts: int, top_k: int, y=Non
     with torch.cuda.device(x.device):
         rc = qmv_run_moe_ex(f, W.data_ptr(), ids.data_ptr(), x2.data_ptr(), y.data_ptr(), k, n,
                             n_experts, n_pos, top_k, 1 if accumulate else 0, s.cuda_stream, a)
+    if rc != QMV_OK:
+        raise QmvError(rc, qmv_last_error())
+    return y
+
+
+def matvec_affine(bits: int, codes, scales, biases, x, k: int, n: int, y=None,
+                  j_start: int = 0, j_end: int | None = None, accumulate: bool = False,
+                  stream=None):
+    """y (=|+=) x @ W on the GPU for affine group-64 rows: codes, scales and
+    biases are contiguous CUDA tensors of n*k*bits/8, n*k/32 and n*k/32 bytes
+    (any dtype holding those bits); x float32 (m, k); y float32 (m, n)."""
+    import torch
+    if j_end is None:
+        j_end = n
+    for name, t, nb in (("codes", codes, n * k * bits // 8), ("scales", scales, n * k // 32),
+                        ("biases", biases, n * k // 32)):
+        if not t.is_cuda or not t.is_contiguous() or t.numel() * t.element_size() != nb:
+            raise ValueError("%s must be a contiguous CUDA tensor of %d bytes" % (name, nb))
+    if x.dtype != torch.float32 or not x.is_cuda or not x.is_contiguous():
+        raise ValueError("x must be a contiguous float32 CUDA tensor")
+    x2 = x.reshape(1, -1) if x.dim() == 1 else x
+    if x2.shape[1] != k:
+        raise ValueError("x has %d columns, expected k=%d" % (x2.shape[1], k))
+    m = x2.shape[0]
+    if y is None:
+        y = torch.empty((m, n), dtype=torch.float32, device=x.device)
+    if y.dtype != torch.float32 or not y.is_cuda or not y.is_contiguous() or y.numel() != m * n:
+        raise ValueError("y must be a contiguous float32 CUDA tensor of m*n elements")
+    ensure_context()
+    s = stream if stream is not None else torch.cuda.current_stream(x.device)
+    with torch.cuda.device(x.device):
+        rc = qmv_run_affine(bits, codes.data_ptr(), scales.data_ptr(), biases.data_ptr(),
+                            x2.data_ptr(), y.data_ptr(), k, n, m, j_start, j_end,
+                            1 if accumulate else 0, s.cuda_stream)
     if rc != QMV_OK:
         raise QmvError(rc, qmv_last_error())
     return y

@@ -474,3 +474,76 @@ int qmv_run_moe(int format, const void *W, const uint32_t *ids, const float *x, 
 }
 
 } // extern "C"
+
+extern "C" {
+
+const char *qmv_affine_kernel_name(int bits, int64_t k) {
+    if ((bits != 4 && bits != 8) || k <= 0 || k % 64 != 0) return "";
+    qmv::GemvPlan p;
+    if (!qmv::plan_gemv(bits == 4 ? qmv::FMT_AFFINE4 : qmv::FMT_AFFINE8, k, 1, 1, 256, &p))
+        return "";
+    return bits == 4 ? "qmv_affine_gemv<4>" : "qmv_affine_gemv<8>";
+}
+
+int qmv_run_affine(int bits, const void *codes, const void *scales, const void *biases,
+                   const float *x, float *y, int64_t k, int64_t n, int64_t m_tokens,
+                   int64_t j_start, int64_t j_end, int accumulate, void *stream) {
+    t_err.clear();
+    if (bits != 4 && bits != 8)
+        return fail(QMV_ERR_INVALID_ARGUMENT, "bits must be 4 or 8, got %d", bits);
+    if (k < 0 || n < 0 || m_tokens < 0)
+        return fail(QMV_ERR_INVALID_ARGUMENT, "negative shape k=%lld n=%lld m=%lld",
+                    (long long)k, (long long)n, (long long)m_tokens);
+    if (k % 64 != 0)
+        return fail(QMV_ERR_INVALID_ARGUMENT, "k %lld must be a multiple of the group size 64",
+                    (long long)k);
+    if (j_start < 0 || j_end < j_start || j_end > n)
+        return fail(QMV_ERR_INVALID_ARGUMENT, "row range [%lld, %lld) outside [0, %lld)",
+                    (long long)j_start, (long long)j_end, (long long)n);
+    if (accumulate != 0 && accumulate != 1)
+        return fail(QMV_ERR_INVALID_ARGUMENT, "accumulate must be 0 or 1, got %d", accumulate);
+    const bool work = m_tokens > 0 && j_end > j_start;
+    if (work) {
+        if (!y) return fail(QMV_ERR_INVALID_ARGUMENT, "y is NULL");
+        if (k > 0 && (!codes || !scales || !biases || !x))
+            return fail(QMV_ERR_INVALID_ARGUMENT, "codes, scales, biases or x is NULL");
+        if (((uintptr_t)codes & 15) != 0)
+            return fail(QMV_ERR_MISALIGNED, "codes must be 16-byte aligned");
+        if (((uintptr_t)scales & 1) != 0 || ((uintptr_t)biases & 1) != 0)
+            return fail(QMV_ERR_MISALIGNED, "scales and biases must be 2-byte aligned");
+        if (((uintptr_t)x & 3) != 0 || ((uintptr_t)y & 3) != 0)
+            return fail(QMV_ERR_MISALIGNED, "x and y must be 4-byte aligned");
+    }
+    if (g_refs.load() <= 0)
+        return fail(QMV_ERR_NOT_INITIALIZED, "qmv_run_affine before qmv_create");
+    if (!work) return QMV_OK;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(QMV_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+    if (dev < 0 || (size_t)dev >= g_dev.size() || !g_dev[(size_t)dev].gfx950)
+        return fail(QMV_ERR_UNSUPPORTED_ARCH, "device %d is not gfx950", dev);
+    const int num_cu = g_dev[(size_t)dev].num_cu;
+    hipStream_t s = (hipStream_t)stream;
+    if (k == 0) {
+        if (accumulate) return QMV_OK;
+        e = qmv::launch_fill_zero(y, n, m_tokens, j_start, j_end, s);
+        if (e != hipSuccess) return fail(QMV_ERR_HIP, "fill launch: %s", hipGetErrorString(e));
+        return QMV_OK;
+    }
+    const int fmt = bits == 4 ? qmv::FMT_AFFINE4 : qmv::FMT_AFFINE8;
+    const int64_t rows = j_end - j_start;
+    for (int64_t t0 = 0; t0 < m_tokens;) {
+        qmv::GemvPlan p;
+        const int mt_max = (m_tokens - t0) >= 2 ? 2 : 1;
+        if (!qmv::plan_gemv(fmt, k, rows, mt_max, num_cu, &p))
+            return fail(QMV_ERR_UNSUPPORTED, "affine plan failed for k=%lld", (long long)k);
+        e = qmv::launch_affine(p, (const uint8_t *)codes, (const uint16_t *)scales,
+                               (const uint16_t *)biases, x + t0 * k, y + t0 * n, k, n, j_start,
+                               j_end, accumulate, s);
+        if (e != hipSuccess) return fail(QMV_ERR_HIP, "affine launch: %s", hipGetErrorString(e));
+        t0 += p.MT;
+    }
+    return QMV_OK;
+}
+
+} // extern "C"

@@ -218,7 +218,8 @@ __device__ __forceinline__ void direct_body(const uint8_t *__restrict__ W,
                                             const float *__restrict__ x, float *__restrict__ y,
                                             int64_t k, int64_t n, int64_t row_bytes,
                                             int64_t j_start, int64_t j_end, int accumulate,
-                                            int U, int L, int P, int G) {
+                                            int U, int L, int P, int G,
+                                            const typename F::Aux &aux) {
     extern __shared__ float smem[];
     const Lanes<UPL> ln(U, L, G);
     const int64_t rows_per_batch = (int64_t)P * RB;
@@ -247,9 +248,11 @@ __device__ __forceinline__ void direct_body(const uint8_t *__restrict__ W,
 #pragma unroll
         for (int r = 0; r < RB; r++) {
             const int64_t jr = b + (int64_t)r * P;
-            const uint8_t *row = jr + ln.slot < j_end ? Wslot + jr * row_bytes : last_row;
+            const bool in = jr + ln.slot < j_end;
+            const uint8_t *row = in ? Wslot + jr * row_bytes : last_row;
+            const int64_t j = in ? jr + ln.slot : j_end - 1; // the row index (per-row fields)
 #pragma unroll
-            for (int i = 0; i < UPL; i++) F::load(raw[r][i], row, ln.ulod[i], U);
+            for (int i = 0; i < UPL; i++) F::load(raw[r][i], row, ln.ulod[i], U, aux, j);
         }
         if (accumulate) yp.fetch(y, n, b, j_end, P, ln.tid, ln.T);
     };
@@ -419,7 +422,7 @@ __global__ __launch_bounds__(512) void qmv_gemv_direct(const uint8_t *__restrict
                                                         int accumulate, int U, int L, int P,
                                                         int G, int) {
     direct_body<F, MT, UPL, RB, XL>(W, x, y, k, n, row_bytes, j_start, j_end, accumulate, U, L,
-                                    P, G);
+                                    P, G, typename F::Aux{});
 }
 
 template <class F, int MT, int UPL, int RB, int NPT, bool XL>
@@ -466,7 +469,7 @@ __global__ __launch_bounds__(512) void qmv_gemv_moe_direct(const uint8_t *__rest
     direct_body<F, 1, UPL, RB, XL>(W + (int64_t)e * n * row_bytes,
                                    x + (int64_t)(blockIdx.y / top_k) * k,
                                    y + (int64_t)blockIdx.y * n, k, n, row_bytes, 0, n,
-                                   accumulate, U, L, P, G);
+                                   accumulate, U, L, P, G, typename F::Aux{});
 }
 
 template <class F, int UPL, int RB, int NPT, bool XL>
@@ -481,6 +484,22 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(
                                         x + (int64_t)(blockIdx.y / top_k) * k,
                                         y + (int64_t)blockIdx.y * n, k, n, row_bytes, 0, n,
                                         accumulate, U, L, P, G, buf_bytes);
+}
+
+// Affine group-64 rows: the direct body over the code words, with the scales
+// and biases of each (row, group) read alongside.
+template <int BITS, int MT, int UPL, int RB, bool XL>
+__global__ __launch_bounds__(512) void qmv_affine_gemv(const uint8_t *__restrict__ codes,
+                                                        const uint16_t *__restrict__ scales,
+                                                        const uint16_t *__restrict__ biases,
+                                                        const float *__restrict__ x,
+                                                        float *__restrict__ y, int64_t k,
+                                                        int64_t n, int64_t j_start, int64_t j_end,
+                                                        int accumulate, int U, int L, int P,
+                                                        int G) {
+    const typename UAffine<BITS>::Aux aux = {scales, biases, k / 64};
+    direct_body<UAffine<BITS>, MT, UPL, RB, XL>(codes, x, y, k, n, k * BITS / 8, j_start, j_end,
+                                                accumulate, U, L, P, G, aux);
 }
 
 // -------------------------------------------------------------- planning
@@ -535,6 +554,8 @@ bool plan_gemv(int fmt, int64_t k, int64_t rows, int mt_max, int num_cu, GemvPla
         if (k % 256) return false;
         rb = (k / 256) * 210;
         break;
+    case FMT_AFFINE4: rb = k / 2; break;
+    case FMT_AFFINE8: rb = k; break;
     default: return false;
     }
     g.staged = staged_format(fmt) ? 1 : 0;
@@ -676,6 +697,54 @@ static hipError_t launch_direct(const GemvPlan &p0, const uint8_t *W, const floa
     if (p.UPL == 2) return launch_direct_rb<F, 1, 2, false>(p, W, x, y, k, n, rb, j0, j1, acc, s);
     if (p.MT == 2) return launch_direct_rb<F, 2, 1, false>(p, W, x, y, k, n, rb, j0, j1, acc, s);
     return launch_direct_rb<F, 1, 1, false>(p, W, x, y, k, n, rb, j0, j1, acc, s);
+}
+
+// ------------------------------------------------ affine launches
+struct AffineArgs {
+    const uint16_t *scales, *biases;
+};
+
+template <int BITS, int MT, int UPL, int RB, bool XL>
+static hipError_t launch_affine_k(const GemvPlan &p, const uint8_t *q, const AffineArgs &a,
+                                  const float *x, float *y, int64_t k, int64_t n, int64_t j0,
+                                  int64_t j1, int acc, hipStream_t s) {
+    auto kernel = qmv_affine_gemv<BITS, MT, UPL, RB, XL>;
+    if (p.lds_bytes > 64 * 1024 &&
+        hipFuncSetAttribute((const void *)kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)p.lds_bytes) != hipSuccess)
+        return hipGetLastError();
+    const int64_t cap = (int64_t)p.num_cu * resident_per_cu(kernel, p.T, p.lds_bytes);
+    const int grid = (int)(p.grid < cap ? p.grid : cap);
+    hipLaunchKernelGGL(kernel, dim3(grid), dim3(p.T), p.lds_bytes, s, q, a.scales, a.biases, x, y,
+                       k, n, j0, j1, acc, p.U, p.L, p.P, p.G);
+    return hipGetLastError();
+}
+
+template <int BITS, bool XL>
+static hipError_t launch_affine_x(const GemvPlan &p, const uint8_t *q, const AffineArgs &a,
+                                  const float *x, float *y, int64_t k, int64_t n, int64_t j0,
+                                  int64_t j1, int acc, hipStream_t s) {
+    if (p.UPL == 2) return launch_affine_k<BITS, 1, 2, 1, XL>(p, q, a, x, y, k, n, j0, j1, acc, s);
+    if (p.MT == 2) return launch_affine_k<BITS, 2, 1, 1, XL>(p, q, a, x, y, k, n, j0, j1, acc, s);
+    if (p.RB == 2) return launch_affine_k<BITS, 1, 1, 2, XL>(p, q, a, x, y, k, n, j0, j1, acc, s);
+    return launch_affine_k<BITS, 1, 1, 1, XL>(p, q, a, x, y, k, n, j0, j1, acc, s);
+}
+
+hipError_t launch_affine(const GemvPlan &p0, const uint8_t *codes, const uint16_t *scales,
+                         const uint16_t *biases, const float *x, float *y, int64_t k, int64_t n,
+                         int64_t j_start, int64_t j_end, int accumulate, hipStream_t s) {
+    GemvPlan p = p0;
+    const AffineArgs a = {scales, biases};
+    const bool xl = use_x_lds(p, x, k);
+    if (p.fmt == FMT_AFFINE4)
+        return xl ? launch_affine_x<4, true>(p, codes, a, x, y, k, n, j_start, j_end, accumulate, s)
+                  : launch_affine_x<4, false>(p, codes, a, x, y, k, n, j_start, j_end, accumulate,
+                                              s);
+    if (p.fmt == FMT_AFFINE8)
+        return xl ? launch_affine_x<8, true>(p, codes, a, x, y, k, n, j_start, j_end, accumulate, s)
+                  : launch_affine_x<8, false>(p, codes, a, x, y, k, n, j_start, j_end, accumulate,
+                                              s);
+    return hipErrorInvalidValue;
 }
 
 // ------------------------------------------------ expert-indexed launches

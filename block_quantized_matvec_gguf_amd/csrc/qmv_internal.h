@@ -14,7 +14,10 @@ enum Fmt {
     FMT_Q4_K = 4,
     FMT_Q6_K = 5,
     FMT_Q8_0 = 6,
-    FMT_Q5_0 = 7
+    FMT_Q5_0 = 7,
+    // internal: affine group-64 rows (codes, scales and biases in separate arrays)
+    FMT_AFFINE4 = 104,
+    FMT_AFFINE8 = 108
 };
 
 // Geometry of one streaming-GEMV launch (see qmv_gemv.hip for the mapping).
@@ -74,6 +77,12 @@ hipError_t launch_simple(int fmt, const uint8_t *W, const float *x, float *y, in
 
 hipError_t launch_fill_zero(float *y, int64_t n, int64_t m, int64_t j_start, int64_t j_end,
                             hipStream_t stream);
+
+// Affine group-64 rows (bits 4 or 8): codes k*bits/8 bytes per row, bf16
+// scales and biases k/64 per row; y (=|+=) x @ W for rows [j_start, j_end).
+hipError_t launch_affine(const GemvPlan &p, const uint8_t *codes, const uint16_t *scales,
+                         const uint16_t *biases, const float *x, float *y, int64_t k, int64_t n,
+                         int64_t j_start, int64_t j_end, int accumulate, hipStream_t stream);
 
 // Expert-indexed product: pair r = p*top_k + slot of n_pos*top_k computes
 // y[r] (=|+=) x[p] @ W_{ids[r]} over all n rows of that expert.

@@ -520,7 +520,9 @@ template <bool BF>
 struct UHalf {
     struct Raw { u32x4 c[8]; };
     struct X { float v[8][8]; };
-    static __device__ __forceinline__ void load(Raw &r, const uint8_t *row, int u, int U) {
+    struct Aux {}; // nothing beyond the row's bytes
+    static __device__ __forceinline__ void load(Raw &r, const uint8_t *row, int u, int U,
+                                                const Aux &, int64_t) {
 #pragma unroll
         for (int c = 0; c < 8; c++) r.c[c] = ld16(row + 16 * (u + U * c));
     }
@@ -598,6 +600,71 @@ __device__ __forceinline__ void lds_barrier() {
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
+
+// ------------------------------------------- affine group-64 units
+// Rows of affine group-quantized weights (moeflux, tests/graph_diff_oracle.rs:
+// codes packed into u32 words, one bf16 scale and one bf16 bias per group of
+// 64 weights, value code * scale + bias), held in three arrays: the code
+// words (k*BITS/8 bytes per row), the scales and the biases (k/64 per row).
+// Code i of a word sits at bits BITS*i .. BITS*i+BITS-1. A unit is one group:
+// its 32 (4-bit) or 64 (8-bit) code bytes, loaded as 16-byte pieces, and its
+// scale and bias. Each weight is decoded exactly as the oracle does (fma of
+// the code with the scale and the bias: the product is exact, one rounding),
+// then multiplied into the sum.
+template <int BITS>
+struct UAffine {
+    struct Aux {
+        const uint16_t *scales, *biases;
+        int64_t groups; // per row
+    };
+    struct Raw { u32x4 c[BITS / 2]; uint32_t s, b; };
+    struct X { float v[64]; };
+    static __device__ __forceinline__ void load(Raw &r, const uint8_t *row, int u, int,
+                                                const Aux &a, int64_t j) {
+#pragma unroll
+        for (int c = 0; c < BITS / 2; c++) r.c[c] = ld16(row + 8 * BITS * u + 16 * c);
+        r.s = a.scales[j * a.groups + u];
+        r.b = a.biases[j * a.groups + u];
+    }
+    static __device__ __forceinline__ int x4_index(int u, int i, int) { return 16 * u + i; }
+    static __device__ __forceinline__ void x4_slot(int q, int, int &u, int &i) {
+        u = q >> 4;
+        i = q & 15;
+    }
+    static __device__ __forceinline__ void put_x(X &x, int i, f32x4 v) { put4(&x.v[4 * i], v); }
+    static __device__ __forceinline__ f32x4 get_x(const X &x, int i) { return get4(&x.v[4 * i]); }
+    static __device__ __forceinline__ void finish_x(X &) {}
+    static __device__ __forceinline__ float dot(const Raw &r, const X &x, int) {
+        const float s = __builtin_bit_cast(float, r.s << 16);
+        const float b = __builtin_bit_cast(float, r.b << 16);
+        float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+        for (int w = 0; w < 2 * BITS; w++) {
+            const uint32_t word = r.c[w >> 2][w & 3];
+            if (BITS == 4) {
+                // bytes of lo: codes 0, 2, 4, 6 of the word; of hi: 1, 3, 5, 7
+                const uint32_t lo = opaque(word & 0x0f0f0f0fu);
+                const uint32_t hi = opaque((word >> 4) & 0x0f0f0f0fu);
+                const float *xv = &x.v[8 * w];
+                a0 = fmaf(fmaf(ub0(lo), s, b), xv[0], a0);
+                a1 = fmaf(fmaf(ub0(hi), s, b), xv[1], a1);
+                a0 = fmaf(fmaf(ub1(lo), s, b), xv[2], a0);
+                a1 = fmaf(fmaf(ub1(hi), s, b), xv[3], a1);
+                a0 = fmaf(fmaf(ub2(lo), s, b), xv[4], a0);
+                a1 = fmaf(fmaf(ub2(hi), s, b), xv[5], a1);
+                a0 = fmaf(fmaf(ub3(lo), s, b), xv[6], a0);
+                a1 = fmaf(fmaf(ub3(hi), s, b), xv[7], a1);
+            } else {
+                const float *xv = &x.v[4 * w];
+                a0 = fmaf(fmaf(ub0(word), s, b), xv[0], a0);
+                a1 = fmaf(fmaf(ub1(word), s, b), xv[1], a1);
+                a0 = fmaf(fmaf(ub2(word), s, b), xv[2], a0);
+                a1 = fmaf(fmaf(ub3(word), s, b), xv[3], a1);
+            }
+        }
+        return a0 + a1;
+    }
+};
 
 // Lane geometry common to both kernels.
 template <int UPL>

@@ -172,6 +172,9 @@ WORKLOADS = {
     "q4_k_prefill": dict(id=5, fmt="q4_k", k=4096, n=14336, m=64),
     # expert-indexed decode: 64 stacked experts of n rows, 8 chosen per position
     "q4_k_moe_decode": dict(id=8, fmt="q4_k", k=2048, n=1536, m=1, experts=64, top_k=8),
+    # affine group-64 rows (codes, scales and biases in three arrays)
+    "affine4_ffn_up": dict(id=9, fmt="affine", bits=4, k=2560, n=10240, m=1),
+    "affine8_ffn_up": dict(id=10, fmt="affine", bits=8, k=2560, n=10240, m=1),
 }
 
 
@@ -188,6 +191,15 @@ def workload(name: str, n: int | None = None):
     W = gen_weights(f, rw, spec["n"] * spec.get("experts", 1), spec["k"])
     x = gen_x(rx, spec["m"], spec["k"])
     return f, W, x, spec
+
+
+def affine_workload(name: str):
+    """(words, scales, biases, x) of a named affine workload."""
+    spec = WORKLOADS[name]
+    rw = np.random.default_rng(0x51A70000 + spec["id"])
+    rx = np.random.default_rng(0x51A71000 + spec["id"])
+    words, sc, bi = gen_affine(rw, spec["bits"], spec["n"], spec["k"])
+    return words, sc, bi, gen_x(rx, spec["m"], spec["k"])
 
 
 def moe_ids(spec) -> np.ndarray:

@@ -194,6 +194,30 @@ int qmv_run_moe_ex(int format, const void *W, const uint32_t *ids, const float *
                    int64_t k, int64_t n, int64_t n_experts, int64_t n_pos, int64_t top_k,
                    int accumulate, void *stream, int algo);
 
+/* Enqueue y (=|+=) x @ W for rows [j_start, j_end) on `stream`, W held as
+ * affine group-quantized rows (moeflux, tests/graph_diff_oracle.rs, the
+ * 4-bit embedding fixture and its MatvecNTokens 4-bit / 8-bit variants):
+ *
+ *     w_j[i] = code_j[i] * scale_j[i / 64] + bias_j[i / 64]
+ *
+ *   bits        4 or 8.
+ *   codes       n rows of k*bits/32 little-endian u32 words, 16-byte aligned;
+ *               code i of a row is bits-wide field i mod (32/bits) of word
+ *               i / (32/bits), lowest bits first.
+ *   scales, biases  n rows of k/64 bfloat16 values each (2-byte aligned).
+ *   x, y, k, n, m_tokens, j_start, j_end, accumulate, stream  as for qmv_run;
+ *               k a multiple of 64 and at most 65536 (QMV_ERR_UNSUPPORTED
+ *               above).
+ *
+ * Returns the codes of qmv_run. Allocates nothing; deterministic; a row's
+ * result does not depend on the row range. */
+int qmv_run_affine(int bits, const void *codes, const void *scales, const void *biases,
+                   const float *x, float *y, int64_t k, int64_t n, int64_t m_tokens,
+                   int64_t j_start, int64_t j_end, int accumulate, void *stream);
+
+/* Name of the kernel qmv_run_affine launches, or "" for an invalid request. */
+const char *qmv_affine_kernel_name(int bits, int64_t k);
+
 /* Release one reference to the context; the last one frees it. Safe to call
  * when not initialised. Must not race with qmv_run or qmv_create. */
 void qmv_destroy(void);

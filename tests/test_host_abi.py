@@ -30,7 +30,8 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     for need in ("qmv_create", "qmv_run", "qmv_destroy", "qmv_run_ex", "qmv_weight_bytes",
                  "qmv_last_error", "qmv_run_t", "qmv_run_t_ex", "qmv_t_kernel_name",
-                 "qmv_run_moe", "qmv_run_moe_ex", "qmv_moe_kernel_name"):
+                 "qmv_run_moe", "qmv_run_moe_ex", "qmv_moe_kernel_name", "qmv_run_affine",
+                 "qmv_affine_kernel_name"):
         assert need in names
 
 
@@ -116,6 +117,29 @@ def test_moe_kernel_names_and_errors(lib):
     assert run(n_pos=70000, top_k=1) == qb.QMV_ERR_UNSUPPORTED
     assert run() == qb.QMV_ERR_NOT_INITIALIZED
     assert run(n_pos=0, ids=0, x=0, y=0) == qb.QMV_ERR_NOT_INITIALIZED
+
+
+def test_affine_kernel_names_and_errors(lib):
+    assert qb.qmv_affine_kernel_name(4, 2560) == "qmv_affine_gemv<4>"
+    assert qb.qmv_affine_kernel_name(8, 64) == "qmv_affine_gemv<8>"
+    assert qb.qmv_affine_kernel_name(4, 96) == ""
+    assert qb.qmv_affine_kernel_name(3, 64) == ""
+
+    def run(**kw):
+        a = dict(bits=4, codes=0x1000, scales=0x2000, biases=0x3000, x=0x4000, y=0x5000, k=128,
+                 n=8, m=1, j0=0, j1=8, acc=0)
+        a.update(kw)
+        return qb.qmv_run_affine(a["bits"], a["codes"], a["scales"], a["biases"], a["x"],
+                                 a["y"], a["k"], a["n"], a["m"], a["j0"], a["j1"], a["acc"],
+                                 None)
+    E = qb.QMV_ERR_INVALID_ARGUMENT
+    assert run(bits=2) == E
+    assert run(k=96) == E
+    assert run(j1=9) == E
+    assert run(biases=0) == E
+    assert run(codes=0x1004) == qb.QMV_ERR_MISALIGNED
+    assert run(scales=0x2001) == qb.QMV_ERR_MISALIGNED
+    assert run() == qb.QMV_ERR_NOT_INITIALIZED
 
 
 def _run_t(**kw):
