@@ -18,7 +18,7 @@
 //     launch. At the end the P slots' vectors are added in a fixed tree in LDS
 //     and the workgroup writes its partial dx (k floats) to scratch.
 //  2. qmv_gemv_t_reduce: adds the partials of all workgroups in a fixed order
-//     (16 interleaved running sums, then a fixed tree) and writes or adds dx.
+//     (64 interleaved running sums, then a fixed tree) and writes or adds dx.
 // Scratch (grid * k floats) comes from the stream's memory pool
 // (hipMallocAsync / hipFreeAsync). Rows are assigned to workgroups by the
 // row range and the grid size only, so a launch is deterministic run to run.
@@ -144,28 +144,28 @@ __global__ __launch_bounds__(512) void qmv_gemv_t_staged(const uint8_t *__restri
     }
 }
 
-// dx (=|+=) sum over the G workgroup partials. Workgroup: 64 consecutive
-// outputs (16 float4 pieces) x 16 running sums; running sum g adds partials
-// g, g+16, g+32, ... in that order, then the 16 sums meet in a fixed tree.
+// dx (=|+=) sum over the G workgroup partials. Workgroup: 16 consecutive
+// outputs (4 float4 pieces) x 64 running sums; running sum g adds partials
+// g, g+64, g+128, ... in that order, then the 64 sums meet in a fixed tree.
 __global__ __launch_bounds__(256) void qmv_gemv_t_reduce(const float *__restrict__ part,
                                                          float *__restrict__ dx, int64_t k, int G,
                                                          int accumulate) {
-    __shared__ f32x4 red[16][16];
-    const int p = threadIdx.x & 15, g = threadIdx.x >> 4;
-    const int64_t e = (int64_t)blockIdx.x * 64 + 4 * p;
+    __shared__ f32x4 red[64][4];
+    const int p = threadIdx.x & 3, g = threadIdx.x >> 2;
+    const int64_t e = (int64_t)blockIdx.x * 16 + 4 * p;
     f32x4 s = {0.f, 0.f, 0.f, 0.f};
     int q = g;
-    for (; q + 16 * 7 < G; q += 16 * 8) {
+    for (; q + 64 * 7 < G; q += 64 * 8) {
         f32x4 v[8];
 #pragma unroll
-        for (int u = 0; u < 8; u++) v[u] = *(const f32x4 *)(part + (int64_t)(q + 16 * u) * k + e);
+        for (int u = 0; u < 8; u++) v[u] = *(const f32x4 *)(part + (int64_t)(q + 64 * u) * k + e);
 #pragma unroll
         for (int u = 0; u < 8; u++) s += v[u];
     }
-    for (; q < G; q += 16) s += *(const f32x4 *)(part + (int64_t)q * k + e);
+    for (; q < G; q += 64) s += *(const f32x4 *)(part + (int64_t)q * k + e);
     red[g][p] = s;
     __syncthreads();
-    for (int h = 8; h >= 1; h >>= 1) {
+    for (int h = 32; h >= 1; h >>= 1) {
         if (g < h) red[g][p] += red[g + h][p];
         __syncthreads();
     }
@@ -232,8 +232,12 @@ bool plan_gemv_t(int fmt, int64_t k, int64_t rows, int num_cu, GemvTPlan *out) {
     // (+16: the unaligned field reads may touch one dword past a row)
     g.lds_bytes = (wbuf > red ? wbuf : red) + 16;
     if (g.lds_bytes > 160 * 1024) return false;
+    // enough batches per workgroup (8) to pipeline the copies, at least one
+    // workgroup per compute unit, at most T_MAX_GRID partials
     const int64_t batches = (rows + g.P - 1) / g.P;
-    g.grid = (int)(batches < T_MAX_GRID ? batches : T_MAX_GRID);
+    int64_t want = batches / 8 > num_cu ? batches / 8 : num_cu;
+    if (want > batches) want = batches;
+    g.grid = (int)(want < T_MAX_GRID ? want : T_MAX_GRID);
     g.num_cu = num_cu;
     *out = g;
     return true;
@@ -261,7 +265,7 @@ hipError_t launch_t_k(const GemvTPlan &p, const uint8_t *W, const float *dy, flo
                            row_bytes, j_start, j_end, p.U, p.L, p.P, p.buf_bytes);
         e = hipGetLastError();
         if (e != hipSuccess) break;
-        hipLaunchKernelGGL(qmv_gemv_t_reduce, dim3((unsigned)(k / 64)), dim3(256), 0, s, part,
+        hipLaunchKernelGGL(qmv_gemv_t_reduce, dim3((unsigned)(k / 16)), dim3(256), 0, s, part,
                            dx + t * k, k, grid, accumulate);
         e = hipGetLastError();
     }
