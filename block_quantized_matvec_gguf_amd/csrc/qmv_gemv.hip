@@ -167,9 +167,18 @@ __device__ __forceinline__ void finish_batch(const float *rb, const float *ybuf,
         const int s = rr / RB, r = rr % RB;
         const int64_t j = base + (int64_t)r * P + s;
         if (j < j_end) {
+            // the group sums in order g = 0, 1, ...; the reads of each run of
+            // eight are issued together rather than one LDS round trip each
             const float *src = rb + q * NG;
             float v = src[0];
-            for (int g = 1; g < NG; g++) v += src[g];
+            for (int g0 = 1; g0 < NG; g0 += 8) {
+                float c[8];
+#pragma unroll
+                for (int i = 0; i < 8; i++) c[i] = g0 + i < NG ? src[g0 + i] : 0.f;
+#pragma unroll
+                for (int i = 0; i < 8; i++)
+                    if (g0 + i < NG) v += c[i];
+            }
             store_y(y + t * n + j, v, accumulate, ybuf, q);
         }
     }
@@ -332,9 +341,11 @@ __device__ __forceinline__ void staged_body(const uint8_t *__restrict__ W,
     const int n4 = (int)(k >> 2), nt4 = n4 * MT;
     const int nq = P * RB * MT;
     const int rbytes = (int)row_bytes; // a row of one batch fits in LDS, so in 32 bits
-    const int wave = ln.tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(ln.tid >> 6); // in a scalar register
     // LDS: [x][weight buffer 0][weight buffer 1][2 x group sums][2 x old y]
-    uint8_t *wb = (uint8_t *)(smem + (XL ? k * MT : 0));
+    // (without x in front, 16 bytes of padding: unit reads may touch the
+    // dword before a row)
+    uint8_t *wb = (uint8_t *)(smem + (XL ? k * MT : 4));
     float *red = (float *)(wb + 2 * buf_bytes);
     float *ybuf = red + 2 * nq * ln.NG;
 
@@ -348,14 +359,16 @@ __device__ __forceinline__ void staged_body(const uint8_t *__restrict__ W,
         const __amdgpu_buffer_rsrc_t rs = batch_rsrc(W + a0, 16 * np);
         const int last = 16 * (np - 1);
         uint8_t *dst = wb + bi * buf_bytes;
+        const int voff = 16 * ln.tid;
 #pragma unroll
         for (int s = 0; s < NPT; s++) {
-            const int off = 16 * (ln.tid + s * ln.T);
-            // lane l of this wave writes piece s*T + 64*wave + l
-            uint8_t *slot = dst + __builtin_amdgcn_readfirstlane(16 * (s * ln.T + 64 * wave));
-            if (off <= last) // the buffer holds exactly the batch's pieces
+            // lane l of this wave writes piece s*T + 64*wave + l; the piece's
+            // byte offset is 16*tid (per lane) + 16*s*T (scalar)
+            const int soff = 16 * s * ln.T;
+            uint8_t *slot = dst + 16 * (s * ln.T + 64 * wave);
+            if (voff <= last - soff) // the buffer holds exactly the batch's pieces
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                    rs, (__attribute__((address_space(3))) void *)slot, 16, off, 0, 0,
+                    rs, (__attribute__((address_space(3))) void *)slot, 16, voff, soff, 0,
                     2 /* nontemporal */);
         }
         if (accumulate) yp.fetch(y, n, b, j_end, P, ln.tid, ln.T);
@@ -604,7 +617,7 @@ bool plan_gemv(int fmt, int64_t k, int64_t rows, int mt_max, int num_cu, GemvPla
     // x goes through LDS when everything fits in 96 KB; otherwise each lane
     // reads its x units straight from global memory
     g.x_in_lds = (xb + wbuf + red <= 96 * 1024) ? 1 : 0;
-    g.lds_bytes = (g.x_in_lds ? xb : 0) + wbuf + red;
+    g.lds_bytes = (g.x_in_lds ? xb : (g.staged ? 16 : 0)) + wbuf + red;
     if (g.lds_bytes > 160 * 1024) return false;
     *p = g;
     return true;
@@ -664,7 +677,7 @@ static hipError_t launch_direct_rb(const GemvPlan &p, const uint8_t *W, const fl
 // LDS copy moves 16-byte pieces).
 static bool use_x_lds(GemvPlan &p, const float *x, int64_t k) {
     if (p.x_in_lds && ((uintptr_t)x & 15) == 0) return true;
-    if (p.x_in_lds) p.lds_bytes -= (size_t)k * p.MT * sizeof(float);
+    if (p.x_in_lds) p.lds_bytes -= (size_t)k * p.MT * sizeof(float) - (p.staged ? 16 : 0);
     p.x_in_lds = 0;
     return false;
 }

@@ -41,8 +41,10 @@ __global__ __launch_bounds__(512) void qmv_gemv_t_staged(const uint8_t *__restri
     const Lanes<UPL> ln(U, L, L);
     const int64_t stride = (int64_t)gridDim.x * P;
     const int rbytes = (int)row_bytes;
-    const int wave = ln.tid >> 6;
-    uint8_t *wb = (uint8_t *)smem; // [weight buffer 0][weight buffer 1]
+    const int wave = __builtin_amdgcn_readfirstlane(ln.tid >> 6); // in a scalar register
+    // [16 bytes of padding][weight buffer 0][weight buffer 1]: unit reads may
+    // touch the dword before a row
+    uint8_t *wb = (uint8_t *)smem + 16;
 
     // Start copying the rows [b, b + P) (clipped to j_end) into buffer bi.
     auto copy = [&](int64_t b, int bi) {
@@ -53,13 +55,14 @@ __global__ __launch_bounds__(512) void qmv_gemv_t_staged(const uint8_t *__restri
         const __amdgpu_buffer_rsrc_t rs = batch_rsrc(W + a0, 16 * np);
         const int last = 16 * (np - 1);
         uint8_t *dst = wb + bi * buf_bytes;
+        const int voff = 16 * ln.tid;
 #pragma unroll
         for (int s = 0; s < NPT; s++) {
-            const int off = 16 * (ln.tid + s * ln.T);
-            uint8_t *slot = dst + __builtin_amdgcn_readfirstlane(16 * (s * ln.T + 64 * wave));
-            if (off <= last)
+            const int soff = 16 * s * ln.T;
+            uint8_t *slot = dst + 16 * (s * ln.T + 64 * wave);
+            if (voff <= last - soff)
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                    rs, (__attribute__((address_space(3))) void *)slot, 16, off, 0, 0,
+                    rs, (__attribute__((address_space(3))) void *)slot, 16, voff, soff, 0,
                     2 /* nontemporal */);
         }
     };
@@ -229,8 +232,9 @@ bool plan_gemv_t(int fmt, int64_t k, int64_t rows, int num_cu, GemvTPlan *out) {
     g.buf_bytes = (int)((((g.P * rb + slack + 15) / 16) * 16 + 63) & ~(int64_t)63);
     const size_t wbuf = (size_t)2 * g.buf_bytes;
     const size_t red = (size_t)(g.P / 2) * k * sizeof(float);
-    // (+16: the unaligned field reads may touch one dword past a row)
-    g.lds_bytes = (wbuf > red ? wbuf : red) + 16;
+    // (+16 in front of the weight buffers and +16 after them: the unaligned
+    // field reads may touch one dword before or past a row)
+    g.lds_bytes = (wbuf + 16 > red ? wbuf + 16 : red) + 16;
     if (g.lds_bytes > 160 * 1024) return false;
     // enough batches per workgroup (8) to pipeline the copies, at least one
     // workgroup per compute unit, at most T_MAX_GRID partials

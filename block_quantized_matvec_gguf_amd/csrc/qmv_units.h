@@ -428,21 +428,45 @@ struct UQ4_K {
 // ql[64h + 16lq + i] (g = 0 low nibble, g = 2 high nibble) and
 // ql[64h + 32 + 16lq + i] (g = 1, 3), their top 2 bits are bits 2g..2g+1 of
 // qh[32h + 16lq + i], and their scales are the int8 scales[8h + 2g + lq].
-// Super-blocks are 210 bytes, so fields may sit 2 bytes off a dword
-// boundary (read through lds16u/lds8u). The signed code q-32 is the 6-bit
-// two's-complement reading of q^32: the high 2-bit fields are XORed with
-// 0b10, the 6-bit code is assembled in the top of its byte, and a
-// sign-extending byte conversion yields 4*(q-32).
+// The signed code q-32 is the 6-bit two's-complement reading of q^32: the
+// high 2-bit fields are XORed with 0b10, the 6-bit code is assembled in the
+// top of its byte, and a sign-extending byte conversion yields 4*(q-32).
+//
+// Super-blocks are 210 bytes, so a unit's fields sit either on a dword
+// boundary (sh = 0) or 2 bytes past one (sh = 2), the same for all of its
+// fields. They are read as dwords at aligned LDS addresses and realigned by
+// funnel shifts that also place the nibbles: with the ql dwords read from
+// 4 - sh bytes before the field, alignbit(a[j+1], a[j], 30 - 8 sh) is the
+// field's dword j shifted left by 2 (low nibbles in bits 2..5 of each byte)
+// and alignbit of two such neighbours by 4 is dword j shifted right by 2
+// (high nibbles in bits 2..5). The dword before a field lies in LDS (the
+// previous block, or padding in front of the weight buffers); its bits only
+// reach masked-off positions.
 struct UQ6_K {
-    struct Raw { u32x4 a, b, h; u32x2 s; uint32_t d; };
+    struct Raw {
+        uint32_t a[6], b[6]; // ql dwords from 4 - sh bytes before the field
+        uint32_t h[5];       // qh dwords from sh bytes before the field
+        int s[4];            // the unit's four scales
+        uint32_t d, sh;
+    };
     struct X { float v[4][16]; };
     static __device__ __forceinline__ void load_lds(Raw &r, const uint8_t *row, int u, int) {
         const uint8_t *o = row + 210 * (u >> 2);
         const int h = (u >> 1) & 1, lq = u & 1;
-        r.a = lds16u(o + 64 * h + 16 * lq);
-        r.b = lds16u(o + 64 * h + 32 + 16 * lq);
-        r.h = lds16u(o + 128 + 32 * h + 16 * lq);
-        r.s = lds8u(o + 192 + 8 * h);
+        const uint32_t sh = (uint32_t)(uintptr_t)o & 2u;
+        r.sh = sh;
+        const uint32_t *dl = (const uint32_t *)(o + sh - 4);
+        const uint32_t *dh = (const uint32_t *)(o - sh);
+        const int fa = 16 * h + 4 * lq, fh = 32 + 8 * h + 4 * lq;
+#pragma unroll
+        for (int i = 0; i < 6; i++) {
+            r.a[i] = dl[fa + i];
+            r.b[i] = dl[fa + 8 + i];
+        }
+#pragma unroll
+        for (int i = 0; i < 5; i++) r.h[i] = dh[fh + i];
+#pragma unroll
+        for (int i = 0; i < 4; i++) r.s[i] = *(const int8_t *)(o + 192 + 8 * h + 2 * i + lq);
         r.d = lds2(o + 208);
     }
     // piece i = 4g + i4 holds weights 128h + 32g + 16lq + 4i4 .. +3
@@ -461,54 +485,52 @@ struct UQ6_K {
     }
     static __device__ __forceinline__ void finish_x(X &) {}
     static __device__ __forceinline__ void finish_t(X &) {}
-    static __device__ __forceinline__ void axpy(const Raw &r, float dy, X &a, int u) {
-        const uint32_t A[4] = {r.a.x, r.a.y, r.a.z, r.a.w};
-        const uint32_t B[4] = {r.b.x, r.b.y, r.b.z, r.b.w};
-        const uint32_t H[4] = {r.h.x, r.h.y, r.h.z, r.h.w};
-        const int lq8 = 8 * (u & 1);
-        const float d = (f16lo(r.d) * 0.25f) * dy;
-        const float s0 = d * (float)(int)__builtin_amdgcn_sbfe((int)r.s.x, lq8, 8);
-        const float s1 = d * (float)(int)__builtin_amdgcn_sbfe((int)r.s.x, lq8 + 16, 8);
-        const float s2 = d * (float)(int)__builtin_amdgcn_sbfe((int)r.s.y, lq8, 8);
-        const float s3 = d * (float)(int)__builtin_amdgcn_sbfe((int)r.s.y, lq8 + 16, 8);
+    // q[g][j]: bytes of 4*(q-32) for quarter g, weights 16lq + 4j .. +3
+    static __device__ __forceinline__ void codes(const Raw &r, uint32_t (&q)[4][4]) {
+        const uint32_t fl = 30u - 8u * r.sh;
+        uint32_t a2[5], b2[5]; // ql dword j << 2 (bits 0..1 of each byte: don't care)
+#pragma unroll
+        for (int j = 0; j < 5; j++) {
+            a2[j] = __builtin_amdgcn_alignbit(r.a[j + 1], r.a[j], fl);
+            b2[j] = __builtin_amdgcn_alignbit(r.b[j + 1], r.b[j], fl);
+        }
 #pragma unroll
         for (int j = 0; j < 4; j++) {
-            const uint32_t h = H[j] ^ 0xaaaaaaaau;
-            saxpy4(opaque(((A[j] << 2) & 0x3c3c3c3cu) | ((h << 6) & 0xc0c0c0c0u)), s0, &a.v[0][4 * j]);
-            saxpy4(opaque(((B[j] << 2) & 0x3c3c3c3cu) | ((h << 4) & 0xc0c0c0c0u)), s1, &a.v[1][4 * j]);
-            saxpy4(opaque(((A[j] >> 2) & 0x3c3c3c3cu) | ((h << 2) & 0xc0c0c0c0u)), s2, &a.v[2][4 * j]);
-            saxpy4(opaque(((B[j] >> 2) & 0x3c3c3c3cu) | (h & 0xc0c0c0c0u)), s3, &a.v[3][4 * j]);
+            // top bit of every 2-bit field flipped
+            const uint32_t hx = __builtin_amdgcn_alignbyte(r.h[j + 1], r.h[j], r.sh) ^ 0xaaaaaaaau;
+            const uint32_t ar = __builtin_amdgcn_alignbit(a2[j + 1], a2[j], 4); // dword j >> 2
+            const uint32_t br = __builtin_amdgcn_alignbit(b2[j + 1], b2[j], 4);
+            q[0][j] = opaque((a2[j] & 0x3c3c3c3cu) | ((hx << 6) & 0xc0c0c0c0u));
+            q[1][j] = opaque((b2[j] & 0x3c3c3c3cu) | ((hx << 4) & 0xc0c0c0c0u));
+            q[2][j] = opaque((ar & 0x3c3c3c3cu) | ((hx << 2) & 0xc0c0c0c0u));
+            q[3][j] = opaque((br & 0x3c3c3c3cu) | (hx & 0xc0c0c0c0u));
         }
     }
-    static __device__ __forceinline__ float dot(const Raw &r, const X &x, int u) {
-        const uint32_t A[4] = {r.a.x, r.a.y, r.a.z, r.a.w};
-        const uint32_t B[4] = {r.b.x, r.b.y, r.b.z, r.b.w};
-        const uint32_t H[4] = {r.h.x, r.h.y, r.h.z, r.h.w};
+    static __device__ __forceinline__ void axpy(const Raw &r, float dy, X &a, int) {
+        uint32_t q[4][4];
+        codes(r, q);
+        const float d = (f16lo(r.d) * 0.25f) * dy;
+        float s[4];
+#pragma unroll
+        for (int g = 0; g < 4; g++) s[g] = d * (float)r.s[g];
+#pragma unroll
+        for (int j = 0; j < 4; j++)
+#pragma unroll
+            for (int g = 0; g < 4; g++) saxpy4(q[g][j], s[g], &a.v[g][4 * j]);
+    }
+    static __device__ __forceinline__ float dot(const Raw &r, const X &x, int) {
+        uint32_t q[4][4];
+        codes(r, q);
         float acc[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int j = 0; j < 4; j++) {
-            const uint32_t h = H[j] ^ 0xaaaaaaaau; // top bit of every 2-bit field flipped
-            // bytes of 4*(q-32) for quarters g = 0..3
-            const uint32_t q0 = opaque(((A[j] << 2) & 0x3c3c3c3cu) | ((h << 6) & 0xc0c0c0c0u));
-            const uint32_t q1 = opaque(((B[j] << 2) & 0x3c3c3c3cu) | ((h << 4) & 0xc0c0c0c0u));
-            const uint32_t q2 = opaque(((A[j] >> 2) & 0x3c3c3c3cu) | ((h << 2) & 0xc0c0c0c0u));
-            const uint32_t q3 = opaque(((B[j] >> 2) & 0x3c3c3c3cu) | (h & 0xc0c0c0c0u));
-            acc[0] = sdot4(q0, &x.v[0][4 * j], acc[0]);
-            acc[1] = sdot4(q1, &x.v[1][4 * j], acc[1]);
-            acc[2] = sdot4(q2, &x.v[2][4 * j], acc[2]);
-            acc[3] = sdot4(q3, &x.v[3][4 * j], acc[3]);
-        }
-        const int lq8 = 8 * (u & 1);
+        for (int j = 0; j < 4; j++)
+#pragma unroll
+            for (int g = 0; g < 4; g++) acc[g] = sdot4(q[g][j], &x.v[g][4 * j], acc[g]);
         const float d = f16lo(r.d) * 0.25f;
-        // the scale bytes are signed: extract with sign extension, convert as int
-        const float s0 = (float)(int)__builtin_amdgcn_sbfe((int)r.s.x, lq8, 8);
-        const float s1 = (float)(int)__builtin_amdgcn_sbfe((int)r.s.x, lq8 + 16, 8);
-        const float s2 = (float)(int)__builtin_amdgcn_sbfe((int)r.s.y, lq8, 8);
-        const float s3 = (float)(int)__builtin_amdgcn_sbfe((int)r.s.y, lq8 + 16, 8);
-        float r0 = (d * s0) * acc[0];
-        r0 = fmaf(d * s1, acc[1], r0);
-        r0 = fmaf(d * s2, acc[2], r0);
-        return fmaf(d * s3, acc[3], r0);
+        float r0 = (d * (float)r.s[0]) * acc[0];
+        r0 = fmaf(d * (float)r.s[1], acc[1], r0);
+        r0 = fmaf(d * (float)r.s[2], acc[2], r0);
+        return fmaf(d * (float)r.s[3], acc[3], r0);
     }
 };
 
