@@ -631,7 +631,9 @@ static hipError_t launch_k(K kernel, const GemvPlan &p, const uint8_t *W, const 
         hipFuncSetAttribute((const void *)kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
                             (int)p.lds_bytes) != hipSuccess)
         return hipGetLastError();
-    const int64_t cap = (int64_t)p.num_cu * resident_per_cu(kernel, p.T, p.lds_bytes);
+    int res = resident_per_cu(kernel, p.T, p.lds_bytes);
+    if (p.staged && res > STAGED_PER_CU) res = STAGED_PER_CU;
+    const int64_t cap = (int64_t)p.num_cu * res;
     const int grid = (int)(p.grid < cap ? p.grid : cap);
     hipLaunchKernelGGL(kernel, dim3(grid), dim3(p.T), p.lds_bytes, s, W, x, y, k, n, row_bytes,
                        j0, j1, acc, p.U, p.L, p.P, p.G, p.buf_bytes);
@@ -776,6 +778,7 @@ static hipError_t launch_moe_k(K kernel, const GemvPlan &p, const uint8_t *W, co
         hipFuncSetAttribute((const void *)kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
                             (int)p.lds_bytes) != hipSuccess)
         return hipGetLastError();
+    // (every resident workgroup: the pairs' short row ranges are latency-bound)
     const int64_t cap = (int64_t)p.num_cu * resident_per_cu(kernel, p.T, p.lds_bytes);
     int64_t per = cap / a.pairs;
     if (per > p.grid) per = p.grid;

@@ -258,7 +258,9 @@ hipError_t launch_t_k(const GemvTPlan &p, const uint8_t *W, const float *dy, flo
         hipFuncSetAttribute((const void *)kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
                             (int)p.lds_bytes) != hipSuccess)
         return hipGetLastError();
-    const int64_t cap = (int64_t)p.num_cu * resident_per_cu(kernel, p.T, p.lds_bytes);
+    int res = resident_per_cu(kernel, p.T, p.lds_bytes);
+    if (res > STAGED_PER_CU) res = STAGED_PER_CU;
+    const int64_t cap = (int64_t)p.num_cu * res;
     const int grid = (int)(p.grid < cap ? p.grid : cap);
     void *buf = nullptr;
     hipError_t e = hipMallocAsync(&buf, (size_t)grid * k * sizeof(float), s);

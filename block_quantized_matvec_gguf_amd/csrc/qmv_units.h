@@ -710,6 +710,14 @@ struct Lanes {
     }
 };
 
+// Workgroups per compute unit that the LDS-staged streaming kernels are
+// launched with: at most two, even where three would stay resident. On the
+// Q6_K vocabulary product two per compute unit stream the weights about 12%
+// faster than three (measured mean residency with three was about 7 waves
+// per compute unit, and grids between two and three per compute unit leave
+// the compute units unevenly loaded).
+constexpr int STAGED_PER_CU = 2;
+
 // Buffer descriptor over [p, p + bytes) (raw buffer loads check the range).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t batch_rsrc(const uint8_t *p, int bytes) {
     return __builtin_amdgcn_make_buffer_rsrc((void *)p, (short)0, bytes, 0x00020000);
