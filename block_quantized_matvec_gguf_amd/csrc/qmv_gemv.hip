@@ -632,7 +632,7 @@ static hipError_t launch_k(K kernel, const GemvPlan &p, const uint8_t *W, const 
                             (int)p.lds_bytes) != hipSuccess)
         return hipGetLastError();
     int res = resident_per_cu(kernel, p.T, p.lds_bytes);
-    if (p.staged && res > STAGED_PER_CU) res = STAGED_PER_CU;
+    if (res > STREAM_PER_CU) res = STREAM_PER_CU;
     const int64_t cap = (int64_t)p.num_cu * res;
     const int grid = (int)(p.grid < cap ? p.grid : cap);
     hipLaunchKernelGGL(kernel, dim3(grid), dim3(p.T), p.lds_bytes, s, W, x, y, k, n, row_bytes,
@@ -728,7 +728,9 @@ static hipError_t launch_affine_k(const GemvPlan &p, const uint8_t *q, const Aff
         hipFuncSetAttribute((const void *)kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
                             (int)p.lds_bytes) != hipSuccess)
         return hipGetLastError();
-    const int64_t cap = (int64_t)p.num_cu * resident_per_cu(kernel, p.T, p.lds_bytes);
+    int res = resident_per_cu(kernel, p.T, p.lds_bytes);
+    if (res > STREAM_PER_CU) res = STREAM_PER_CU;
+    const int64_t cap = (int64_t)p.num_cu * res;
     const int grid = (int)(p.grid < cap ? p.grid : cap);
     hipLaunchKernelGGL(kernel, dim3(grid), dim3(p.T), p.lds_bytes, s, q, a.scales, a.biases, x, y,
                        k, n, j0, j1, acc, p.U, p.L, p.P, p.G);

@@ -259,7 +259,7 @@ hipError_t launch_t_k(const GemvTPlan &p, const uint8_t *W, const float *dy, flo
                             (int)p.lds_bytes) != hipSuccess)
         return hipGetLastError();
     int res = resident_per_cu(kernel, p.T, p.lds_bytes);
-    if (res > STAGED_PER_CU) res = STAGED_PER_CU;
+    if (res > STREAM_PER_CU) res = STREAM_PER_CU;
     const int64_t cap = (int64_t)p.num_cu * res;
     const int grid = (int)(p.grid < cap ? p.grid : cap);
     void *buf = nullptr;

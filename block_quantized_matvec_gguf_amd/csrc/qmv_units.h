@@ -710,13 +710,15 @@ struct Lanes {
     }
 };
 
-// Workgroups per compute unit that the LDS-staged streaming kernels are
-// launched with: at most two, even where three would stay resident. On the
-// Q6_K vocabulary product two per compute unit stream the weights about 12%
-// faster than three (measured mean residency with three was about 7 waves
-// per compute unit, and grids between two and three per compute unit leave
-// the compute units unevenly loaded).
-constexpr int STAGED_PER_CU = 2;
+// Workgroups per compute unit that the streaming GEMV kernels (staged,
+// direct, transposed) are launched with: at most two, even where three would
+// stay resident. On the Q6_K vocabulary product two per compute unit stream
+// the weights about 12% faster than three (measured mean residency with
+// three was about 7 waves per compute unit, and grids between two and three
+// per compute unit leave the compute units unevenly loaded); the k=2560 x
+// 10240 products gain as well. The expert-indexed launches keep every
+// resident workgroup.
+constexpr int STREAM_PER_CU = 2;
 
 // Buffer descriptor over [p, p + bytes) (raw buffer loads check the range).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t batch_rsrc(const uint8_t *p, int bytes) {
