@@ -21,9 +21,9 @@ namespace qmv {
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
-// LDS reads at 2-byte alignment (block fields): single ds_read_b128/b64.
+// LDS reads of 16-byte fields (Q4_K super-blocks and 16-bit rows, which sit
+// on 16-byte boundaries of the staged rows): a single ds_read_b128.
 typedef uint32_t u32x4h __attribute__((ext_vector_type(4), aligned(2)));
-typedef uint32_t u32x2h __attribute__((ext_vector_type(2), aligned(2)));
 
 __device__ __forceinline__ u32x4 ld16(const uint8_t *p) {
     return __builtin_nontemporal_load((const u32x4 *)p);
@@ -32,30 +32,7 @@ __device__ __forceinline__ u32x4 lds16(const uint8_t *p) {
     const u32x4h v = *(const u32x4h *)p;
     return u32x4{v.x, v.y, v.z, v.w};
 }
-__device__ __forceinline__ u32x2 lds8(const uint8_t *p) {
-    const u32x2h v = *(const u32x2h *)p;
-    return u32x2{v.x, v.y};
-}
 __device__ __forceinline__ uint32_t lds2(const uint8_t *p) { return *(const uint16_t *)p; }
-// LDS serves 16- and 8-byte reads that are not naturally aligned, but only
-// with a large stall, so fields of the 2-byte aligned block formats are read
-// as the dwords covering them (ds_read2_b32) and shifted into place with
-// v_alignbyte_b32. The dword after a field is read even when the field is
-// dword aligned; it lies inside the LDS allocation and is then not used.
-__device__ __forceinline__ u32x4 lds16u(const uint8_t *p) {
-    const uint32_t sh = (uint32_t)(uintptr_t)p & 3u;
-    const uint32_t *d = (const uint32_t *)(p - sh);
-    const uint32_t w0 = d[0], w1 = d[1], w2 = d[2], w3 = d[3], w4 = d[4];
-    return u32x4{__builtin_amdgcn_alignbyte(w1, w0, sh), __builtin_amdgcn_alignbyte(w2, w1, sh),
-                 __builtin_amdgcn_alignbyte(w3, w2, sh), __builtin_amdgcn_alignbyte(w4, w3, sh)};
-}
-__device__ __forceinline__ u32x2 lds8u(const uint8_t *p) {
-    const uint32_t sh = (uint32_t)(uintptr_t)p & 3u;
-    const uint32_t *d = (const uint32_t *)(p - sh);
-    const uint32_t w0 = d[0], w1 = d[1], w2 = d[2];
-    return u32x2{__builtin_amdgcn_alignbyte(w1, w0, sh), __builtin_amdgcn_alignbyte(w2, w1, sh)};
-}
-
 // Keeps the compiler from folding a byte mask into per-element bit-field
 // extracts, so that the byte conversions select v_cvt_f32_{ubyte,i32 sdwa}.
 __device__ __forceinline__ uint32_t opaque(uint32_t v) {
