@@ -254,6 +254,31 @@ def test_misaligned_pointers_rejected():
     torch.cuda.synchronize()
 
 
+@pytest.mark.parametrize("fmt", [Q4_0, Q4_K, Q6_K, Q8_0, Q5_0], ids=lambda f: synth.FORMAT_NAMES[f])
+def test_x_only_4_byte_aligned(fmt):
+    """x 4 bytes past a 16-byte boundary: the staged kernels then read x from
+    global memory (no copy of x in LDS), and the weight buffers start behind
+    the 16-byte pad that the Q6_K field reads may touch. Same bits as with x
+    aligned, and within tolerance of the oracle, over a row range whose
+    batches start at every offset."""
+    k, n, m = 2560, 3000, 1
+    W, x = gen(fmt, k, n, m, 21)
+    print("case fmt=%s k=%d n=%d x offset 4 bytes" % (synth.FORMAT_NAMES[fmt], k, n), flush=True)
+    Wd = dev(W)
+    buf = torch.zeros(k + 4, dtype=torch.float32, device="cuda")
+    buf[1:k + 1] = torch.from_numpy(x[0]).cuda()
+    xd_off = buf[1:k + 1]
+    assert xd_off.data_ptr() % 16 == 4
+    base = np.full((m, n), SENTINEL, np.float32)
+    j0, j1 = 3, n - 5
+    y_off = run_gpu(fmt, W, x, k, n, base, "gemv", j0, j1, Wd=Wd, xd=xd_off)
+    y_al = run_gpu(fmt, W, x, k, n, base, "gemv", j0, j1, Wd=Wd)
+    assert np.array_equal(y_off.view(np.uint32), y_al.view(np.uint32))
+    sel = np.arange(j0, j1)
+    yref, sref = oracle.gemv_rows(fmt, W, x, k, n, sel)
+    assert oracle.check_parity(y_off[:, sel], yref, sref)["ok"]
+
+
 def test_run_to_run_determinism():
     k, n = 2560, 4096
     W, x = gen(Q6_K, k, n, 1, 9)
