@@ -195,6 +195,7 @@ __device__ __forceinline__ void reduce_batch(float (&part)[RB][MT], const Lanes<
     for (int r = 0; r < RB; r++)
 #pragma unroll
         for (int t = 0; t < MT; t++) part[r][t] = group_sum(part[r][t], G);
+    if (ln.slot >= P) return; // lanes past the last row slot (workgroup padding)
     if (ln.NG == 1) {
         if (ln.lane == 0) {
 #pragma unroll
@@ -257,7 +258,7 @@ __device__ __forceinline__ void direct_body(const uint8_t *__restrict__ W,
 #pragma unroll
         for (int r = 0; r < RB; r++) {
             const int64_t jr = b + (int64_t)r * P;
-            const bool in = jr + ln.slot < j_end;
+            const bool in = ln.slot < P && jr + ln.slot < j_end;
             const uint8_t *row = in ? Wslot + jr * row_bytes : last_row;
             const int64_t j = in ? jr + ln.slot : j_end - 1; // the row index (per-row fields)
 #pragma unroll
@@ -279,7 +280,7 @@ __device__ __forceinline__ void direct_body(const uint8_t *__restrict__ W,
         float part[RB][MT];
 #pragma unroll
         for (int r = 0; r < RB; r++) {
-            const bool live = base + (int64_t)r * P + ln.slot < j_end;
+            const bool live = ln.slot < P && base + (int64_t)r * P + ln.slot < j_end;
 #pragma unroll
             for (int t = 0; t < MT; t++) {
                 float v = 0.f;
@@ -400,7 +401,7 @@ __device__ __forceinline__ void staged_body(const uint8_t *__restrict__ W,
 #pragma unroll
         for (int r = 0; r < RB; r++) {
             const int rr = r * P + ln.slot;
-            const bool live = base + rr < j_end;
+            const bool live = ln.slot < P && base + rr < j_end;
             const uint8_t *row = bl + (live ? rr : 0) * rbytes;
 #pragma unroll
             for (int t = 0; t < MT; t++) part[r][t] = 0.f;
@@ -551,6 +552,25 @@ bool plan_gemv(int fmt, int64_t k, int64_t rows, int mt_max, int num_cu, GemvPla
     // workgroups share the rows
     while (g.P > 1 && g.P * g.L > 64 && (rows + g.P - 1) / g.P < num_cu) g.P /= 2;
     g.T = g.P * g.L;
+    g.per_cu = STREAM_PER_CU;
+    // The waves of a workgroup are dealt to the compute unit's four SIMDs in
+    // turn, so a workgroup of 4w+1 waves puts two waves of every workgroup on
+    // one SIMD, which then carries twice the decode work of the others. Where
+    // the row slots do not fill whole groups of four waves (e.g. 40 lanes per
+    // row: 8 slots = 5 waves) and the rows make at least 4 batches for each
+    // of 4 workgroups per compute unit, the workgroup is padded to 256
+    // threads with idle lanes past the last slot, if that idles at most 1/8
+    // of them. (Measured: Q6_K k=2560 x 262144 120 -> 113 us; the k=2560 x
+    // 10240 products, a few batches per workgroup, run 1-9% slower padded.)
+    if (g.T % 256 != 0 && g.T > 64 && g.L <= 256) {
+        const int P4 = 256 / g.L;
+        if (P4 >= 1 && (256 - P4 * g.L) * 8 <= 256 &&
+            (rows + P4 - 1) / P4 >= 16 * (int64_t)num_cu) {
+            g.P = P4;
+            g.T = 256;
+            g.per_cu = STREAM_PER_CU_4W;
+        }
+    }
     g.MT = (g.UPL == 1 && mt_max >= 2) ? 2 : 1;
     int64_t rb;
     switch (fmt) {
@@ -632,7 +652,7 @@ static hipError_t launch_k(K kernel, const GemvPlan &p, const uint8_t *W, const 
                             (int)p.lds_bytes) != hipSuccess)
         return hipGetLastError();
     int res = resident_per_cu(kernel, p.T, p.lds_bytes);
-    if (res > STREAM_PER_CU) res = STREAM_PER_CU;
+    if (res > p.per_cu) res = p.per_cu;
     const int64_t cap = (int64_t)p.num_cu * res;
     const int grid = (int)(p.grid < cap ? p.grid : cap);
     hipLaunchKernelGGL(kernel, dim3(grid), dim3(p.T), p.lds_bytes, s, W, x, y, k, n, row_bytes,
@@ -729,7 +749,7 @@ static hipError_t launch_affine_k(const GemvPlan &p, const uint8_t *q, const Aff
                             (int)p.lds_bytes) != hipSuccess)
         return hipGetLastError();
     int res = resident_per_cu(kernel, p.T, p.lds_bytes);
-    if (res > STREAM_PER_CU) res = STREAM_PER_CU;
+    if (res > p.per_cu) res = p.per_cu;
     const int64_t cap = (int64_t)p.num_cu * res;
     const int grid = (int)(p.grid < cap ? p.grid : cap);
     hipLaunchKernelGGL(kernel, dim3(grid), dim3(p.T), p.lds_bytes, s, q, a.scales, a.biases, x, y,

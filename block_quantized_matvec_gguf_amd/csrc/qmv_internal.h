@@ -38,6 +38,7 @@ struct GemvPlan {
     int staged;   // weights go through LDS (block formats)
     int buf_bytes; // bytes of one LDS weight buffer (staged kernel)
     int npt;      // 16-byte weight pieces per thread per batch (staged kernel)
+    int per_cu;   // workgroups per compute unit the launch is capped at
     size_t lds_bytes;
 };
 

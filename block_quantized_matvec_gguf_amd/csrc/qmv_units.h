@@ -688,14 +688,17 @@ struct Lanes {
 };
 
 // Workgroups per compute unit that the streaming GEMV kernels (staged,
-// direct, transposed) are launched with: at most two, even where three would
-// stay resident. On the Q6_K vocabulary product two per compute unit stream
-// the weights about 12% faster than three (measured mean residency with
-// three was about 7 waves per compute unit, and grids between two and three
-// per compute unit leave the compute units unevenly loaded); the k=2560 x
-// 10240 products gain as well. The expert-indexed launches keep every
-// resident workgroup.
+// direct, affine, transposed) are launched with. A workgroup's waves are dealt
+// to the four SIMDs of a compute unit in turn, starting at the first SIMD, so
+// workgroups of 4w+1 waves (e.g. 320 threads) pile two waves of every
+// workgroup onto one SIMD: a third such workgroup rarely finds room (measured
+// mean residency about 7 waves per compute unit) and two per compute unit
+// stream best. Launches whose workgroups were padded to 256 threads (4 waves,
+// spread evenly) take four per compute unit, 4 waves per SIMD: on the Q6_K
+// vocabulary product 128 us with two, 118 us with three, 114 us with four.
+// The expert-indexed launches keep every resident workgroup.
 constexpr int STREAM_PER_CU = 2;
+constexpr int STREAM_PER_CU_4W = 4;
 
 // Buffer descriptor over [p, p + bytes) (raw buffer loads check the range).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t batch_rsrc(const uint8_t *p, int bytes) {

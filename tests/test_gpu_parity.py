@@ -289,6 +289,34 @@ def test_run_to_run_determinism():
     assert np.array_equal(y1.view(np.uint32), y2.view(np.uint32))
 
 
+@pytest.mark.parametrize("fmt", ALL_FORMATS, ids=lambda f: synth.FORMAT_NAMES[f])
+def test_padded_workgroups(fmt):
+    """k=2560 (40 lanes per row) with enough rows that the streaming kernels
+    pad their workgroups to 256 threads (6 row slots + 16 idle lanes; 4096+
+    batches): sampled rows against the oracle, every bit equal to row tiles of
+    2048 (unpadded launches), and accumulate over the full range equal to
+    base + untiled."""
+    k, n, m = 2560, 6 * 4096 + 5, 1
+    W, x = gen(fmt, k, n, m, 70 + fmt)
+    Wd, xd = dev(W), dev(x)
+    print("padded fmt=%s k=%d n=%d" % (synth.FORMAT_NAMES[fmt], k, n), flush=True)
+    y_un = run_gpu(fmt, W, x, k, n, np.full((m, n), SENTINEL, np.float32), Wd=Wd, xd=xd)
+    rng = np.random.default_rng(71)
+    rows = np.unique(np.concatenate([np.arange(40), np.arange(n - 40, n),
+                                     rng.integers(0, n, 1024)]))
+    yref, sref = oracle.gemv_rows(fmt, W, x, k, n, rows)
+    res = oracle.check_parity(y_un[:, rows], yref, sref)
+    assert res["ok"], res
+    yd = dev(np.full((m, n), SENTINEL, np.float32))
+    for j0 in range(0, n, 2048):
+        qb.matvec(fmt, Wd, xd, k, n, y=yd, j_start=j0, j_end=min(n, j0 + 2048))
+    torch.cuda.synchronize()
+    assert np.array_equal(yd.cpu().numpy().view(np.uint32), y_un.view(np.uint32))
+    base = np.random.default_rng(72).uniform(-1, 1, size=(m, n)).astype(np.float32)
+    y_acc = run_gpu(fmt, W, x, k, n, base, accumulate=True, Wd=Wd, xd=xd)
+    assert np.array_equal(y_acc.view(np.uint32), (base + y_un).view(np.uint32))
+
+
 # ------------------------------------------------------- measured workloads
 
 @pytest.mark.parametrize("name", ["bf16_ffn_up", "f16_ffn_up", "q4_k_ffn_up", "q8_0_ffn_up",
