@@ -39,6 +39,14 @@ __device__ __forceinline__ uint32_t opaque(uint32_t v) {
     asm("" : "+v"(v));
     return v;
 }
+// (m & a) | (~m & b) as one v_bfi_b32. Written out, the compiler uses the
+// known-zero bits of b to re-mask it in separate instructions; the asm
+// (a plain VALU operation, no memory access) keeps it to one.
+__device__ __forceinline__ uint32_t bfi(uint32_t m, uint32_t a, uint32_t b) {
+    uint32_t r;
+    asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(r) : "s"(m), "v"(a), "v"(b));
+    return r;
+}
 __device__ __forceinline__ float ub0(uint32_t v) { return (float)(v & 0xffu); }
 __device__ __forceinline__ float ub1(uint32_t v) { return (float)((v >> 8) & 0xffu); }
 __device__ __forceinline__ float ub2(uint32_t v) { return (float)((v >> 16) & 0xffu); }
@@ -462,9 +470,16 @@ struct UQ6_K {
     }
     static __device__ __forceinline__ void finish_x(X &) {}
     static __device__ __forceinline__ void finish_t(X &) {}
-    // q[g][j]: bytes of 4*(q-32) for quarter g, weights 16lq + 4j .. +3
+    // q[g][j]: bytes of 4*(q-32) for quarter g, weights 16lq + 4j .. +3.
+    // Each byte is assembled as (nibble << 2) | ((high 2 bits ^ 2) << 6): the
+    // nibble from a funnel-shifted ql dword (bits 2..5 of every byte), the
+    // two high bits from the qh dword with the top bit of every 2-bit field
+    // flipped, fields 0/2 and 1/3 masked apart so that each of the four
+    // shifted copies below has zeros in bits 0..1 of every byte; one bit-field
+    // insert (bits 2..5 from the nibble side) then yields the code byte.
     static __device__ __forceinline__ void codes(const Raw &r, uint32_t (&q)[4][4]) {
         const uint32_t fl = 30u - 8u * r.sh;
+        constexpr uint32_t NIB = 0x3c3c3c3cu;
         uint32_t a2[5], b2[5]; // ql dword j << 2 (bits 0..1 of each byte: don't care)
 #pragma unroll
         for (int j = 0; j < 5; j++) {
@@ -473,14 +488,15 @@ struct UQ6_K {
         }
 #pragma unroll
         for (int j = 0; j < 4; j++) {
-            // top bit of every 2-bit field flipped
-            const uint32_t hx = __builtin_amdgcn_alignbyte(r.h[j + 1], r.h[j], r.sh) ^ 0xaaaaaaaau;
+            const uint32_t h = __builtin_amdgcn_alignbyte(r.h[j + 1], r.h[j], r.sh);
+            const uint32_t hA = (h ^ 0xaaaaaaaau) & 0x33333333u; // fields 0 and 2
+            const uint32_t hB = (h ^ 0xaaaaaaaau) & 0xccccccccu; // fields 1 and 3
             const uint32_t ar = __builtin_amdgcn_alignbit(a2[j + 1], a2[j], 4); // dword j >> 2
             const uint32_t br = __builtin_amdgcn_alignbit(b2[j + 1], b2[j], 4);
-            q[0][j] = opaque((a2[j] & 0x3c3c3c3cu) | ((hx << 6) & 0xc0c0c0c0u));
-            q[1][j] = opaque((b2[j] & 0x3c3c3c3cu) | ((hx << 4) & 0xc0c0c0c0u));
-            q[2][j] = opaque((ar & 0x3c3c3c3cu) | ((hx << 2) & 0xc0c0c0c0u));
-            q[3][j] = opaque((br & 0x3c3c3c3cu) | (hx & 0xc0c0c0c0u));
+            q[0][j] = bfi(NIB, a2[j], hA << 6);
+            q[1][j] = bfi(NIB, b2[j], hB << 4);
+            q[2][j] = bfi(NIB, ar, hA << 2);
+            q[3][j] = bfi(NIB, br, hB);
         }
     }
     static __device__ __forceinline__ void axpy(const Raw &r, float dy, X &a, int) {
@@ -503,11 +519,11 @@ struct UQ6_K {
         for (int j = 0; j < 4; j++)
 #pragma unroll
             for (int g = 0; g < 4; g++) acc[g] = sdot4(q[g][j], &x.v[g][4 * j], acc[g]);
-        const float d = f16lo(r.d) * 0.25f;
-        float r0 = (d * (float)r.s[0]) * acc[0];
-        r0 = fmaf(d * (float)r.s[1], acc[1], r0);
-        r0 = fmaf(d * (float)r.s[2], acc[2], r0);
-        return fmaf(d * (float)r.s[3], acc[3], r0);
+        float r0 = (float)r.s[0] * acc[0];
+        r0 = fmaf((float)r.s[1], acc[1], r0);
+        r0 = fmaf((float)r.s[2], acc[2], r0);
+        r0 = fmaf((float)r.s[3], acc[3], r0);
+        return (f16lo(r.d) * 0.25f) * r0;
     }
 };
 
