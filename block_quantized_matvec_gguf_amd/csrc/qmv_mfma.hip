@@ -83,32 +83,33 @@ __device__ __forceinline__ uint32_t pk_f16(float a, float b) {
 
 // ------------------------------------------------------------ x staging
 
-// Workgroup (256 threads) per (16-token quarter of a 64-token tile,
-// super-block): grid (k/256, tiles, 4).
-__global__ __launch_bounds__(256) void qmv_mfma_prep_x(const float *__restrict__ x, int64_t k,
-                                                       int64_t m, uint8_t *__restrict__ xs,
-                                                       uint8_t *__restrict__ sm,
-                                                       float *__restrict__ ps) {
-    __shared__ int e_tok[16];
-    __shared__ float s_tok[16][8];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int s = blockIdx.x, T = blockIdx.y, qt = blockIdx.z; // tokens 16qt..16qt+15 of T
+// One wave per (4-token group of a 64-token tile, super-block): grid
+// (k/256, tiles, 16), 64 threads.
+__global__ __launch_bounds__(64) void qmv_mfma_prep_x(const float *__restrict__ x, int64_t k,
+                                                      int64_t m, uint8_t *__restrict__ xs,
+                                                      uint8_t *__restrict__ sm,
+                                                      float *__restrict__ ps) {
+    __shared__ int e_tok[4];
+    __shared__ float s_tok[4][8];
+    __shared__ f32x4 xv[4][64]; // the group's x slice, read once from memory
+    const int lane = threadIdx.x;
+    const int s = blockIdx.x, T = blockIdx.y, qg = blockIdx.z; // tokens 4qg..4qg+3 of T
     const int64_t nsb = k >> 8;
     const int64_t ts = (int64_t)T * nsb + s; // (tile, super-block) index
 
-    // Phase 1: per token, the exponent and the eight sub-block sums; wave w
-    // takes tokens 4w..4w+3 of the quarter, lane l elements 4l..4l+3.
+    // Phase 1: per token, the exponent and the eight sub-block sums; lane l
+    // takes elements 4l..4l+3 of each of the 4 tokens.
     float v[4][4];
 #pragma unroll
     for (int i = 0; i < 4; i++) {
-        const int64_t t = (int64_t)T * TM + 16 * qt + 4 * wave + i;
+        const int64_t t = (int64_t)T * TM + 4 * qg + i;
 #pragma unroll
         for (int j = 0; j < 4; j++)
             v[i][j] = t < m ? x[t * k + 256 * (int64_t)s + 4 * lane + j] : 0.f;
+        xv[i][lane] = f32x4{v[i][0], v[i][1], v[i][2], v[i][3]};
     }
 #pragma unroll
     for (int i = 0; i < 4; i++) {
-        const int tq = 4 * wave + i;
         float mx = fmaxf(fmaxf(fabsf(v[i][0]), fabsf(v[i][1])),
                          fmaxf(fabsf(v[i][2]), fabsf(v[i][3])));
         float sum = (v[i][0] + v[i][1]) + (v[i][2] + v[i][3]);
@@ -124,30 +125,26 @@ __global__ __launch_bounds__(256) void qmv_mfma_prep_x(const float *__restrict__
                 e -= 15;              // mx / 2^e in [2^14, 2^15)
                 e = e < -100 ? -100 : (e > 100 ? 100 : e);
             }
-            e_tok[tq] = e;
+            e_tok[i] = e;
         }
-        if ((lane & 7) == 0) s_tok[tq][lane >> 3] = sum;
+        if ((lane & 7) == 0) s_tok[i][lane >> 3] = sum;
     }
     __syncthreads();
 
-    // Phase 2: the operand pieces of the quarter's tokens: piece (g, tp, jh,
-    // lane-in-quarter) gives the hi and lo 16-byte pieces of that slot.
-    const int tb = qt >> 1;
+    // Phase 2: the operand pieces of the group's tokens: piece (g, tp, jh,
+    // token) gives the hi and lo 16-byte pieces of that slot. Token tt of the
+    // tile sits in MFMA row nl = tt % 32 of token half tb = tt / 32.
     uint8_t *xt = xs + ts * 64 * 1024;
 #pragma unroll
     for (int it = 0; it < 2; it++) {
-        const int pc = tid + 256 * it;
-        const int lq = pc & 15, jh = (pc >> 4) & 1, tp = (pc >> 5) & 1, g = pc >> 6;
-        const int tq = lq, nl = 16 * (qt & 1) + lq, ln = nl + 32 * jh;
-        const int64_t t = (int64_t)T * TM + 16 * qt + tq;
+        const int pc = lane + 64 * it;
+        const int lq = pc & 3, jh = (pc >> 2) & 1, tp = (pc >> 3) & 1, g = pc >> 4;
+        const int tt = 4 * qg + lq, tb = tt >> 5, ln = (tt & 31) + 32 * jh;
         float w[8];
-        if (t < m) {
-            const float *p = x + t * k + 256 * (int64_t)s + 32 * g + 16 * jh + 8 * tp;
+        {
+            const float *p = (const float *)&xv[lq][0] + 32 * g + 16 * jh + 8 * tp;
 #pragma unroll
-            for (int j = 0; j < 8; j++) w[j] = ldexpf(p[perm8(j)], -e_tok[tq]);
-        } else {
-#pragma unroll
-            for (int j = 0; j < 8; j++) w[j] = 0.f;
+            for (int j = 0; j < 8; j++) w[j] = ldexpf(p[perm8(j)], -e_tok[lq]);
         }
         uint32_t hi[4], lo[4];
 #pragma unroll
@@ -162,9 +159,9 @@ __global__ __launch_bounds__(256) void qmv_mfma_prep_x(const float *__restrict__
         *(u32x4 *)(xt + base + 1024) = u32x4{lo[0], lo[1], lo[2], lo[3]};
     }
     // Sums for the min term and the table of p.
-    if (tid < 32) {
-        const int lq = tid & 15, jh = tid >> 4;
-        const int nl = 16 * (qt & 1) + lq, ln = nl + 32 * jh;
+    if (lane < 8) {
+        const int lq = lane & 3, jh = lane >> 2;
+        const int tt = 4 * qg + lq, tb = tt >> 5, ln = (tt & 31) + 32 * jh;
         uint32_t o[4];
 #pragma unroll
         for (int j = 0; j < 4; j++) {
@@ -179,9 +176,9 @@ __global__ __launch_bounds__(256) void qmv_mfma_prep_x(const float *__restrict__
             o[j] = pk_f16(a2[0], a2[1]);
         }
         *(u32x4 *)(sm + (ts * 2 + tb) * 64 * 16 + (size_t)ln * 16) = u32x4{o[0], o[1], o[2], o[3]};
-    } else if (tid < 48) {
-        const int tq = tid - 32;
-        ps[ts * TM + 16 * qt + tq] = ldexpf(1.f, e_tok[tq]);
+    } else if (lane < 12) {
+        const int tq = lane - 8;
+        ps[ts * TM + 4 * qg + tq] = ldexpf(1.f, e_tok[tq]);
     }
 }
 
@@ -454,8 +451,8 @@ hipError_t launch_mfma(const MfmaPlan &p, const uint8_t *W, const float *x, floa
     if (e != hipSuccess) return e;
     uint8_t *xs = (uint8_t *)buf, *sm = xs + bx;
     float *ps = (float *)(sm + bs);
-    hipLaunchKernelGGL(qmv_mfma_prep_x, dim3((unsigned)nsb, p.tiles_m, 4), dim3(256), 0, stream, x,
-                       k, m, xs, sm, ps);
+    hipLaunchKernelGGL(qmv_mfma_prep_x, dim3((unsigned)nsb, p.tiles_m, TM / 4), dim3(64), 0, stream,
+                       x, k, m, xs, sm, ps);
     e = hipGetLastError();
     if (e == hipSuccess) {
         hipLaunchKernelGGL(qmv_mfma_q4_k, dim3(p.tiles_n, p.tiles_m), dim3(NT), LDS_BYTES,
