@@ -29,7 +29,7 @@ struct GemvPlan {
     int G;        // lanes per shuffle-reduction group: power of two <= 16 dividing L
     int NG;       // reduction groups per row slot (L / G)
     int P;        // row slots per workgroup
-    int T;        // threads per workgroup (P * L)
+    int T;        // threads per workgroup (P * L, or 256 with idle lanes past P * L)
     int RB;       // rows per slot per batch
     int MT;       // tokens per launch (1 or 2)
     int grid;     // workgroups wanted (one per batch); the launch caps it at residency

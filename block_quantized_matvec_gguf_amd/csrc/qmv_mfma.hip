@@ -25,16 +25,17 @@
 //     dmin * sum_g m_g * sum(x over g) takes one more MFMA per super-block
 //     (A = the hi/lo sums, B = the 6-bit mins, exact), scaled by dmin*p.
 //
-// Mapping of the main kernel. A workgroup owns 64 tokens x 64 rows and has 4
-// waves; K is split over the waves (wave w takes super-blocks w, w+4, ...),
-// every wave holds the whole tile as four 32x32 accumulators (lane l feeds
-// A[l%32][8(l/32)+i] and B[8(l/32)+i][l%32] and receives
+// Mapping of the main kernel. A workgroup owns 64 tokens x 64 rows and has 8
+// waves: wave w takes token half th = w&1 and K quarter kq = w>>1 (super-blocks
+// kq, kq+4, ...) and holds its 32 tokens x 64 rows as two 32x32 accumulators
+// (lane l feeds A[l%32][8(l/32)+i] and B[8(l/32)+i][l%32] and receives
 // D[8(r/4)+4(l/32)+r%4][l%32] in register r). Tokens are the MFMA rows and
-// weight rows the columns, so a lane's block scales are scalars. Each wave
-// copies the weight bytes of its super-blocks into LDS (buffer_load ... lds,
-// one contiguous run per row) before its loop; the four partial tiles are
-// summed in LDS in wave order. Results depend only on k, never on the row
-// range or the token tiling.
+// weight rows the columns, so a lane's block scales are scalars. Each quarter
+// stages the weight bytes of its super-blocks in LDS (buffer_load ... lds, one
+// contiguous run per row), the next super-block's while one is decoded (two
+// slots per quarter, each copy split between the quarter's two waves); the
+// four quarters' partial tiles are summed in LDS in quarter order. Results
+// depend only on k, never on the row range or the token tiling.
 #include "qmv_internal.h"
 
 namespace qmv {
@@ -51,9 +52,8 @@ constexpr int TN = 64;      // weight rows per tile
 constexpr int KQ = 4;       // split of K over the waves of the main kernel
 constexpr int NT = 64 * 2 * KQ; // threads per workgroup: 2 token halves x KQ
 constexpr int SBB = 144;    // bytes of a Q4_K super-block
-constexpr int RSB = 4;      // super-blocks a quarter stages per round
 constexpr int PF = 3;       // sub-blocks of x operands loaded ahead
-constexpr int QUARTER_W = TN * SBB * RSB;                         // staged bytes per quarter
+constexpr int QUARTER_W = TN * SBB * 2; // a quarter's two staging slots (one super-block each)
 constexpr size_t RED_BYTES = (size_t)KQ * TM * TN * sizeof(float); // partial tiles
 constexpr size_t LDS_BYTES =
     (size_t)KQ * QUARTER_W > RED_BYTES ? (size_t)KQ * QUARTER_W : RED_BYTES;
@@ -273,28 +273,27 @@ __global__ __launch_bounds__(NT) void qmv_mfma_q4_k(const uint8_t *__restrict__ 
 #pragma unroll
         for (int r = 0; r < 16; r++) acc[b][r] = 0.f;
 
-    // super-blocks of this quarter; every wave runs the same number of rounds
+    // super-blocks of this quarter (nw); every wave runs nmax iterations. The
+    // quarter's next super-block is copied into its other slot while one is
+    // decoded; the two waves of the quarter split each copy.
     const int nw = kq < nsb ? (nsb - kq + KQ - 1) / KQ : 0;
-    const int rounds = ((nsb + KQ - 1) / KQ + RSB - 1) / RSB;
-    f16x8 ring[4][4]; // x operands of four sub-blocks: [sub-block & 3][2*tp + hl]
-    for (int rd = 0; rd < rounds; rd++) {
-        const int i0 = rd * RSB;
-        const int nr = nw - i0 < RSB ? (nw - i0 > 0 ? nw - i0 : 0) : RSB;
-        if (rd > 0) __syncthreads(); // the quarter's previous round is read
-        // the two waves of the quarter copy alternate super-blocks
-        for (int r = th; r < nr; r += 2) {
-            const int sboff = SBB * (kq + KQ * (i0 + r));
-#pragma unroll
-            for (int i = 0; i < 9; i++) {
-                uint8_t *slot = wl + r * (TN * SBB) + 1024 * i;
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                    rs, (__attribute__((address_space(3))) void *)slot, 16, poff[i] + sboff, 0,
-                    0, 2 /* nontemporal */);
-            }
+    const int nmax = (nsb + KQ - 1) / KQ;
+    auto copy_sb = [&](int i, int slot) {
+        const int sboff = SBB * (kq + KQ * i);
+        for (int c = th; c < 9; c += 2) {
+            uint8_t *dst = wl + slot * (TN * SBB) + 1024 * c;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rs, (__attribute__((address_space(3))) void *)dst, 16, poff[c] + sboff, 0, 0,
+                2 /* nontemporal */);
         }
-        __builtin_amdgcn_s_waitcnt(WAIT_VM0); // this wave's copies have landed
-        __syncthreads();                       // and the partner's
-        if (rd == 0 && nr > 0) {
+    };
+    if (nw > 0) copy_sb(0, 0);
+    f16x8 ring[4][4]; // x operands of four sub-blocks: [sub-block & 3][2*tp + hl]
+    for (int i = 0; i < nmax; i++) {
+        __builtin_amdgcn_s_waitcnt(WAIT_VM0); // this wave's part of super-block i has landed
+        __syncthreads(); // and the partner's; the other slot's super-block is read
+        if (i + 1 < nw) copy_sb(i + 1, (i + 1) & 1);
+        if (i == 0 && nw > 0) {
             // first PF sub-blocks of the wave's first super-block
             const uint8_t *xf0 = xs + ((int64_t)T * nsb + kq) * 64 * 1024 + lane * 16;
 #pragma unroll
@@ -304,14 +303,13 @@ __global__ __launch_bounds__(NT) void qmv_mfma_q4_k(const uint8_t *__restrict__ 
                     ring[g][f] = __builtin_bit_cast(
                         f16x8, ldc(xf0 + ((8 * g + 4 * (f >> 1) + 2 * th + (f & 1)) << 10)));
         }
-
-        for (int r = 0; r < nr; r++) {
-            const int s = kq + KQ * (i0 + r);
+        if (i < nw) {
+            const int s = kq + KQ * i;
             const int64_t ts = (int64_t)T * nsb + s;
             const uint8_t *xf = xs + ts * 64 * 1024 + lane * 16 + (2 * th << 10);
             const uint8_t *xfn =
-                i0 + r + 1 < nw ? xf + (int64_t)KQ * 64 * 1024 : xf; // next super-block
-            const uint8_t *wsb = wl + r * (TN * SBB);
+                i + 1 < nw ? xf + (int64_t)KQ * 64 * 1024 : xf; // next super-block
+            const uint8_t *wsb = wl + (i & 1) * (TN * SBB);
             const uint8_t *wrow[2] = {wsb + nl * SBB, wsb + (nl + 32) * SBB};
 
             // block scales of the lane's two rows
