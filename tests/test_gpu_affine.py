@@ -127,3 +127,21 @@ def test_affine_ffn_workload():
     spec = synth.WORKLOADS["affine4_ffn_up"]
     words, sc, bi, x = synth.affine_workload("affine4_ffn_up")
     check_a(4, spec["k"], spec["n"], spec["m"], arrays=(words, sc, bi, x))
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+def test_affine_padded_workgroups(bits):
+    """k=2560 with enough rows that the launch pads its workgroups to 256
+    threads (6 row slots + 16 idle lanes): every output against the oracle,
+    and every bit equal to row tiles of 2048 (unpadded launches)."""
+    k, n, m = 2560, 6 * 4096 + 5, 1
+    arrays = gen_a(bits, k, n, m, 31 + bits)
+    y_un = check_a(bits, k, n, m, arrays=arrays, seed=6)
+    words, sc, bi, x = arrays
+    Wd, Sd, Bd, xd = (dev(words.view(np.int32)), dev(sc.view(np.int16)),
+                      dev(bi.view(np.int16)), dev(x))
+    yd = dev(np.full((m, n), SENTINEL, np.float32))
+    for j0 in range(0, n, 2048):
+        qb.matvec_affine(bits, Wd, Sd, Bd, xd, k, n, y=yd, j_start=j0, j_end=min(n, j0 + 2048))
+    torch.cuda.synchronize()
+    assert np.array_equal(yd.cpu().numpy().view(np.uint32), y_un.view(np.uint32))
