@@ -149,3 +149,22 @@ def test_moe_decode_workload():
     f, W, x, spec = synth.workload("q4_k_moe_decode")
     ids = synth.moe_ids(spec)
     check_moe(f, W, ids, x, spec["k"], spec["n"], spec["experts"], spec["top_k"])
+
+
+@pytest.mark.parametrize("fmt", [Q6_K, BF16], ids=lambda f: synth.FORMAT_NAMES[f])
+def test_moe_padded_workgroups(fmt):
+    """Experts of k=2560 x 24581 rows: the launch pads its workgroups to 256
+    threads (6 row slots + 16 idle lanes). Against the oracle, and every row
+    bit-equal to qmv_run on that expert's matrix."""
+    k, n, E, n_pos, top_k = 2560, 6 * 4096 + 5, 2, 1, 2
+    rng = np.random.default_rng(300 + fmt)
+    W = synth.gen_weights(fmt, rng, n * E, k)
+    ids = [1, 0]
+    x = synth.gen_x(rng, n_pos, k)
+    y, _ = check_moe(fmt, W, ids, x, k, n, E, top_k)
+    slab = qb.qmv_weight_bytes(fmt, k, n)
+    for r, e in enumerate(ids):
+        yr = dev(np.zeros((1, n), np.float32))
+        qb.matvec(fmt, dev(W[e * slab:(e + 1) * slab]), dev(x[r // top_k]), k, n, y=yr)
+        torch.cuda.synchronize()
+        assert np.array_equal(yr.cpu().numpy()[0].view(np.uint32), y[r].view(np.uint32)), r
