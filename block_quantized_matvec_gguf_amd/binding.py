@@ -68,6 +68,8 @@ def load(path: str | None = None):
         lib.qmv_status_string.restype = ctypes.c_char_p
         lib.qmv_kernel_name.argtypes = [ci, i64, i64, ci]
         lib.qmv_kernel_name.restype = ctypes.c_char_p
+        lib.qmv_gemv_geometry.argtypes = [ci, i64, i64, i64, ci, ctypes.POINTER(i64)]
+        lib.qmv_gemv_geometry.restype = ci
         lib.qmv_run_t.argtypes = run_args
         lib.qmv_run_t.restype = ci
         lib.qmv_run_t_ex.argtypes = run_args + [ci]
@@ -172,6 +174,17 @@ def qmv_status_string(status: int) -> str:
 
 def qmv_kernel_name(format: int, k: int, m_tokens: int, algo: int = QMV_ALGO_AUTO) -> str:
     return load().qmv_kernel_name(format, k, m_tokens, algo).decode()
+
+
+GEOMETRY_FIELDS = ("threads", "slots", "lanes", "units_per_lane", "rows_per_slot", "tokens",
+                   "per_cu", "staged")
+
+
+def qmv_gemv_geometry(format: int, k: int, rows: int, m_tokens: int, num_cu: int):
+    """(status, dict of the streaming GEMV launch geometry or None)."""
+    out = (ctypes.c_int64 * 8)()
+    rc = load().qmv_gemv_geometry(format, k, rows, m_tokens, num_cu, out)
+    return rc, (dict(zip(GEOMETRY_FIELDS, list(out))) if rc == QMV_OK else None)
 
 
 # ------------------------------------------------------- torch convenience

@@ -192,6 +192,19 @@ const char *qmv_kernel_name(int format, int64_t k, int64_t m_tokens, int algo) {
     return name.c_str();
 }
 
+int qmv_gemv_geometry(int format, int64_t k, int64_t rows, int64_t m_tokens, int num_cu,
+                      int64_t *out) {
+    if (!out || block_elems(format) <= 0 || k <= 0 || k % block_elems(format) != 0 ||
+        rows < 1 || m_tokens < 1 || num_cu < 1)
+        return QMV_ERR_INVALID_ARGUMENT;
+    qmv::GemvPlan p;
+    if (!qmv::plan_gemv(format, k, rows, m_tokens >= 2 ? 2 : 1, num_cu, &p))
+        return QMV_ERR_UNSUPPORTED;
+    const int64_t g[8] = {p.T, p.P, p.L, p.UPL, p.RB, p.MT, p.per_cu, p.staged};
+    for (int i = 0; i < 8; i++) out[i] = g[i];
+    return QMV_OK;
+}
+
 int qmv_run_ex(int format, const void *W, const float *x, float *y, int64_t k, int64_t n,
                int64_t m_tokens, int64_t j_start, int64_t j_end, int accumulate, void *stream,
                int algo) {

@@ -245,6 +245,19 @@ const char *qmv_kernel_name(int format, int64_t k, int64_t m_tokens, int algo);
 const char *qmv_t_kernel_name(int format, int64_t k, int algo);
 const char *qmv_moe_kernel_name(int format, int64_t k, int algo);
 
+/* Launch geometry the streaming GEMV family (QMV_ALGO_GEMV) plans for `rows`
+ * rows of k weights and m_tokens tokens on a device with num_cu compute units.
+ * Host-only; needs no context or device. out (host memory, 8 entries)
+ * receives: threads per workgroup, row slots per workgroup, lanes per slot,
+ * 64-weight units per lane, rows per slot per batch, tokens per launch (1 or
+ * 2), the workgroups-per-compute-unit cap of the launch, and 1 when the
+ * weights are staged through LDS (block formats) else 0. Threads past
+ * slots*lanes are idle padding. Returns QMV_OK, QMV_ERR_INVALID_ARGUMENT for a
+ * bad format, shape, count or null out, or QMV_ERR_UNSUPPORTED when the
+ * streaming kernels do not cover the shape (the per-row kernel then runs). */
+int qmv_gemv_geometry(int format, int64_t k, int64_t rows, int64_t m_tokens, int num_cu,
+                      int64_t *out);
+
 #ifdef __cplusplus
 }
 #endif

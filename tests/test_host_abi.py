@@ -212,3 +212,47 @@ def test_create_without_a_device(lib):
     rc = qb.qmv_create()
     assert rc in (qb.QMV_ERR_NO_DEVICE, qb.QMV_ERR_UNSUPPORTED_ARCH)
     assert _run() == qb.QMV_ERR_NOT_INITIALIZED
+
+
+def test_gemv_geometry(lib):
+    """Host-side launch planning of the streaming GEMV family (no device):
+    large launches of 40-lane rows pad their workgroups to 4 whole waves and
+    take four per compute unit; small ones keep their row-slot workgroups."""
+    geo = qb.qmv_gemv_geometry
+    rc, g = geo(qb.QMV_FMT_Q6_K, 2560, 262144, 1, 256)  # vocabulary projection
+    assert rc == qb.QMV_OK
+    assert g == dict(threads=256, slots=6, lanes=40, units_per_lane=1, rows_per_slot=1,
+                     tokens=1, per_cu=4, staged=1)
+    rc, g = geo(qb.QMV_FMT_Q4_K, 2560, 10240, 1, 256)  # k=2560 x 10240: a few batches each
+    assert rc == qb.QMV_OK
+    assert (g["threads"], g["slots"], g["lanes"], g["per_cu"]) == (320, 8, 40, 2)
+    rc, g = geo(qb.QMV_FMT_BF16, 2560, 262144, 1, 256)  # direct kernel, same padding
+    assert (g["threads"], g["slots"], g["per_cu"], g["staged"]) == (256, 6, 4, 0)
+    rc, g = geo(qb.QMV_FMT_Q4_K, 4096, 14336, 2, 256)  # 64 lanes: already whole waves
+    assert (g["threads"], g["slots"], g["lanes"], g["tokens"], g["per_cu"]) == (256, 4, 64, 2, 2)
+    # the padding threshold: at least 4 batches per workgroup at 4 per compute unit
+    assert geo(qb.QMV_FMT_Q6_K, 2560, 6 * 4096, 1, 256)[1]["threads"] == 256
+    assert geo(qb.QMV_FMT_Q6_K, 2560, 6 * 4096 - 6, 1, 256)[1]["threads"] == 320
+    assert geo(qb.QMV_FMT_Q6_K, 2560, 6 * 4096 + 5, 1, 256)[1]["threads"] == 256
+    # invariants over shapes
+    for fmt in (qb.QMV_FMT_Q4_0, qb.QMV_FMT_Q4_K, qb.QMV_FMT_Q6_K, qb.QMV_FMT_BF16,
+                qb.QMV_FMT_Q8_0, qb.QMV_FMT_Q5_0):
+        for k in (256, 1024, 2304, 2560, 4096, 8192, 16384):
+            for rows in (1, 7, 300, 10240, 262144):
+                for m in (1, 2):
+                    rc, g = geo(fmt, k, rows, m, 256)
+                    assert rc == qb.QMV_OK, (fmt, k, rows, m)
+                    busy = g["slots"] * g["lanes"]
+                    assert busy <= g["threads"] <= 512
+                    assert g["lanes"] * g["units_per_lane"] >= k // 64
+                    if g["per_cu"] == 4:
+                        assert g["threads"] == 256 and (256 - busy) * 8 <= 256
+                    else:
+                        assert g["per_cu"] == 2 and g["threads"] == busy
+    # shapes the streaming kernels do not take, and bad arguments
+    assert geo(qb.QMV_FMT_F16, 96, 10, 1, 256)[0] == qb.QMV_ERR_UNSUPPORTED
+    assert geo(qb.QMV_FMT_Q4_K, 2560, 0, 1, 256)[0] == qb.QMV_ERR_INVALID_ARGUMENT
+    assert geo(qb.QMV_FMT_Q4_K, 2500, 10, 1, 256)[0] == qb.QMV_ERR_INVALID_ARGUMENT
+    assert geo(9, 2560, 10, 1, 256)[0] == qb.QMV_ERR_INVALID_ARGUMENT
+    assert lib.qmv_gemv_geometry(qb.QMV_FMT_Q4_K, 2560, 10, 1, 256, None) == \
+        qb.QMV_ERR_INVALID_ARGUMENT
