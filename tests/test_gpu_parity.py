@@ -386,3 +386,16 @@ def test_prefill_shape_gemv_path():
     rows = np.unique(np.concatenate([np.arange(32), np.arange(spec["n"] - 32, spec["n"]),
                                      np.random.default_rng(6).integers(0, spec["n"], 192)]))
     check_case(f, spec["k"], spec["n"], spec["m"], algo="gemv", W=W, x=x, rows=rows)
+
+
+@pytest.mark.parametrize("fmt", [Q6_K, Q4_K, BF16], ids=lambda f: synth.FORMAT_NAMES[f])
+def test_padded_workgroups_two_tokens(fmt):
+    """Padded launches with two tokens per launch (m=2): sampled rows of both
+    tokens against the oracle, and accumulate onto a base over a row range."""
+    k, n, m = 2560, 6 * 4096 + 5, 2
+    W, x = gen(fmt, k, n, m, 80 + fmt)
+    rows = np.unique(np.concatenate([np.arange(20), np.arange(n - 20, n),
+                                     np.random.default_rng(81).integers(0, n, 512)]))
+    check_case(fmt, k, n, m, W=W, x=x, rows=rows)
+    check_case(fmt, k, n, m, j0=3, j1=n - 2, accumulate=True, W=W, x=x, seed=82,
+               rows=rows[(rows >= 3) & (rows < n - 2)])
