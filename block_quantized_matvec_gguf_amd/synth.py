@@ -175,6 +175,11 @@ WORKLOADS = {
     # affine group-64 rows (codes, scales and biases in three arrays)
     "affine4_ffn_up": dict(id=9, fmt="affine", bits=4, k=2560, n=10240, m=1),
     "affine8_ffn_up": dict(id=10, fmt="affine", bits=8, k=2560, n=10240, m=1),
+    # the vocabulary-sized shape in other formats (streaming rate at a size
+    # where launch latency does not matter)
+    "q4_k_vocab": dict(id=11, fmt="q4_k", k=2560, n=262144, m=1, tiles=8),
+    "q8_0_vocab": dict(id=12, fmt="q8_0", k=2560, n=262144, m=1, tiles=8),
+    "bf16_vocab": dict(id=13, fmt="bf16", k=2560, n=262144, m=1, tiles=8),
 }
 
 
