@@ -677,11 +677,12 @@ static hipError_t launch_staged_npt(const GemvPlan &p, const uint8_t *W, const f
     }
 }
 
+// (the staged plan always has one row per slot per batch)
 template <class F, int MT, int UPL, bool XL>
 static hipError_t launch_staged_rb(const GemvPlan &p, const uint8_t *W, const float *x,
                                    float *y, int64_t k, int64_t n, int64_t rb, int64_t j0,
                                    int64_t j1, int acc, hipStream_t s) {
-    if (p.RB == 2) return launch_staged_npt<F, MT, UPL, 2, XL>(p, W, x, y, k, n, rb, j0, j1, acc, s);
+    if (p.RB != 1) return hipErrorInvalidValue;
     return launch_staged_npt<F, MT, UPL, 1, XL>(p, W, x, y, k, n, rb, j0, j1, acc, s);
 }
 
@@ -862,11 +863,11 @@ hipError_t launch_gemv_moe(const GemvPlan &p, const uint8_t *W, const uint32_t *
     const MoeArgs a = {ids, n_experts, top_k, (int)(n_pos * top_k)};
     const int64_t rb = row_bytes;
     switch (p.fmt) {
-    case FMT_Q4_0: return launch_moe_f<UQ4_0, true>(p, W, a, x, y, k, n, rb, accumulate, s);
-    case FMT_Q4_K: return launch_moe_f<UQ4_K, true>(p, W, a, x, y, k, n, rb, accumulate, s);
-    case FMT_Q6_K: return launch_moe_f<UQ6_K, true>(p, W, a, x, y, k, n, rb, accumulate, s);
-    case FMT_Q8_0: return launch_moe_f<UQ8_0, true>(p, W, a, x, y, k, n, rb, accumulate, s);
-    case FMT_Q5_0: return launch_moe_f<UQ5_0, true>(p, W, a, x, y, k, n, rb, accumulate, s);
+    case FMT_Q4_0: return launch_moe_f<IntX<UQ4_0>, true>(p, W, a, x, y, k, n, rb, accumulate, s);
+    case FMT_Q4_K: return launch_moe_f<IntX<UQ4_K>, true>(p, W, a, x, y, k, n, rb, accumulate, s);
+    case FMT_Q6_K: return launch_moe_f<IntX<UQ6_K>, true>(p, W, a, x, y, k, n, rb, accumulate, s);
+    case FMT_Q8_0: return launch_moe_f<IntX<UQ8_0>, true>(p, W, a, x, y, k, n, rb, accumulate, s);
+    case FMT_Q5_0: return launch_moe_f<IntX<UQ5_0>, true>(p, W, a, x, y, k, n, rb, accumulate, s);
     case FMT_BF16:
         return launch_moe_f<UHalf<true>, false>(p, W, a, x, y, k, n, rb, accumulate, s);
     case FMT_F16:
@@ -892,19 +893,19 @@ hipError_t launch_gemv(const GemvPlan &p, const uint8_t *W, const float *x, floa
                        int64_t j_end, int accumulate, hipStream_t stream) {
     switch (p.fmt) {
     case FMT_Q4_0:
-        return launch_staged<UQ4_0>(p, W, x, y, k, n, row_bytes, j_start, j_end, accumulate,
+        return launch_staged<IntX<UQ4_0>>(p, W, x, y, k, n, row_bytes, j_start, j_end, accumulate,
                                     stream);
     case FMT_Q4_K:
-        return launch_staged<UQ4_K>(p, W, x, y, k, n, row_bytes, j_start, j_end, accumulate,
+        return launch_staged<IntX<UQ4_K>>(p, W, x, y, k, n, row_bytes, j_start, j_end, accumulate,
                                     stream);
     case FMT_Q6_K:
-        return launch_staged<UQ6_K>(p, W, x, y, k, n, row_bytes, j_start, j_end, accumulate,
+        return launch_staged<IntX<UQ6_K>>(p, W, x, y, k, n, row_bytes, j_start, j_end, accumulate,
                                     stream);
     case FMT_Q8_0:
-        return launch_staged<UQ8_0>(p, W, x, y, k, n, row_bytes, j_start, j_end, accumulate,
+        return launch_staged<IntX<UQ8_0>>(p, W, x, y, k, n, row_bytes, j_start, j_end, accumulate,
                                     stream);
     case FMT_Q5_0:
-        return launch_staged<UQ5_0>(p, W, x, y, k, n, row_bytes, j_start, j_end, accumulate,
+        return launch_staged<IntX<UQ5_0>>(p, W, x, y, k, n, row_bytes, j_start, j_end, accumulate,
                                     stream);
     case FMT_BF16:
         return launch_direct<UHalf<true>>(p, W, x, y, k, n, row_bytes, j_start, j_end,

@@ -61,22 +61,6 @@ __device__ __forceinline__ float f16lo(uint32_t v) {
 __device__ __forceinline__ float f16hi(uint32_t v) {
     return (float)__builtin_bit_cast(_Float16, (uint16_t)(v >> 16));
 }
-// acc + sum_b byte_b(q) * x[b]
-__device__ __forceinline__ float dot4(uint32_t q, const float *x, float acc) {
-    acc = fmaf(ub0(q), x[0], acc);
-    acc = fmaf(ub1(q), x[1], acc);
-    acc = fmaf(ub2(q), x[2], acc);
-    acc = fmaf(ub3(q), x[3], acc);
-    return acc;
-}
-// acc + sum_b signed_byte_b(q) * x[b]
-__device__ __forceinline__ float sdot4(uint32_t q, const float *x, float acc) {
-    acc = fmaf(sb0(q), x[0], acc);
-    acc = fmaf(sb1(q), x[1], acc);
-    acc = fmaf(sb2(q), x[2], acc);
-    acc = fmaf(sb3(q), x[3], acc);
-    return acc;
-}
 // a[b] += s * byte_b(q), unsigned / signed bytes
 __device__ __forceinline__ void uaxpy4(uint32_t q, float s, float *a) {
     a[0] = fmaf(ub0(q), s, a[0]);
@@ -96,6 +80,88 @@ __device__ __forceinline__ void put4(float *d, f32x4 v) {
     d[1] = v.y;
     d[2] = v.z;
     d[3] = v.w;
+}
+
+// ------------------------------------- forward products on integer dots
+// The forward product of the block formats multiplies integer codes by x.
+// Instead of converting every code to f32 and issuing one FMA per weight,
+// x of a unit (64 values, fixed for the whole launch) is written once as
+// 24-bit integers with a power-of-two scale,
+//     x_e ~= s * X_e,   X_e = x2_e * 65536 + x1_e * 256 + x0_e,
+// each digit a signed byte, and the codes (signed bytes) meet the three
+// digit planes in v_dot4_i32_i8: four exact multiply-adds per instruction.
+// Integer partial sums of a scale group are exact; the group scale is
+// applied with a 24-bit integer multiply-add, and the three plane sums are
+// combined in f32 once per unit. s = 2^E with max|x| / s in [2^21, 2^22), so
+// every x_e is represented with an absolute error of at most s/2 <= 2^-22
+// max|x| over its unit (values far below the unit's largest carry
+// correspondingly fewer bits). E is kept >= -126 (s normal); a unit with a
+// non-finite x gets s = NaN, so its rows come out NaN.
+struct XI {
+    float f[64];       // the unit's x while loading: piece i is f[4i..4i+3]
+    uint32_t p[3][16]; // digit planes: byte b of p[d][i] is digit d of x_{4i+b}
+    float s;           // the power-of-two scale (NaN for a non-finite x)
+    int ofs[2][3];     // per block (or half) and plane: a format-specific integer offset
+    float sum[2];      // Q4_K: f32 sums of pieces 0..7 and 8..15
+};
+
+__device__ __forceinline__ void x_planes(XI &x) {
+    float mx = 0.f;
+    bool finite = true;
+#pragma unroll
+    for (int e = 0; e < 64; e++) {
+        const float a = fabsf(x.f[e]);
+        finite = finite && (a <= 3.4028235e38f); // false for NaN and infinities
+        mx = fmaxf(mx, a);
+    }
+    int e2 = 0;
+    if (mx > 0.f) (void)frexpf(mx, &e2); // mx in [2^(e2-1), 2^e2)
+    int E = e2 - 22;
+    if (E < -126) E = -126;
+    x.s = finite ? ldexpf(1.f, E) : __builtin_nanf("");
+#pragma unroll
+    for (int i = 0; i < 16; i++) {
+        uint32_t d0 = 0, d1 = 0, d2 = 0;
+#pragma unroll
+        for (int b = 0; b < 4; b++) {
+            const int X = (int)rintf(ldexpf(x.f[4 * i + b], -E)); // |X| <= 2^22
+            const int x0 = (int)((uint32_t)X << 24) >> 24;        // balanced base-256 digits
+            const int r = (X - x0) >> 8;
+            const int x1 = (int)((uint32_t)r << 24) >> 24;
+            const int x2 = (r - x1) >> 8;                          // |x2| <= 65
+            d0 |= ((uint32_t)x0 & 0xffu) << (8 * b);
+            d1 |= ((uint32_t)x1 & 0xffu) << (8 * b);
+            d2 |= ((uint32_t)x2 & 0xffu) << (8 * b);
+        }
+        x.p[0][i] = d0;
+        x.p[1][i] = d1;
+        x.p[2][i] = d2;
+    }
+}
+
+// Sum of the signed digit bytes of plane dwords [i0, i1).
+__device__ __forceinline__ int plane_sum(const XI &x, int d, int i0, int i1) {
+    int s = 0;
+    for (int i = i0; i < i1; i++) s = __builtin_amdgcn_sdot4((int)x.p[d][i], 0x01010101, s, false);
+    return s;
+}
+
+__device__ __forceinline__ int sdot4i(uint32_t a, uint32_t b, int c) {
+    return __builtin_amdgcn_sdot4((int)a, (int)b, c, false);
+}
+// The first dot of a chain: v_dot4_i32_i8 with a zero addend (written out,
+// the compiler zeroes a register and uses the accumulating form, one more
+// instruction). Plain VALU operations, no memory access.
+__device__ __forceinline__ int sdot4z(uint32_t a, uint32_t b) {
+    int r;
+    asm("v_dot4_i32_i8 %0, %1, %2, 0" : "=v"(r) : "v"(a), "v"(b));
+    return r;
+}
+// a * b + c with a, b within 24 bits (a 24-bit multiply and an add)
+__device__ __forceinline__ int mad24(int a, int b, int c) { return __mul24(a, b) + c; }
+// s * (A2 * 65536 + A1 * 256 + A0) for the three plane sums
+__device__ __forceinline__ float planes_f32(int a0, int a1, int a2) {
+    return fmaf((float)a2, 65536.f, fmaf((float)a1, 256.f, (float)a0));
 }
 
 // Each unit type below provides
@@ -158,21 +224,36 @@ struct UQ4_0 : NibbleBlocksX {
         r.d1 = e[4] >> 16;
         r.q1 = u32x4{e[5], e[6], e[7], e[8]};
     }
-    static __device__ __forceinline__ float block(u32x4 qv, uint32_t dbits, const X &x, int b) {
-        const uint32_t q[4] = {qv.x, qv.y, qv.z, qv.w};
-        float acc_lo = 0.f, acc_hi = 0.f;
+    // Forward product on integer planes (pieces 8b..8b+3 are the low nibbles
+    // of block b, 8b+4..8b+7 the high nibbles). Low nibbles enter as q (0..15)
+    // with -8 * sum(x) of the low half as the chain's start, high nibbles as
+    // the signed byte 16*(q-8); 16 * low + high is then 16 * sum (q-8) x.
+    static __device__ __forceinline__ void finish_xi(XI &x) {
 #pragma unroll
-        for (int j = 0; j < 4; j++) {
-            // bytes of 16*(q-8): low nibbles moved up, then both XOR 8 in the top nibble
-            const uint32_t lo = opaque(((q[j] << 4) ^ 0x80808080u) & 0xf0f0f0f0u);
-            const uint32_t hi = opaque((q[j] ^ 0x80808080u) & 0xf0f0f0f0u);
-            acc_lo = sdot4(lo, &x.lo[b][4 * j], acc_lo);
-            acc_hi = sdot4(hi, &x.hi[b][4 * j], acc_hi);
-        }
-        return (f16lo(dbits) * 0.0625f) * (acc_lo + acc_hi);
+        for (int b = 0; b < 2; b++)
+#pragma unroll
+            for (int d = 0; d < 3; d++) x.ofs[b][d] = -8 * plane_sum(x, d, 8 * b, 8 * b + 4);
     }
-    static __device__ __forceinline__ float dot(const Raw &r, const X &x, int) {
-        return block(r.q0, r.d0, x, 0) + block(r.q1, r.d1, x, 1);
+    static __device__ __forceinline__ float block_i(u32x4 qv, uint32_t dbits, const XI &x,
+                                                    int b) {
+        const uint32_t q[4] = {qv.x, qv.y, qv.z, qv.w};
+        int t[3];
+#pragma unroll
+        for (int d = 0; d < 3; d++) {
+            int lo = x.ofs[b][d];
+            int hi = sdot4z((q[0] & 0xf0f0f0f0u) ^ 0x80808080u, x.p[d][8 * b + 4]);
+#pragma unroll
+            for (int j = 0; j < 4; j++) {
+                lo = sdot4i(q[j] & 0x0f0f0f0fu, x.p[d][8 * b + j], lo);
+                if (j > 0)
+                    hi = sdot4i((q[j] & 0xf0f0f0f0u) ^ 0x80808080u, x.p[d][8 * b + 4 + j], hi);
+            }
+            t[d] = (lo << 4) + hi;
+        }
+        return f16lo(dbits) * planes_f32(t[0], t[1], t[2]);
+    }
+    static __device__ __forceinline__ float dot_i(const Raw &r, const XI &x, int) {
+        return (0.0625f * x.s) * (block_i(r.q0, r.d0, x, 0) + block_i(r.q1, r.d1, x, 1));
     }
     static __device__ __forceinline__ void axpy_block(u32x4 qv, uint32_t dbits, float dy, X &a,
                                                       int b) {
@@ -232,18 +313,23 @@ struct UQ8_0 {
             saxpy4(r.q1[j], s1, &a.v[1][4 * j]);
         }
     }
-    static __device__ __forceinline__ float block(const uint32_t (&q)[8], uint32_t dbits,
-                                                  const X &x, int b) {
-        float a0 = 0.f, a1 = 0.f;
+    // Forward product on integer planes: the code bytes are the signed
+    // multipliers as they are (pieces 8b..8b+7 = block b).
+    static __device__ __forceinline__ void finish_xi(XI &) {}
+    static __device__ __forceinline__ float block_i(const uint32_t (&q)[8], uint32_t dbits,
+                                                    const XI &x, int b) {
+        int t[3];
 #pragma unroll
-        for (int j = 0; j < 8; j += 2) {
-            a0 = sdot4(q[j], &x.v[b][4 * j], a0);
-            a1 = sdot4(q[j + 1], &x.v[b][4 * j + 4], a1);
+        for (int d = 0; d < 3; d++) {
+            int a = sdot4z(q[0], x.p[d][8 * b]);
+#pragma unroll
+            for (int j = 1; j < 8; j++) a = sdot4i(q[j], x.p[d][8 * b + j], a);
+            t[d] = a;
         }
-        return f16lo(dbits) * (a0 + a1);
+        return f16lo(dbits) * planes_f32(t[0], t[1], t[2]);
     }
-    static __device__ __forceinline__ float dot(const Raw &r, const X &x, int) {
-        return block(r.q0, r.d0, x, 0) + block(r.q1, r.d1, x, 1);
+    static __device__ __forceinline__ float dot_i(const Raw &r, const XI &x, int) {
+        return x.s * (block_i(r.q0, r.d0, x, 0) + block_i(r.q1, r.d1, x, 1));
     }
 };
 
@@ -280,22 +366,32 @@ struct UQ5_0 : NibbleBlocksX {
         const uint32_t m = opaque(__umul24(__builtin_amdgcn_ubfe(nh, at, 4), 0x204081u));
         return (m & 0x01010101u) << 7;
     }
-    static __device__ __forceinline__ float block(u32x4 qv, uint32_t qh, uint32_t dbits,
-                                                  const X &x, int b) {
+    // Forward product on integer planes: the signed bytes 8*(q-16) of both
+    // halves of block b meet pieces 8b..8b+7.
+    static __device__ __forceinline__ void finish_xi(XI &) {}
+    static __device__ __forceinline__ float block_i(u32x4 qv, uint32_t qh, uint32_t dbits,
+                                                    const XI &x, int b) {
         const uint32_t q[4] = {qv.x, qv.y, qv.z, qv.w};
         const uint32_t nh = ~qh;
-        float acc_lo = 0.f, acc_hi = 0.f;
+        uint32_t c[8];
 #pragma unroll
         for (int j = 0; j < 4; j++) {
-            const uint32_t lo = opaque(((q[j] << 3) & 0x78787878u) | spread4(nh, 4 * j));
-            const uint32_t hi = opaque(((q[j] >> 1) & 0x78787878u) | spread4(nh, 16 + 4 * j));
-            acc_lo = sdot4(lo, &x.lo[b][4 * j], acc_lo);
-            acc_hi = sdot4(hi, &x.hi[b][4 * j], acc_hi);
+            c[j] = ((q[j] << 3) & 0x78787878u) | spread4(nh, 4 * j);
+            c[4 + j] = ((q[j] >> 1) & 0x78787878u) | spread4(nh, 16 + 4 * j);
         }
-        return (f16lo(dbits) * 0.125f) * (acc_lo + acc_hi);
+        int t[3];
+#pragma unroll
+        for (int d = 0; d < 3; d++) {
+            int a = sdot4z(c[0], x.p[d][8 * b]);
+#pragma unroll
+            for (int j = 1; j < 8; j++) a = sdot4i(c[j], x.p[d][8 * b + j], a);
+            t[d] = a;
+        }
+        return f16lo(dbits) * planes_f32(t[0], t[1], t[2]);
     }
-    static __device__ __forceinline__ float dot(const Raw &r, const X &x, int) {
-        return block(r.q0, r.h0, r.d0, x, 0) + block(r.q1, r.h1, r.d1, x, 1);
+    static __device__ __forceinline__ float dot_i(const Raw &r, const XI &x, int) {
+        return (0.125f * x.s) *
+               (block_i(r.q0, r.h0, r.d0, x, 0) + block_i(r.q1, r.h1, r.d1, x, 1));
     }
     static __device__ __forceinline__ void axpy_block(u32x4 qv, uint32_t qh, uint32_t dbits,
                                                       float dy, X &a, int b) {
@@ -369,24 +465,40 @@ struct UQ4_K {
         sc = ((a >> sa) & 15u) | (((d1 >> hs) & 3u) << 4);
         mn = ((b >> sb) & 15u) | (((d2 >> hs) & 3u) << 4);
     }
-    static __device__ __forceinline__ float dot(const Raw &r, const X &x, int u) {
-        const uint32_t q[8] = {r.q0.x, r.q0.y, r.q0.z, r.q0.w, r.q1.x, r.q1.y, r.q1.z, r.q1.w};
-        float acc_lo = 0.f, acc_hi = 0.f;
+    // Forward product on integer planes. Pieces 0..7 are the low nibbles
+    // (sub-block 2c), 8..15 the high nibbles (2c+1). Low nibbles enter as q
+    // (0..15); high nibbles as the signed byte 16*(q-8), the chain starting at
+    // 128 * sum(x) over the high pieces, which gives 16 * sum q x. The min
+    // term dmin * m * sum(x) uses the f32 sums of the two halves.
+    static __device__ __forceinline__ void finish_xi(XI &x) {
+        float a = 0.f, b = 0.f;
+        for (int i = 0; i < 32; i++) a += x.f[i];
+        for (int i = 32; i < 64; i++) b += x.f[i];
+        x.sum[0] = a;
+        x.sum[1] = b;
 #pragma unroll
-        for (int i = 0; i < 8; i++) {
-            const uint32_t lo = opaque(q[i] & 0x0f0f0f0fu), hi = opaque(q[i] & 0xf0f0f0f0u);
-            acc_lo = dot4(lo, &x.lo[4 * i], acc_lo);
-            acc_hi = dot4(hi, &x.hi[4 * i], acc_hi); // 16x the high nibble
-        }
+        for (int d = 0; d < 3; d++) x.ofs[0][d] = 128 * plane_sum(x, d, 8, 16);
+    }
+    static __device__ __forceinline__ float dot_i(const Raw &r, const XI &x, int u) {
+        const uint32_t q[8] = {r.q0.x, r.q0.y, r.q0.z, r.q0.w, r.q1.x, r.q1.y, r.q1.z, r.q1.w};
         const int s0 = 2 * (u & 3);
         uint32_t sc0, mn0, sc1, mn1;
         scale_min(r.hd.y, r.hd.z, r.hd.w, s0, sc0, mn0);
         scale_min(r.hd.y, r.hd.z, r.hd.w, s0 + 1, sc1, mn1);
+        int t[3];
+#pragma unroll
+        for (int d = 0; d < 3; d++) {
+            int lo = sdot4z(q[0] & 0x0f0f0f0fu, x.p[d][0]), hi = x.ofs[0][d];
+#pragma unroll
+            for (int i = 0; i < 8; i++) {
+                if (i > 0) lo = sdot4i(q[i] & 0x0f0f0f0fu, x.p[d][i], lo);
+                hi = sdot4i((q[i] & 0xf0f0f0f0u) ^ 0x80808080u, x.p[d][8 + i], hi);
+            }
+            t[d] = mad24((int)sc0 << 4, lo, __mul24((int)sc1, hi)); // 16 * sum sc q x
+        }
         const float d = f16lo(r.hd.x), dmin = f16hi(r.hd.x);
-        const float f0 = d * (float)sc0;
-        const float f1 = (d * 0.0625f) * (float)sc1;
-        const float mt = dmin * fmaf((float)mn1, x.shi, (float)mn0 * x.slo);
-        return fmaf(f1, acc_hi, fmaf(f0, acc_lo, -mt));
+        const float mt = dmin * fmaf((float)mn1, x.sum[1], (float)mn0 * x.sum[0]);
+        return fmaf((d * 0.0625f) * x.s, planes_f32(t[0], t[1], t[2]), -mt);
     }
     static __device__ __forceinline__ void axpy(const Raw &r, float dy, X &a, int u) {
         const int s0 = 2 * (u & 3);
@@ -511,19 +623,24 @@ struct UQ6_K {
 #pragma unroll
             for (int g = 0; g < 4; g++) saxpy4(q[g][j], s[g], &a.v[g][4 * j]);
     }
-    static __device__ __forceinline__ float dot(const Raw &r, const X &x, int) {
+    // Forward product on integer planes: the signed bytes 4*(q-32) of quarter
+    // g meet pieces 4g..4g+3; each quarter's three plane sums take its int8
+    // scale by a 24-bit multiply-add.
+    static __device__ __forceinline__ void finish_xi(XI &) {}
+    static __device__ __forceinline__ float dot_i(const Raw &r, const XI &x, int) {
         uint32_t q[4][4];
         codes(r, q);
-        float acc[4] = {0.f, 0.f, 0.f, 0.f};
+        int a[3] = {0, 0, 0};
 #pragma unroll
-        for (int j = 0; j < 4; j++)
+        for (int g = 0; g < 4; g++)
 #pragma unroll
-            for (int g = 0; g < 4; g++) acc[g] = sdot4(q[g][j], &x.v[g][4 * j], acc[g]);
-        float r0 = (float)r.s[0] * acc[0];
-        r0 = fmaf((float)r.s[1], acc[1], r0);
-        r0 = fmaf((float)r.s[2], acc[2], r0);
-        r0 = fmaf((float)r.s[3], acc[3], r0);
-        return (f16lo(r.d) * 0.25f) * r0;
+            for (int d = 0; d < 3; d++) {
+                int t = sdot4z(q[g][0], x.p[d][4 * g]);
+#pragma unroll
+                for (int j = 1; j < 4; j++) t = sdot4i(q[g][j], x.p[d][4 * g + j], t);
+                a[d] = g == 0 ? __mul24(r.s[g], t) : mad24(r.s[g], t, a[d]);
+            }
+        return ((f16lo(r.d) * 0.25f) * x.s) * planes_f32(a[0], a[1], a[2]);
     }
 };
 
@@ -604,6 +721,31 @@ struct UHalf {
             }
         }
         return acc0 + acc1;
+    }
+};
+
+// Forward-product view of a block unit U: its raw registers and LDS reads,
+// x as integer planes (XI), and U::dot_i for the unit's contribution.
+template <class U>
+struct IntX {
+    using Raw = typename U::Raw;
+    using X = XI;
+    static __device__ __forceinline__ void load_lds(Raw &r, const uint8_t *row, int u, int U_) {
+        U::load_lds(r, row, u, U_);
+    }
+    static __device__ __forceinline__ int x4_index(int u, int i, int U_) {
+        return U::x4_index(u, i, U_);
+    }
+    static __device__ __forceinline__ void x4_slot(int q, int U_, int &u, int &i) {
+        U::x4_slot(q, U_, u, i);
+    }
+    static __device__ __forceinline__ void put_x(X &x, int i, f32x4 v) { put4(&x.f[4 * i], v); }
+    static __device__ __forceinline__ void finish_x(X &x) {
+        x_planes(x);
+        U::finish_xi(x);
+    }
+    static __device__ __forceinline__ float dot(const Raw &r, const X &x, int u) {
+        return U::dot_i(r, x, u);
     }
 };
 
