@@ -309,7 +309,8 @@ __device__ __forceinline__ void direct_body(const uint8_t *__restrict__ W,
 
 // ------------------------------------------------------- staged kernel
 // Block formats. The byte range of a batch, [base*row_bytes,
-// end*row_bytes), is copied in 16-byte pieces aligned down to 16 bytes (so
+// end*row_bytes), is copied in 16-byte pieces aligned down to 16 bytes of
+// the 16-byte aligned base pointer (so
 // up to 15 bytes before it and, at the very end of W, up to 15 bytes after it
 // inside the same 16-byte granule, are read and ignored; W is 16-byte
 // aligned, so such a granule never crosses a page). The copy goes straight
@@ -329,8 +330,10 @@ struct StagedOccupancy {
     static constexpr int waves = (MT == 1 && UPL == 1 && RB == 1 && NPT <= 4) ? 4 : 1;
 };
 
+// W is 16-byte aligned; the matrix's row 0 starts w_off bytes after it (a
+// stacked expert's slice need not start on a 16-byte boundary).
 template <class F, int MT, int UPL, int RB, int NPT, bool XL>
-__device__ __forceinline__ void staged_body(const uint8_t *__restrict__ W,
+__device__ __forceinline__ void staged_body(const uint8_t *__restrict__ W, int64_t w_off,
                                             const float *__restrict__ x, float *__restrict__ y,
                                             int64_t k, int64_t n, int64_t row_bytes,
                                             int64_t j_start, int64_t j_end, int accumulate,
@@ -354,7 +357,7 @@ __device__ __forceinline__ void staged_body(const uint8_t *__restrict__ W,
     // Start copying batch b into weight buffer bi (and read its old y).
     auto copy = [&](int64_t b, int bi) {
         const int64_t r1 = b + rows_per_batch < j_end ? b + rows_per_batch : j_end;
-        const int64_t s0 = b * row_bytes, s1 = r1 * row_bytes;
+        const int64_t s0 = w_off + b * row_bytes, s1 = w_off + r1 * row_bytes;
         const int64_t a0 = s0 & ~(int64_t)15;
         const int np = (int)((((s1 + 15) & ~(int64_t)15) - a0) >> 4);
         const __amdgpu_buffer_rsrc_t rs = batch_rsrc(W + a0, 16 * np);
@@ -395,7 +398,7 @@ __device__ __forceinline__ void staged_body(const uint8_t *__restrict__ W,
         if (ln.NG > 1 && prev >= 0)
             finish_batch<MT, RB>(red + (cur ^ 1) * nq * ln.NG, ybuf + (cur ^ 1) * nq, ln.NG,
                                  P, ln.tid, ln.T, prev, j_end, y, n, accumulate);
-        const int off = (int)((base * row_bytes) & 15);
+        const int off = (int)((w_off + base * row_bytes) & 15);
         const uint8_t *bl = wb + cur * buf_bytes + off;
         float part[RB][MT];
 #pragma unroll
@@ -449,8 +452,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(
                                                                   int64_t j_start, int64_t j_end,
                                                                   int accumulate, int U, int L,
                                                                   int P, int G, int buf_bytes) {
-    staged_body<F, MT, UPL, RB, NPT, XL>(W, x, y, k, n, row_bytes, j_start, j_end, accumulate,
-                                         U, L, P, G, buf_bytes);
+    staged_body<F, MT, UPL, RB, NPT, XL>(W, 0, x, y, k, n, row_bytes, j_start, j_end,
+                                         accumulate, U, L, P, G, buf_bytes);
 }
 
 // Expert-indexed product (rullama 0.5.0, src/backend/dispatch/mod.rs, the
@@ -494,7 +497,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(
     int accumulate, int U, int L, int P, int G, int buf_bytes) {
     uint32_t e;
     if (!moe_pair(ids, n_experts, n, y, e)) return;
-    staged_body<F, 1, UPL, RB, NPT, XL>(W + (int64_t)e * n * row_bytes,
+    staged_body<F, 1, UPL, RB, NPT, XL>(W, (int64_t)e * n * row_bytes,
                                         x + (int64_t)(blockIdx.y / top_k) * k,
                                         y + (int64_t)blockIdx.y * n, k, n, row_bytes, 0, n,
                                         accumulate, U, L, P, G, buf_bytes);

@@ -91,16 +91,18 @@ __device__ __forceinline__ void put4(float *d, f32x4 v) {
 // each digit a signed byte, and the codes (signed bytes) meet the three
 // digit planes in v_dot4_i32_i8: four exact multiply-adds per instruction.
 // Integer partial sums of a scale group are exact; the group scale is
-// applied with a 24-bit integer multiply-add, and the three plane sums are
-// combined in f32 once per unit. s = 2^E with max|x| / s in [2^21, 2^22), so
-// every x_e is represented with an absolute error of at most s/2 <= 2^-22
-// max|x| over its unit (values far below the unit's largest carry
-// correspondingly fewer bits). E is kept >= -126 (s normal); a unit with a
-// non-finite x gets s = NaN, so its rows come out NaN.
+// applied with a 24-bit integer multiply, and the three plane sums are
+// combined in f32 once per unit, then scaled by 2^E with one ldexp (so the
+// scale itself never needs to be a normal f32). E is chosen per unit so
+// that max|x| / 2^E lies in [2^21, 2^22): every x_e is represented with an
+// absolute error of at most 2^(E-1) <= 2^-22 max|x| over its unit (values
+// far below the unit's largest carry correspondingly fewer bits). A unit with
+// a non-finite x gets a NaN multiplier, so its rows come out NaN.
 struct XI {
     float f[64];       // the unit's x while loading: piece i is f[4i..4i+3]
     uint32_t p[3][16]; // digit planes: byte b of p[d][i] is digit d of x_{4i+b}
-    float s;           // the power-of-two scale (NaN for a non-finite x)
+    float c;           // the unit's format constant (NaN for a non-finite x)
+    int e;             // E
     int ofs[2][3];     // per block (or half) and plane: a format-specific integer offset
     float sum[2];      // Q4_K: f32 sums of pieces 0..7 and 8..15
 };
@@ -116,9 +118,9 @@ __device__ __forceinline__ void x_planes(XI &x) {
     }
     int e2 = 0;
     if (mx > 0.f) (void)frexpf(mx, &e2); // mx in [2^(e2-1), 2^e2)
-    int E = e2 - 22;
-    if (E < -126) E = -126;
-    x.s = finite ? ldexpf(1.f, E) : __builtin_nanf("");
+    const int E = e2 - 22;
+    x.e = E;
+    x.c = finite ? 1.f : __builtin_nanf("");
 #pragma unroll
     for (int i = 0; i < 16; i++) {
         uint32_t d0 = 0, d1 = 0, d2 = 0;
@@ -229,6 +231,7 @@ struct UQ4_0 : NibbleBlocksX {
     // with -8 * sum(x) of the low half as the chain's start, high nibbles as
     // the signed byte 16*(q-8); 16 * low + high is then 16 * sum (q-8) x.
     static __device__ __forceinline__ void finish_xi(XI &x) {
+        x.c *= 0.0625f;
 #pragma unroll
         for (int b = 0; b < 2; b++)
 #pragma unroll
@@ -253,7 +256,7 @@ struct UQ4_0 : NibbleBlocksX {
         return f16lo(dbits) * planes_f32(t[0], t[1], t[2]);
     }
     static __device__ __forceinline__ float dot_i(const Raw &r, const XI &x, int) {
-        return (0.0625f * x.s) * (block_i(r.q0, r.d0, x, 0) + block_i(r.q1, r.d1, x, 1));
+        return ldexpf(x.c * (block_i(r.q0, r.d0, x, 0) + block_i(r.q1, r.d1, x, 1)), x.e);
     }
     static __device__ __forceinline__ void axpy_block(u32x4 qv, uint32_t dbits, float dy, X &a,
                                                       int b) {
@@ -329,7 +332,7 @@ struct UQ8_0 {
         return f16lo(dbits) * planes_f32(t[0], t[1], t[2]);
     }
     static __device__ __forceinline__ float dot_i(const Raw &r, const XI &x, int) {
-        return x.s * (block_i(r.q0, r.d0, x, 0) + block_i(r.q1, r.d1, x, 1));
+        return ldexpf(x.c * (block_i(r.q0, r.d0, x, 0) + block_i(r.q1, r.d1, x, 1)), x.e);
     }
 };
 
@@ -368,7 +371,7 @@ struct UQ5_0 : NibbleBlocksX {
     }
     // Forward product on integer planes: the signed bytes 8*(q-16) of both
     // halves of block b meet pieces 8b..8b+7.
-    static __device__ __forceinline__ void finish_xi(XI &) {}
+    static __device__ __forceinline__ void finish_xi(XI &x) { x.c *= 0.125f; }
     static __device__ __forceinline__ float block_i(u32x4 qv, uint32_t qh, uint32_t dbits,
                                                     const XI &x, int b) {
         const uint32_t q[4] = {qv.x, qv.y, qv.z, qv.w};
@@ -390,8 +393,8 @@ struct UQ5_0 : NibbleBlocksX {
         return f16lo(dbits) * planes_f32(t[0], t[1], t[2]);
     }
     static __device__ __forceinline__ float dot_i(const Raw &r, const XI &x, int) {
-        return (0.125f * x.s) *
-               (block_i(r.q0, r.h0, r.d0, x, 0) + block_i(r.q1, r.h1, r.d1, x, 1));
+        return ldexpf(x.c * (block_i(r.q0, r.h0, r.d0, x, 0) + block_i(r.q1, r.h1, r.d1, x, 1)),
+                      x.e);
     }
     static __device__ __forceinline__ void axpy_block(u32x4 qv, uint32_t qh, uint32_t dbits,
                                                       float dy, X &a, int b) {
@@ -476,6 +479,7 @@ struct UQ4_K {
         for (int i = 32; i < 64; i++) b += x.f[i];
         x.sum[0] = a;
         x.sum[1] = b;
+        x.c *= 0.0625f;
 #pragma unroll
         for (int d = 0; d < 3; d++) x.ofs[0][d] = 128 * plane_sum(x, d, 8, 16);
     }
@@ -498,7 +502,7 @@ struct UQ4_K {
         }
         const float d = f16lo(r.hd.x), dmin = f16hi(r.hd.x);
         const float mt = dmin * fmaf((float)mn1, x.sum[1], (float)mn0 * x.sum[0]);
-        return fmaf((d * 0.0625f) * x.s, planes_f32(t[0], t[1], t[2]), -mt);
+        return ldexpf((d * x.c) * planes_f32(t[0], t[1], t[2]), x.e) - mt;
     }
     static __device__ __forceinline__ void axpy(const Raw &r, float dy, X &a, int u) {
         const int s0 = 2 * (u & 3);
@@ -626,7 +630,7 @@ struct UQ6_K {
     // Forward product on integer planes: the signed bytes 4*(q-32) of quarter
     // g meet pieces 4g..4g+3; each quarter's three plane sums take its int8
     // scale by a 24-bit multiply-add.
-    static __device__ __forceinline__ void finish_xi(XI &) {}
+    static __device__ __forceinline__ void finish_xi(XI &x) { x.c *= 0.25f; }
     static __device__ __forceinline__ float dot_i(const Raw &r, const XI &x, int) {
         uint32_t q[4][4];
         codes(r, q);
@@ -640,7 +644,7 @@ struct UQ6_K {
                 for (int j = 1; j < 4; j++) t = sdot4i(q[g][j], x.p[d][4 * g + j], t);
                 a[d] = g == 0 ? __mul24(r.s[g], t) : mad24(r.s[g], t, a[d]);
             }
-        return ((f16lo(r.d) * 0.25f) * x.s) * planes_f32(a[0], a[1], a[2]);
+        return ldexpf((f16lo(r.d) * x.c) * planes_f32(a[0], a[1], a[2]), x.e);
     }
 };
 
