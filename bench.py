@@ -144,6 +144,35 @@ def summarize_pmc(args):
     print(json.dumps(out))
 
 
+def host_threads():
+    """Host threads for the oracle baseline: every CPU this process may run
+    on (its affinity mask), capped by OMP_NUM_THREADS when that is set (the
+    GPU machine sets it to the host share of one GPU)."""
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except AttributeError:
+        avail = os.cpu_count() or 1
+    omp = os.environ.get("OMP_NUM_THREADS")
+    threads = min(avail, int(omp)) if omp and omp.isdigit() and int(omp) > 0 else avail
+    return max(1, threads), avail, omp
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline_entry(value, threads, avail, omp, sample):
+    return {"value": value, "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": sample, "nproc": os.cpu_count(), "cpus_in_affinity": avail,
+            "omp_num_threads": omp, "cpu_model": cpu_model()}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -362,61 +391,57 @@ def main():
 
     if not args.no_cpu_baseline and op_aff:
         import oracle
-        threads = max(1, min(os.cpu_count() or 1, 16))
+        threads, avail, omp = host_threads()
         t0 = time.perf_counter()
         yref, sref = oracle.affine_gemv(fmt, words, scales, biases, x, k, n, threads=threads)
         dt = time.perf_counter() - t0
-        out["cpu_baseline"] = {
-            "value": round(wbytes / dt / 1e9, 3), "unit": "GB/s", "cores": threads,
-            "kind": "oracle", "sample": "all %d rows, m=%d, f64 accumulation; %.2f s"
-                                        % (n, m, dt)}
+        out["cpu_baseline"] = cpu_baseline_entry(
+            round(wbytes / dt / 1e9, 3), threads, avail, omp,
+            "all %d rows, m=%d, f64 accumulation; %.2f s" % (n, m, dt))
         res = oracle.check_parity(y_main, yref, sref)
         out["parity"] = {"ok": res["ok"], "max_err_over_tol": round(res["max_ratio"], 5),
                          "cosine": res["cosine"], "outputs": res["n"]}
     elif not args.no_cpu_baseline and op_moe:
         import oracle
-        threads = max(1, min(os.cpu_count() or 1, 16))
+        threads, avail, omp = host_threads()
         t0 = time.perf_counter()
         yref, sref = oracle.moe(fmt, W, last_ids, x, k, n, E, top_k, threads=threads)
         dt = time.perf_counter() - t0
-        out["cpu_baseline"] = {
-            "value": round(wbytes / dt / 1e9, 3), "unit": "GB/s", "cores": threads,
-            "kind": "oracle",
-            "sample": "the whole call (%d expert rows x %d), f64 accumulation; %.2f s"
-                      % (len(last_ids) * n, k, dt)}
+        out["cpu_baseline"] = cpu_baseline_entry(
+            round(wbytes / dt / 1e9, 3), threads, avail, omp,
+            "the whole call (%d expert rows x %d), f64 accumulation; %.2f s"
+            % (len(last_ids) * n, k, dt))
         res = oracle.check_parity(y_main, yref, sref)
         out["parity"] = {"ok": res["ok"], "max_err_over_tol": round(res["max_ratio"], 5),
                          "cosine": res["cosine"], "outputs": res["n"]}
     elif not args.no_cpu_baseline and op_t:
         import oracle
-        threads = max(1, min(os.cpu_count() or 1, 16))
+        threads, avail, omp = host_threads()
         # a bounded sample of columns (each needs every row of the range)
         ncols = max(1, min(k, 400_000_000 // max(1, n * m)))
         cols = np.linspace(0, k - 1, ncols).astype(np.int64)
         t0 = time.perf_counter()
         dref, sref = oracle.gemv_t_cols(fmt, W, x, k, n, cols, threads=threads)
         dt = time.perf_counter() - t0
-        out["cpu_baseline"] = {
-            "value": round(wbytes * ncols / k / dt / 1e9, 3), "unit": "GB/s",
-            "cores": threads, "kind": "oracle",
-            "sample": "%d of %d columns (evenly spaced), all %d rows, m=%d, f64 accumulation; "
-                      "%.2f s" % (ncols, k, n, m, dt)}
+        out["cpu_baseline"] = cpu_baseline_entry(
+            round(wbytes * ncols / k / dt / 1e9, 3), threads, avail, omp,
+            "%d of %d columns (evenly spaced), all %d rows, m=%d, f64 accumulation; %.2f s"
+            % (ncols, k, n, m, dt))
         res = oracle.check_parity(y_main[:, cols], dref, sref)
         out["parity"] = {"ok": res["ok"], "max_err_over_tol": round(res["max_ratio"], 5),
                          "cosine": res["cosine"], "outputs": res["n"]}
     elif not args.no_cpu_baseline:
         import oracle
-        threads = max(1, min(os.cpu_count() or 1, 16))
+        threads, avail, omp = host_threads()
         # the whole workload when it is small enough, else a bounded row sample
         rows = n if k * n * m <= 4_000_000_000 else max(1, 4_000_000_000 // (k * m))
         t0 = time.perf_counter()
         yref, sref = oracle.gemv(fmt, W, x, k, n, 0, rows, threads=threads)
         dt = time.perf_counter() - t0
-        out["cpu_baseline"] = {
-            "value": round(rows * (wbytes / n) / dt / 1e9, 3), "unit": "GB/s",
-            "cores": threads, "kind": "oracle",
-            "sample": "rows 0..%d of %d (%s), m=%d, f64 accumulation; %.2f s" % (
-                rows, n, "all" if rows == n else "first rows", m, dt)}
+        out["cpu_baseline"] = cpu_baseline_entry(
+            round(rows * (wbytes / n) / dt / 1e9, 3), threads, avail, omp,
+            "rows 0..%d of %d (%s), m=%d, f64 accumulation; %.2f s" % (
+                rows, n, "all" if rows == n else "first rows", m, dt))
         res = oracle.check_parity(y_main[:, :rows], yref, sref)
         out["parity"] = {"ok": res["ok"], "max_err_over_tol": round(res["max_ratio"], 5),
                          "cosine": res["cosine"], "outputs": res["n"]}

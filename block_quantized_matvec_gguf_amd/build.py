@@ -33,31 +33,56 @@ def common_flags():
             "-I", INCLUDE, "-I", CSRC, "-Wall", "-Wno-unused-command-line-argument"]
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    cc = hipcc()
+# Host code of this build is instrumented with AddressSanitizer and
+# UndefinedBehaviorSanitizer (device code is built as usual); the CPU tests
+# exercise its argument validation and planning with the sanitizer runtime
+# preloaded. It is never loaded on a GPU.
+SAN_BUILD = os.path.join(BUILD, "san")
+SAN_LIB = os.path.join(SAN_BUILD, "libqmv_hostsan.so")
+SAN_FLAGS = ["-Xarch_host", "-g", "-Xarch_host", "-fno-omit-frame-pointer", "-Xarch_host", "-fsanitize=address",
+             "-Xarch_host", "-fsanitize=undefined", "-Xarch_host", "-fno-sanitize-recover=undefined"]
 
-    def compile_one(src):
-        obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-        lang = ["-x", "hip"] if src.endswith(".hip") else []
-        cmd = [cc] + common_flags() + lang + ["-c", os.path.join(CSRC, src), "-o", obj]
-        r = subprocess.run(cmd, capture_output=True, text=True)
-        out = "\n".join(l for l in (r.stdout + r.stderr).splitlines()
-                        if "packed-fp32-ops" not in l and l.strip())
-        if r.returncode != 0:
-            raise RuntimeError("compile failed: %s\n%s" % (" ".join(cmd), out))
-        if verbose and out:
-            print(out)
-        return obj
 
-    with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(compile_one, SOURCES))
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [cc, "-shared", "-fPIC", "--offload-arch=" + ARCH, "-o", tmp] + objs
+def _compile(cc, src, outdir, extra, verbose):
+    obj = os.path.join(outdir, os.path.splitext(src)[0] + ".o")
+    lang = ["-x", "hip"] if src.endswith(".hip") else []
+    cmd = [cc] + common_flags() + extra + lang + ["-c", os.path.join(CSRC, src), "-o", obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    out = "\n".join(l for l in (r.stdout + r.stderr).splitlines()
+                    if "packed-fp32-ops" not in l and l.strip())
+    if r.returncode != 0:
+        raise RuntimeError("compile failed: %s\n%s" % (" ".join(cmd), out))
+    if verbose and out:
+        print(out)
+    return obj
+
+
+def _link(cc, objs, lib, extra):
+    tmp = lib + ".tmp%d" % os.getpid()
+    cmd = [cc, "-shared", "-fPIC", "--offload-arch=" + ARCH] + extra + ["-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed: %s\n%s%s" % (" ".join(cmd), r.stdout, r.stderr))
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False, sanitized: bool = True) -> str:
+    """Build libqmv.so and, with sanitized=True, the host-sanitizer build
+    next to the objects (both in parallel)."""
+    os.makedirs(BUILD, exist_ok=True)
+    os.makedirs(SAN_BUILD, exist_ok=True)
+    cc = hipcc()
+    jobs = [(src, BUILD, []) for src in SOURCES]
+    if sanitized:
+        jobs += [(src, SAN_BUILD, SAN_FLAGS) for src in SOURCES]
+    # the slowest sources first
+    jobs.sort(key=lambda j: os.path.getsize(os.path.join(CSRC, j[0])), reverse=True)
+    with ThreadPoolExecutor(max_workers=min(len(jobs), os.cpu_count() or 4)) as ex:
+        objs = list(ex.map(lambda j: (j[1], _compile(cc, j[0], j[1], j[2], verbose)), jobs))
+    _link(cc, [o for d, o in objs if d == BUILD], LIB, [])
+    if sanitized:
+        _link(cc, [o for d, o in objs if d == SAN_BUILD], SAN_LIB,
+              ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined"])
     return LIB
 
 

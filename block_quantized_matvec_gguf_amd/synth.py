@@ -19,14 +19,19 @@ Q8_0 and Q5_0 draws mirror Q4_0's, as no measured workload uses them):
 * Q5_0: per 32-weight block f16 d ~ U[0.001, 0.02], a uniform random 32-bit
   word of fifth bits and 16 uniform code bytes (every 5-bit code uniform on
   0..31).
-* F16 / BF16: weights ~ N(0, 0.02), rounded to nearest-even in the storage
-  type (f64 draw -> f32 -> storage type).
-* Affine 4-bit / 8-bit group-64 rows: uniform u32 code words, bf16 scales ~
-  U[0.01, 0.06] and biases ~ U[-0.1, 0.1] per group (the spans of the pages'
-  4-bit fixture; rounded to nearest even).
+* F16 / BF16: weights ~ N(0, 0.02), the f64 draw rounded once, to nearest
+  even, to the storage type.
+* Affine 4-bit / 8-bit group-64 rows: uniform u32 code words and, per group,
+  a bf16 scale 0.05 u + 0.01 and a bf16 bias 0.2 u' - 0.1 with u, u' ~
+  U[-1, 1) (the draws of the pages' 4-bit fixture: scales in [-0.04, 0.06),
+  biases in [-0.3, 0.1); rounded to nearest even where the fixture
+  truncates).
 * x: f32 ~ U[-1, 1].
 
-All generators take a numpy Generator; the named workloads use fixed seeds.
+All generators take a numpy Generator (PCG64); the named workloads use fixed
+seeds. The inputs only need to be seeded and reproducible, so numpy's
+generator serves; the tests that rebuild the pages' own fixtures use the
+pages' byte formulas and generator instead.
 """
 from __future__ import annotations
 
@@ -66,9 +71,19 @@ def _f16_bytes(values: np.ndarray) -> np.ndarray:
 
 
 def bf16_bits(values: np.ndarray) -> np.ndarray:
-    """Round f32 values to bfloat16 (nearest, ties to even) and return the
-    16-bit patterns. Inputs must be finite."""
-    f = np.ascontiguousarray(values, dtype=np.float32)
+    """Round values to bfloat16 (nearest, ties to even) and return the 16-bit
+    patterns. f64 input is rounded once, from f64 (it must be finite and zero
+    or at least 2^-126 in magnitude, where bf16 keeps 8 significant bits);
+    any other input is taken as f32 (finite)."""
+    v = np.asarray(values)
+    if v.dtype == np.float64:
+        u = np.ascontiguousarray(v).view(np.uint64)
+        # keep the top 8 significant bits of the f64 (bit 45 up), ties to even
+        half = np.uint64((1 << 44) - 1)
+        r = (u + half + ((u >> np.uint64(45)) & np.uint64(1))) & ~np.uint64((1 << 45) - 1)
+        f = r.view(np.float64).astype(np.float32)  # exact: 8 significant bits
+        return (f.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+    f = np.ascontiguousarray(v, dtype=np.float32)
     u = f.view(np.uint32).astype(np.uint64)
     rounded = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
     return rounded.astype(np.uint16)
@@ -79,12 +94,13 @@ def gen_x(rng: np.random.Generator, m: int, k: int) -> np.ndarray:
 
 
 def gen_f16(rng, n, k, std=0.02) -> np.ndarray:
-    w = rng.normal(0.0, std, size=(n, k)).astype(np.float32)
+    w = rng.normal(0.0, std, size=(n, k))  # f64, rounded once to f16
     return np.ascontiguousarray(w.astype("<f2")).view(np.uint8).reshape(-1)
 
 
 def gen_bf16(rng, n, k, std=0.02) -> np.ndarray:
-    w = rng.normal(0.0, std, size=(n, k)).astype(np.float32)
+    w = rng.normal(0.0, std, size=(n, k))
+    w[np.abs(w) < 2.0 ** -126] = 0.0  # (never drawn in practice)
     return bf16_bits(w).astype("<u2").view(np.uint8).reshape(-1)
 
 
@@ -140,18 +156,21 @@ def gen_q5_0(rng, n, k, d_range=(0.001, 0.02)) -> np.ndarray:
     return blk.reshape(-1)
 
 
-def gen_affine(rng, bits, n, k, scale_range=(0.01, 0.06), bias_range=(-0.1, 0.1)):
+def gen_affine(rng, bits, n, k):
     """Affine group-quantized rows: uniform random u32 code words (k*bits/32
-    per row), bf16 scales ~ U[0.01, 0.06] and biases ~ U[-0.1, 0.1] per group
-    of 64 (the spans of the pages' 4-bit fixture). Returns (words, scales,
-    biases) as uint32 (n, k*bits/32), uint16 (n, k/64), uint16 (n, k/64)."""
+    per row) and, per group of 64, a bf16 scale 0.05 u + 0.01 and a bf16
+    bias 0.2 u' - 0.1 with u, u' ~ U[-1, 1) (the pages' 4-bit fixture draws
+    its scales and biases this way). Returns (words, scales, biases) as
+    uint32 (n, k*bits/32), uint16 (n, k/64), uint16 (n, k/64)."""
     if bits not in (4, 8) or k % 64:
         raise ValueError("affine rows need bits 4 or 8 and k % 64 == 0")
     words = rng.integers(0, 2 ** 32, size=(n, k * bits // 32), dtype=np.uint64).astype(np.uint32)
     g = k // 64
-    scales = bf16_bits(rng.uniform(scale_range[0], scale_range[1], size=(n, g)).astype(np.float32))
-    biases = bf16_bits(rng.uniform(bias_range[0], bias_range[1], size=(n, g)).astype(np.float32))
-    return words, scales, biases
+    sc = 0.05 * rng.uniform(-1.0, 1.0, size=(n, g)) + 0.01
+    bi = 0.2 * rng.uniform(-1.0, 1.0, size=(n, g)) - 0.1
+    sc[np.abs(sc) < 2.0 ** -126] = 0.0  # (never drawn in practice)
+    bi[np.abs(bi) < 2.0 ** -126] = 0.0
+    return words, bf16_bits(sc), bf16_bits(bi)
 
 
 def gen_weights(fmt, rng, n, k) -> np.ndarray:

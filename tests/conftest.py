@@ -12,6 +12,20 @@ def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
 
 
+def pytest_sessionstart(session):
+    """In the sanitizer child run (tests/test_sanitizers.py), load the
+    sanitizer builds of the oracle and of the host side of the library in
+    place of the regular ones."""
+    so = os.environ.get("QMV_SANITIZED_ORACLE")
+    if so:
+        import oracle
+        oracle.use_library(oracle.load_library(so))
+    sl = os.environ.get("QMV_SANITIZED_LIB")
+    if sl:
+        from block_quantized_matvec_gguf_amd import binding
+        binding.load(sl)
+
+
 GOLDEN = os.path.join(ROOT, "tests", "golden")
 
 

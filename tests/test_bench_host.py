@@ -77,3 +77,21 @@ def test_stale_traffic_is_ignored(tmp_path, monkeypatch):
     p.write_text(json.dumps({"kernel_source_sha256": bench.kernel_source_hash("gemv"),
                              "bytes_per_launch": 1.0}))
     assert bench.load_traffic("w", "gemv")["bytes_per_launch"] == 1.0
+
+
+def test_cpu_baseline_threads(monkeypatch):
+    """The oracle baseline uses every CPU in the process's affinity mask,
+    capped by OMP_NUM_THREADS when set, and reports what it used and why."""
+    import bench
+    avail = len(os.sched_getaffinity(0))
+    monkeypatch.delenv("OMP_NUM_THREADS", raising=False)
+    assert bench.host_threads() == (avail, avail, None)
+    monkeypatch.setenv("OMP_NUM_THREADS", "1")
+    assert bench.host_threads() == (1, avail, "1")
+    monkeypatch.setenv("OMP_NUM_THREADS", str(avail + 5))
+    assert bench.host_threads()[0] == avail
+    e = bench.cpu_baseline_entry(1.5, 1, avail, "1", "sample text")
+    for key in ("value", "unit", "cores", "kind", "sample", "nproc", "cpus_in_affinity",
+                "omp_num_threads", "cpu_model"):
+        assert key in e
+    assert e["kind"] == "oracle" and e["cores"] == 1 and e["cpu_model"]
