@@ -112,5 +112,11 @@ hipError_t launch_mfma(const MfmaPlan &p, const uint8_t *W, const float *x, floa
                        int64_t k, int64_t n, int64_t m, int64_t row_bytes, int64_t j_start,
                        int64_t j_end, int accumulate, hipStream_t stream);
 const char *mfma_kernel_name(const MfmaPlan &p);
+// Bytes of the staging buffer a matrix-core launch uses, and the launch with
+// that buffer supplied by the caller (device memory, 16-byte aligned).
+size_t mfma_scratch_bytes(const MfmaPlan &p, int64_t k);
+hipError_t launch_mfma_ws(const MfmaPlan &p, const uint8_t *W, const float *x, float *y,
+                          int64_t k, int64_t n, int64_t m, int64_t row_bytes, int64_t j_start,
+                          int64_t j_end, int accumulate, void *scratch, hipStream_t stream);
 
 } // namespace qmv

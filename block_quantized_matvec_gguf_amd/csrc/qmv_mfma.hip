@@ -9,33 +9,36 @@
 // w = d*sc*q - dmin*m.
 //
 // Two kernels on the caller's stream:
-//  1. qmv_mfma_prep_x: for every (token, super-block) choose a power of two
-//     p = 2^e with max|x|/p in [2^14, 2^15), and write x/p as two f16 terms
-//     hi = f16(x/p), lo = f16(x/p - hi) (22 significant bits together; the
-//     scaling keeps hi and lo normal for all but negligible values), laid out
-//     in the MFMA operand order so that every wave load of the main kernel
-//     reads one contiguous KB. It also writes, per token and 32-weight
-//     sub-block, the f32 sum of x (fixed order) divided by 32p, split hi/lo, and
-//     the table of p. Staging memory comes from the stream's device pool
-//     (hipMallocAsync/hipFreeAsync), m*k*4 bytes plus k*m/8 + k*m/64.
-//  2. qmv_mfma_q4_k: each super-block's product runs on
-//     v_mfma_f32_32x32x16_f16 with B = sc*q, an exact f16 integer (<= 945),
-//     against hi and lo; the 16 K-steps of a super-block accumulate in f32 in
-//     a fresh tile, then one f32 FMA per output adds d*p*tile. The min term
-//     dmin * sum_g m_g * sum(x over g) takes one more MFMA per super-block
-//     (A = the hi/lo sums, B = the 6-bit mins, exact), scaled by dmin*p.
+//  1. qmv_mfma_prep_x, one wave per (token, pair of super-blocks): finds the
+//     power of two p with max|x_t|/p in [2^14, 2^15) and writes x_t/p as two
+//     f16 terms hi = f16(x/p), lo = f16(x/p - hi) (22 significant bits
+//     together) in the order the main kernel's A operands take them, so that
+//     each of its wave loads reads one contiguous kilobyte; also the f32 sum
+//     of each 32-weight sub-block (fixed order) divided by 32p, split hi/lo,
+//     and p.
+//  2. qmv_mfma_q4_k: v_mfma_f32_32x32x16_f16 with B = sc*q, an exact f16
+//     integer (<= 945) made by inserting the nibble into the mantissa of 1024
+//     and one packed f16 FMA, against hi and lo. The 16 K-steps of a
+//     super-block accumulate in a fresh f32 tile; then acc += d*tile. The min
+//     term dmin * sum_g m_g * sum(x over g) takes one more MFMA per
+//     super-block (A = the hi/lo sums, B = the 6-bit mins, exact); the token's
+//     p scales the result once, at the store (by its exponent, so that p need
+//     not be a normal f32).
 //
-// Mapping of the main kernel. A workgroup owns 64 tokens x 64 rows and has 8
-// waves: wave w takes token half th = w&1 and K quarter kq = w>>1 (super-blocks
-// kq, kq+4, ...) and holds its 32 tokens x 64 rows as two 32x32 accumulators
-// (lane l feeds A[l%32][8(l/32)+i] and B[8(l/32)+i][l%32] and receives
-// D[8(r/4)+4(l/32)+r%4][l%32] in register r). Tokens are the MFMA rows and
-// weight rows the columns, so a lane's block scales are scalars. Each quarter
-// stages the weight bytes of its super-blocks in LDS (buffer_load ... lds, one
-// contiguous run per row), the next super-block's while one is decoded (two
-// slots per quarter, each copy split between the quarter's two waves); the
-// four quarters' partial tiles are summed in LDS in quarter order. Results
-// depend only on k, never on the row range or the token tiling.
+// Mapping of the main kernel. A workgroup owns 64 tokens x 64 rows and has 4
+// waves, one per SIMD; wave w takes super-blocks w, w+4, ... and all 64 x 64
+// outputs, as four 32x32 accumulators (token tile tt x row tile rt). Lane l feeds
+// A[l%32][8(l/32)+i] and B[8(l/32)+i][l%32] and receives
+// D[8(r/4)+4(l/32)+r%4][l%32] in register r: tokens are the MFMA rows, weight
+// rows the columns, so a lane's block scales are those of one weight row. Each
+// decoded B operand feeds four MFMAs (two token tiles, hi and lo) and each A
+// operand two (both row tiles). Each wave copies its super-blocks' bytes of the
+// 64 rows into its own LDS slots (buffer_load ... lds, two slots, one
+// super-block ahead) and reads its lanes' fields from there; its A operands
+// come from the staged x in global memory (L2), six K-steps ahead in
+// registers. At the end the four waves' partial tiles are summed in LDS in
+// wave order. Results depend
+// only on k, never on the row range or the token tiling.
 #include "qmv_internal.h"
 
 namespace qmv {
@@ -47,32 +50,33 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int TM = 64;      // tokens per tile
-constexpr int TN = 64;      // weight rows per tile
-constexpr int KQ = 4;       // split of K over the waves of the main kernel
-constexpr int NT = 64 * 2 * KQ; // threads per workgroup: 2 token halves x KQ
-constexpr int SBB = 144;    // bytes of a Q4_K super-block
-constexpr int PF = 3;       // sub-blocks of x operands loaded ahead
-constexpr int QUARTER_W = TN * SBB * 2; // a quarter's two staging slots (one super-block each)
-constexpr size_t RED_BYTES = (size_t)KQ * TM * TN * sizeof(float); // partial tiles
-constexpr size_t LDS_BYTES =
-    (size_t)KQ * QUARTER_W > RED_BYTES ? (size_t)KQ * QUARTER_W : RED_BYTES;
+constexpr int TM = 64;          // tokens per tile
+constexpr int TN = 64;          // weight rows per tile
+constexpr int KW = 4;           // waves per workgroup (split of the super-blocks)
+constexpr int NT = 64 * KW;     // threads per workgroup
+constexpr int SBB = 144;        // bytes of a Q4_K super-block
+constexpr int SLOT = TN * SBB;  // one super-block of the tile's rows in LDS
+constexpr int PF = 6;           // K-steps of A operands loaded ahead
+constexpr int RING = 8;         // A operand slots (16 K-steps per super-block: a multiple)
+static_assert((size_t)(KW / 2) * TM * TN * sizeof(float) <= (size_t)KW * SLOT,
+              "the partial tiles of half the waves fit in one slot array");
 
-// Staging layout, per 64-token tile T and super-block s (NSB = k/256):
-//   XS: [T][s][g 8][tp 2][tb 2][hl 2][lane 64] x 16 bytes (8 f16)
-//   SM: [T][s][tb 2][lane 64] x 16 bytes (8 f16 sums/(32p): lanes 0-31 hi, 32-63 lo)
-//   PS: [T][s][token 64] floats (the power of two p)
-// Lane (nl, jh) of (g, tp, tb) holds token 32tb+nl, elements
-// 32g + 16jh + 8tp + PERM[i] of the super-block: the order in which the code
-// decoder below produces its f16 pairs.
+// Staged x, per 64-token group T and super-block s (nsb = k/256):
+//   XS: [T][s][j 16][tt 2][h 2][lane 64] x 16 bytes (8 f16, h = 0 hi, 1 lo);
+//       lane l holds token 32tt + l%32, elements 32(j/2) + 16(l/32) + 8(j%2) +
+//       perm8(i) of the super-block in slot i
+//   SM: [T][s][tt 2][lane 64] x 16 bytes: sub-block sums / 32p (lanes 0-31 hi,
+//       32-63 lo; slot g = sub-block g)
+//   PE: [T][token 64] ints: the exponent of p
 constexpr size_t xs_bytes(int64_t tiles, int64_t nsb) { return (size_t)tiles * nsb * 64 * 1024; }
-constexpr size_t sm_bytes(int64_t tiles, int64_t nsb) { return (size_t)tiles * nsb * 2 * 64 * 16; }
-constexpr size_t ps_bytes(int64_t tiles, int64_t nsb) { return (size_t)tiles * nsb * 64 * 4; }
+constexpr size_t sm_bytes(int64_t tiles, int64_t nsb) { return (size_t)tiles * nsb * 2 * 1024; }
+constexpr size_t pe_bytes(int64_t tiles) { return (size_t)tiles * 64 * 4; }
 
+// Slot i of an 8-wide operand piece holds element perm8(i): the order in which
+// the code decoder below produces its f16 pairs (bytes 0 and 2 of a word, then
+// bytes 1 and 3).
 __device__ __forceinline__ int perm8(int i) { return (i & 4) | ((i & 1) << 1) | ((i >> 1) & 1); }
 
-// Staged x is read by every row tile: ordinary cached loads.
-__device__ __forceinline__ u32x4 ldc(const uint8_t *p) { return *(const u32x4 *)p; }
 __device__ __forceinline__ float h2f(uint32_t h) {
     return (float)__builtin_bit_cast(_Float16, (uint16_t)(h & 0xffffu));
 }
@@ -83,102 +87,97 @@ __device__ __forceinline__ uint32_t pk_f16(float a, float b) {
 
 // ------------------------------------------------------------ x staging
 
-// One wave per (4-token group of a 64-token tile, super-block): grid
-// (k/256, tiles, 16), 64 threads.
+// One wave per (token of the padded token range, pair of super-blocks c);
+// tokens at or past m stage zeros. Lane q takes 8-element group G = 64c + q;
+// group G of super-block s = G/32 covers elements 8(G%32) .. +7, which is
+// K-step j = 2g + j2 of lane half kh for g = (G%32)/4, kh = (G/2)%2, j2 = G%2. Every wave first finds the token's largest magnitude over all of k
+// (the row is read again from cache by each wave of the token).
 __global__ __launch_bounds__(64) void qmv_mfma_prep_x(const float *__restrict__ x, int64_t k,
                                                       int64_t m, uint8_t *__restrict__ xs,
                                                       uint8_t *__restrict__ sm,
-                                                      float *__restrict__ ps) {
-    __shared__ int e_tok[4];
-    __shared__ float s_tok[4][8];
-    __shared__ f32x4 xv[4][64]; // the group's x slice, read once from memory
+                                                      int *__restrict__ pe) {
     const int lane = threadIdx.x;
-    const int s = blockIdx.x, T = blockIdx.y, qg = blockIdx.z; // tokens 4qg..4qg+3 of T
+    const int64_t t = blockIdx.y;
+    const int64_t T = t >> 6;
+    const int tt = (int)((t >> 5) & 1), ln = (int)(t & 31);
     const int64_t nsb = k >> 8;
-    const int64_t ts = (int64_t)T * nsb + s; // (tile, super-block) index
+    const int64_t ng = k >> 3; // 8-element groups
+    const bool live = t < m;
+    const f32x4 *xt = (const f32x4 *)(x + (live ? t : 0) * k);
 
-    // Phase 1: per token, the exponent and the eight sub-block sums; lane l
-    // takes elements 4l..4l+3 of each of the 4 tokens.
-    float v[4][4];
+    // this lane's group, loaded before the max pass so that both are in flight
+    const int64_t G = (int64_t)blockIdx.x * 64 + lane;
+    const bool has = G < ng; // a lone last super-block leaves lanes 32-63 idle
+    float v[8];
+    if (live && has) {
+        const f32x4 a = xt[2 * G], b = xt[2 * G + 1];
+        v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+        v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+    } else {
+#pragma unroll
+        for (int i = 0; i < 8; i++) v[i] = 0.f;
+    }
+
+    // the token's largest magnitude
+    float mx = 0.f;
+    if (live) {
+        // sixteen independent loads in flight per lane (k/4 is a multiple of 64)
+        int64_t q = lane;
+        for (; q + 960 < 2 * ng; q += 1024) {
+            f32x4 c[16];
+#pragma unroll
+            for (int u = 0; u < 16; u++) c[u] = xt[q + 64 * u];
+#pragma unroll
+            for (int u = 0; u < 16; u++)
+                mx = fmaxf(mx, fmaxf(fmaxf(fabsf(c[u].x), fabsf(c[u].y)),
+                                     fmaxf(fabsf(c[u].z), fabsf(c[u].w))));
+        }
+        for (; q < 2 * ng; q += 64) {
+            const f32x4 c = xt[q];
+            mx = fmaxf(mx, fmaxf(fmaxf(fabsf(c.x), fabsf(c.y)), fmaxf(fabsf(c.z), fabsf(c.w))));
+        }
+    }
+    for (int o = 1; o < 64; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+    int e = 0;
+    if (mx > 0.f) {
+        (void)frexpf(mx, &e); // mx = f * 2^e, f in [0.5, 1)
+        e -= 15;              // mx / 2^e in [2^14, 2^15)
+    }
+    if (blockIdx.x == 0 && lane == 0) pe[t] = e;
+
+    if (!has) return; // whole sub-blocks of lanes leave together
+    const int64_t s = G >> 5;
+    const int gi = (int)(G & 31);
+    const int g = gi >> 2, kh = (gi >> 1) & 1, j2 = gi & 1;
+    float w[8], sum = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+        w[i] = ldexpf(v[perm8(i)], -e);
+        sum += ldexpf(v[i], -e);
+    }
+    uint32_t hi[4], lo[4];
 #pragma unroll
     for (int i = 0; i < 4; i++) {
-        const int64_t t = (int64_t)T * TM + 4 * qg + i;
-#pragma unroll
-        for (int j = 0; j < 4; j++)
-            v[i][j] = t < m ? x[t * k + 256 * (int64_t)s + 4 * lane + j] : 0.f;
-        xv[i][lane] = f32x4{v[i][0], v[i][1], v[i][2], v[i][3]};
+        const _Float16 h0 = (_Float16)w[2 * i], h1 = (_Float16)w[2 * i + 1];
+        hi[i] = (uint32_t)__builtin_bit_cast(uint16_t, h0) |
+                ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
+        lo[i] = pk_f16(w[2 * i] - (float)h0, w[2 * i + 1] - (float)h1);
     }
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-        float mx = fmaxf(fmaxf(fabsf(v[i][0]), fabsf(v[i][1])),
-                         fmaxf(fabsf(v[i][2]), fabsf(v[i][3])));
-        float sum = (v[i][0] + v[i][1]) + (v[i][2] + v[i][3]);
-        // sub-block g = lane / 8: sum over 8 lanes in a fixed pattern
-#pragma unroll
-        for (int o = 1; o < 8; o <<= 1) sum += __shfl_xor(sum, o, 64);
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
-        if (lane == 0) {
-            int e = 0;
-            if (mx > 0.f) {
-                (void)frexpf(mx, &e); // mx = f * 2^e, f in [0.5, 1)
-                e -= 15;              // mx / 2^e in [2^14, 2^15)
-                e = e < -100 ? -100 : (e > 100 ? 100 : e);
-            }
-            e_tok[i] = e;
-        }
-        if ((lane & 7) == 0) s_tok[i][lane >> 3] = sum;
-    }
-    __syncthreads();
-
-    // Phase 2: the operand pieces of the group's tokens: piece (g, tp, jh,
-    // token) gives the hi and lo 16-byte pieces of that slot. Token tt of the
-    // tile sits in MFMA row nl = tt % 32 of token half tb = tt / 32.
-    uint8_t *xt = xs + ts * 64 * 1024;
-#pragma unroll
-    for (int it = 0; it < 2; it++) {
-        const int pc = lane + 64 * it;
-        const int lq = pc & 3, jh = (pc >> 2) & 1, tp = (pc >> 3) & 1, g = pc >> 4;
-        const int tt = 4 * qg + lq, tb = tt >> 5, ln = (tt & 31) + 32 * jh;
-        float w[8];
-        {
-            const float *p = (const float *)&xv[lq][0] + 32 * g + 16 * jh + 8 * tp;
-#pragma unroll
-            for (int j = 0; j < 8; j++) w[j] = ldexpf(p[perm8(j)], -e_tok[lq]);
-        }
-        uint32_t hi[4], lo[4];
-#pragma unroll
-        for (int j = 0; j < 4; j++) {
-            const _Float16 h0 = (_Float16)w[2 * j], h1 = (_Float16)w[2 * j + 1];
-            hi[j] = (uint32_t)__builtin_bit_cast(uint16_t, h0) |
-                    ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
-            lo[j] = pk_f16(w[2 * j] - (float)h0, w[2 * j + 1] - (float)h1);
-        }
-        const size_t base = ((((size_t)g * 2 + tp) * 2 + tb) * 2) * 1024 + (size_t)ln * 16;
-        *(u32x4 *)(xt + base) = u32x4{hi[0], hi[1], hi[2], hi[3]};
-        *(u32x4 *)(xt + base + 1024) = u32x4{lo[0], lo[1], lo[2], lo[3]};
-    }
-    // Sums for the min term and the table of p.
-    if (lane < 8) {
-        const int lq = lane & 3, jh = lane >> 2;
-        const int tt = 4 * qg + lq, tb = tt >> 5, ln = (tt & 31) + 32 * jh;
-        uint32_t o[4];
-#pragma unroll
-        for (int j = 0; j < 4; j++) {
-            float a2[2];
-#pragma unroll
-            for (int q = 0; q < 2; q++) {
-                // a sum of 32 values below 2^15 can reach 2^20: scale by 2^-5 more
-                const float sv = ldexpf(s_tok[lq][2 * j + q], -e_tok[lq] - 5);
-                const float h = (float)(_Float16)sv;
-                a2[q] = jh ? sv - h : h;
-            }
-            o[j] = pk_f16(a2[0], a2[1]);
-        }
-        *(u32x4 *)(sm + (ts * 2 + tb) * 64 * 16 + (size_t)ln * 16) = u32x4{o[0], o[1], o[2], o[3]};
-    } else if (lane < 12) {
-        const int tq = lane - 8;
-        ps[ts * TM + 4 * qg + tq] = ldexpf(1.f, e_tok[tq]);
+    const int j = 2 * g + j2;
+    uint8_t *dst = xs + ((size_t)((T * nsb + s) * 16 + j) * 4 + tt * 2) * 1024 +
+                   (size_t)(ln + 32 * kh) * 16;
+    *(u32x4 *)dst = u32x4{hi[0], hi[1], hi[2], hi[3]};
+    *(u32x4 *)(dst + 1024) = u32x4{lo[0], lo[1], lo[2], lo[3]};
+    // sub-block sum over its four groups (consecutive lanes), fixed order
+    sum += __shfl_xor(sum, 1, 64);
+    sum += __shfl_xor(sum, 2, 64);
+    if ((gi & 3) == 0) {
+        // a sum of 32 values below 2^15 can reach 2^20: divided by 32
+        const float sv = sum * 0.03125f;
+        const _Float16 h = (_Float16)sv;
+        _Float16 *sd = (_Float16 *)(sm + ((size_t)(T * nsb + s) * 2 + tt) * 1024);
+        sd[ln * 8 + g] = h;
+        sd[(ln + 32) * 8 + g] = (_Float16)(sv - (float)h);
     }
 }
 
@@ -187,14 +186,6 @@ __global__ __launch_bounds__(64) void qmv_mfma_prep_x(const float *__restrict__ 
 __device__ __forceinline__ f32x16 mfma(f16x8 a, f16x8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
-
-// Byte i (0..11) of the packed scale/min field of a Q4_K header.
-__device__ __forceinline__ uint32_t scb(const u32x4 &h, int i) {
-    return (h[1 + (i >> 2)] >> (8 * (i & 3))) & 0xffu;
-}
-
-// s_waitcnt operand: vmcnt 0, expcnt and lgkmcnt left free (gfx9 encoding).
-constexpr int WAIT_VM0 = 0x0f70;
 
 // Hide a value from the optimiser (keeps bit-field inserts as v_bfi_b32).
 __device__ __forceinline__ uint32_t opaque(uint32_t v) {
@@ -208,19 +199,13 @@ __device__ __forceinline__ uint32_t opaque(uint32_t v) {
 // the exact f16 integer sc*q by one packed FMA: (1024 + q)*sc - 1024*sc, or
 // (1024 + 16q)*(sc/16) - 64*sc. Bytes 0 and 2 of a word give one f16 pair,
 // bytes 1 and 3 (after a one-byte rotation) the other.
-struct CodeMasks {
-    uint32_t lo, hi; // 0x000f000f, 0x00f000f0 (opaque)
-};
 __device__ __forceinline__ uint32_t code_pair(uint32_t w, uint32_t mask, f16x2 sc, f16x2 off) {
     const uint32_t mag = (w & mask) | (0x64006400u & ~mask); // one v_bfi_b32
     return __builtin_bit_cast(uint32_t,
                               __builtin_elementwise_fma(__builtin_bit_cast(f16x2, mag), sc, off));
 }
-// B operand of K-step tp of sub-block 2c+h from the lane's 16 code bytes of
-// chunk c: slots in perm8 order.
-__device__ __forceinline__ f16x8 codes_b(const u32x4 &q, int tp, uint32_t mask, f16x2 sc,
+__device__ __forceinline__ f16x8 codes_b(uint32_t w0, uint32_t w1, uint32_t mask, f16x2 sc,
                                          f16x2 off) {
-    const uint32_t w0 = q[2 * tp], w1 = q[2 * tp + 1];
     const uint32_t r0 = __builtin_amdgcn_alignbyte(w0, w0, 1);
     const uint32_t r1 = __builtin_amdgcn_alignbyte(w1, w1, 1);
     const u32x4 r = {code_pair(w0, mask, sc, off), code_pair(r0, mask, sc, off),
@@ -228,31 +213,41 @@ __device__ __forceinline__ f16x8 codes_b(const u32x4 &q, int tp, uint32_t mask, 
     return __builtin_bit_cast(f16x8, r);
 }
 
-// Main kernel: 8 waves per workgroup; wave w takes token half th = w&1 of
-// the 64-token tile and K quarter kq = w>>1 (super-blocks kq, kq+4, ...).
-// The two waves of a quarter share its staged weight bytes.
-__global__ __launch_bounds__(NT) void qmv_mfma_q4_k(const uint8_t *__restrict__ W,
-                                                    const uint8_t *__restrict__ xs,
-                                                    const uint8_t *__restrict__ sm,
-                                                    const float *__restrict__ ps,
-                                                    float *__restrict__ y, int64_t k, int64_t n,
-                                                    int64_t m, int64_t row_bytes,
-                                                    int64_t j_start, int64_t j_end,
-                                                    int accumulate) {
-    // LDS: during the K loop, per quarter the staged super-blocks of its
-    // round; afterwards the [KQ][TM][TN] partial tiles.
-    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-    float *red = (float *)lds;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int th = wave & 1, kq = wave >> 1;
-    const int nl = lane & 31, jh = lane >> 5;
+// Byte i (0..11) of the packed scale/min field of a Q4_K header.
+__device__ __forceinline__ uint32_t scb(const u32x4 &h, int i) {
+    return (h[1 + (i >> 2)] >> (8 * (i & 3))) & 0xffu;
+}
+__device__ __forceinline__ void scale_min(const u32x4 &h, int g, uint32_t &sc, uint32_t &mn) {
+    if (g < 4) {
+        sc = scb(h, g) & 63u;
+        mn = scb(h, g + 4) & 63u;
+    } else {
+        sc = (scb(h, g + 4) & 15u) | ((scb(h, g - 4) >> 6) << 4);
+        mn = (scb(h, g + 4) >> 4) | ((scb(h, g) >> 6) << 4);
+    }
+}
+
+__global__ __launch_bounds__(NT, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) void qmv_mfma_q4_k(const uint8_t *__restrict__ W,
+                                                       const uint8_t *__restrict__ xs,
+                                                       const uint8_t *__restrict__ sm,
+                                                       const int *__restrict__ pe,
+                                                       float *__restrict__ y, int64_t k, int64_t n,
+                                                       int64_t m, int64_t row_bytes,
+                                                       int64_t j_start, int64_t j_end,
+                                                       int accumulate) {
+    // Two statically separate LDS arrays for the two weight slots, so that the
+    // compiler can tell that the copy in flight into one slot never touches
+    // the slot being read (otherwise it waits for the copy before every read).
+    __shared__ __attribute__((aligned(16))) uint8_t slot0[KW][SLOT];
+    __shared__ __attribute__((aligned(16))) uint8_t slot1[KW][SLOT];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int nl = lane & 31, kh = lane >> 5;
     const int64_t r0 = j_start + (int64_t)blockIdx.x * TN;
-    const int T = blockIdx.y;
-    const int64_t t0 = (int64_t)T * TM;
+    const int64_t T = blockIdx.y;
     const int nsb = (int)(k >> 8);
     const int rows = (int)(j_end - r0 < TN ? j_end - r0 : TN); // live rows of the tile
-    uint8_t *wl = lds + kq * QUARTER_W;
-    const CodeMasks cm = {opaque(0x000f000fu), opaque(0x00f000f0u)};
+    const uint32_t mlo = opaque(0x000f000fu), mhi = opaque(0x00f000f0u);
 
     // Staging copy: piece p = 64*i + lane of a super-block is bytes
     // 16*(p%9).. of row p/9; it lands at 16*p, so rows sit 144 bytes apart.
@@ -266,152 +261,192 @@ __global__ __launch_bounds__(NT) void qmv_mfma_q4_k(const uint8_t *__restrict__ 
         const int p = 64 * i + lane, r = p / 9;
         poff[i] = (r < rows ? r : rows - 1) * (int)row_bytes + 16 * (p - 9 * r);
     }
-
-    f32x16 acc[2];
+    // A descriptor with no records: every load through it is out of range,
+    // reads nothing and returns zeros. Copies and operand loads past the last
+    // super-block go through it, so that every path issues the same memory
+    // instructions and the compiler's wait counts stay exact (a load issued
+    // on one branch only makes it wait for every load in flight).
+    const __amdgpu_buffer_rsrc_t rnull =
+        __builtin_amdgcn_make_buffer_rsrc((void *)W, (short)0, 0, 0x00020000);
+    auto copy_sb = [&](int s, uint8_t *dst) {
+        const bool ok = s >= 0;
 #pragma unroll
-    for (int b = 0; b < 2; b++)
-#pragma unroll
-        for (int r = 0; r < 16; r++) acc[b][r] = 0.f;
-
-    // super-blocks of this quarter (nw); every wave runs nmax iterations. The
-    // quarter's next super-block is copied into its other slot while one is
-    // decoded; the two waves of the quarter split each copy.
-    const int nw = kq < nsb ? (nsb - kq + KQ - 1) / KQ : 0;
-    const int nmax = (nsb + KQ - 1) / KQ;
-    auto copy_sb = [&](int i, int slot) {
-        const int sboff = SBB * (kq + KQ * i);
-        for (int c = th; c < 9; c += 2) {
-            uint8_t *dst = wl + slot * (TN * SBB) + 1024 * c;
+        for (int i = 0; i < 9; i++)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rs, (__attribute__((address_space(3))) void *)dst, 16, poff[c] + sboff, 0, 0,
-                2 /* nontemporal */);
-        }
+                ok ? rs : rnull, (__attribute__((address_space(3))) void *)(dst + 1024 * i), 16,
+                poff[i], ok ? SBB * s : 0, 0, 2 /* nontemporal */);
     };
-    if (nw > 0) copy_sb(0, 0);
-    f16x8 ring[4][4]; // x operands of four sub-blocks: [sub-block & 3][2*tp + hl]
-    for (int i = 0; i < nmax; i++) {
-        __builtin_amdgcn_s_waitcnt(WAIT_VM0); // this wave's part of super-block i has landed
-        __syncthreads(); // and the partner's; the other slot's super-block is read
-        if (i + 1 < nw) copy_sb(i + 1, (i + 1) & 1);
-        if (i == 0 && nw > 0) {
-            // first PF sub-blocks of the wave's first super-block
-            const uint8_t *xf0 = xs + ((int64_t)T * nsb + kq) * 64 * 1024 + lane * 16;
+
+    f32x16 acc[2][2];
 #pragma unroll
-            for (int g = 0; g < PF; g++)
+    for (int a = 0; a < 2; a++)
 #pragma unroll
-                for (int f = 0; f < 4; f++)
-                    ring[g][f] = __builtin_bit_cast(
-                        f16x8, ldc(xf0 + ((8 * g + 4 * (f >> 1) + 2 * th + (f & 1)) << 10)));
+        for (int b = 0; b < 2; b++)
+#pragma unroll
+            for (int r = 0; r < 16; r++) acc[a][b][r] = 0.f;
+
+    // This wave's super-blocks: wave, wave + KW, ...; the next one's bytes
+    // are copied into the other slot while one is decoded. A operands of
+    // K-step j of super-block s sit at xw + 65536 s + 4096 j + 1024 (2 tt + h);
+    // they are loaded PF K-steps ahead (into the next super-block at the end
+    // of one), the loads pinned there against the scheduler, which would
+    // otherwise sink them next to their MFMAs.
+    const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(xs + (size_t)T * nsb * 65536), (short)0, nsb * 65536, 0x00020000);
+    const __amdgpu_buffer_rsrc_t sr = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(sm + (size_t)T * nsb * 2048), (short)0, nsb * 2048, 0x00020000);
+    f16x8 ring[RING][2][2];
+    auto load_a = [&](int s, int j, int bi) {
+        const bool ok = s >= 0;
+#pragma unroll
+        for (int a = 0; a < 4; a++)
+            ring[bi][a >> 1][a & 1] = __builtin_bit_cast(
+                f16x8, __builtin_amdgcn_raw_buffer_load_b128(ok ? xr : rnull, lane * 16,
+                                                             ok ? s * 65536 + 4096 * j + 1024 * a : 0, 0));
+    };
+    {
+        const int s0 = wave < nsb ? wave : -1;
+        copy_sb(s0, slot0[wave]);
+#pragma unroll
+        for (int j = 0; j < PF; j++) load_a(s0, j, j);
+    }
+    auto super_block = [&](int s, const uint8_t *cur_slot, uint8_t *nxt) {
+        // this super-block's bytes have landed once at most the 4*PF operand
+        // loads issued after its copy are outstanding (loads complete in order)
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(4 * PF) : "memory");
+        const int sn = s + KW < nsb ? s + KW : -1;
+        copy_sb(sn, nxt);
+        // the sub-block sums of x for the min term, needed at the end
+        f16x8 am[2];
+#pragma unroll
+        for (int tt = 0; tt < 2; tt++)
+            am[tt] = __builtin_bit_cast(
+                f16x8, __builtin_amdgcn_raw_buffer_load_b128(sr, lane * 16, s * 2048 + 1024 * tt, 0));
+        const uint8_t *wsb = cur_slot;
+        const uint8_t *wrow[2] = {wsb + nl * SBB, wsb + (nl + 32) * SBB};
+        u32x4 hd[2];
+        float dd[2], dm[2];
+#pragma unroll
+        for (int rt = 0; rt < 2; rt++) {
+            hd[rt] = *(const u32x4 *)wrow[rt];
+            dd[rt] = h2f(hd[rt][0]);
+            dm[rt] = h2f(hd[rt][0] >> 16);
         }
-        if (i < nw) {
-            const int s = kq + KQ * i;
-            const int64_t ts = (int64_t)T * nsb + s;
-            const uint8_t *xf = xs + ts * 64 * 1024 + lane * 16 + (2 * th << 10);
-            const uint8_t *xfn =
-                i + 1 < nw ? xf + (int64_t)KQ * 64 * 1024 : xf; // next super-block
-            const uint8_t *wsb = wl + (i & 1) * (TN * SBB);
-            const uint8_t *wrow[2] = {wsb + nl * SBB, wsb + (nl + 32) * SBB};
-
-            // block scales of the lane's two rows
-            float dd[2], dm[2];
-            uint32_t scg[2][8];
-            f16x8 mins[2];
+        f32x16 tile[2][2];
 #pragma unroll
-            for (int rb = 0; rb < 2; rb++) {
-                const u32x4 hd = *(const u32x4 *)wrow[rb];
-                dd[rb] = h2f(hd[0]);
-                dm[rb] = h2f(hd[0] >> 16);
+        for (int g = 0; g < 8; g++) {
+            const int c = g >> 1, hn = g & 1;
+            u32x4 q[2];
+            f16x2 sc2[2], off2[2];
 #pragma unroll
-                for (int g = 0; g < 8; g++) {
-                    uint32_t sc, mn;
-                    if (g < 4) {
-                        sc = scb(hd, g) & 63u;
-                        mn = scb(hd, g + 4) & 63u;
-                    } else {
-                        sc = (scb(hd, g + 4) & 15u) | ((scb(hd, g - 4) >> 6) << 4);
-                        mn = (scb(hd, g + 4) >> 4) | ((scb(hd, g) >> 6) << 4);
-                    }
-                    scg[rb][g] = sc;
-                    mins[rb][g] = (_Float16)(float)mn;
-                }
+            for (int rt = 0; rt < 2; rt++) {
+                q[rt] = *(const u32x4 *)(wrow[rt] + 16 + 32 * c + 16 * kh);
+                uint32_t sc, mn;
+                scale_min(hd[rt], g, sc, mn);
+                const float scf = (float)sc;
+                const _Float16 sch = (_Float16)(hn ? scf * 0.0625f : scf);
+                const _Float16 off = (_Float16)(hn ? -64.f * scf : -1024.f * scf);
+                sc2[rt] = f16x2{sch, sch};
+                off2[rt] = f16x2{off, off};
             }
-
-            f32x16 tile[2];
 #pragma unroll
-            for (int b = 0; b < 2; b++)
+            for (int j2 = 0; j2 < 2; j2++) {
+                const int j = 2 * g + j2;
+                const int cur = j % RING;
+                // operands PF K-steps ahead, into the next super-block at the end
+                if (j + PF < 16)
+                    load_a(s, j + PF, (j + PF) % RING);
+                else
+                    load_a(sn, j + PF - 16, (j + PF) % RING);
+                __builtin_amdgcn_sched_barrier(0x0386); // VALU, SALU and LDS may cross
+                f16x8 b[2];
 #pragma unroll
-                for (int e = 0; e < 16; e++) tile[b][e] = 0.f;
-            // A operands: fragment (g, tp, tb, hl) at KB 8g + 4tp + 2tb + hl. A
-            // ring of four sub-blocks keeps the loads PF sub-blocks ahead,
-            // running into the wave's next super-block.
+                for (int rt = 0; rt < 2; rt++)
+                    b[rt] = codes_b(q[rt][2 * j2], q[rt][2 * j2 + 1], hn ? mhi : mlo, sc2[rt],
+                                    off2[rt]);
+                // hi for all four tiles, then lo: no accumulator is reused back to back
+#pragma unroll
+                for (int h = 0; h < 2; h++)
+#pragma unroll
+                    for (int tt = 0; tt < 2; tt++)
+#pragma unroll
+                        for (int rt = 0; rt < 2; rt++)
+                            tile[tt][rt] = mfma(ring[cur][tt][h], b[rt],
+                                                (j == 0 && h == 0) ? f32x16{} : tile[tt][rt]);
+            }
+        }
+        // acc += d * tile - 32 * dmin * (sum_g m_g * sum_g(x) / 32)
+        f16x8 mins[2];
+#pragma unroll
+        for (int rt = 0; rt < 2; rt++)
 #pragma unroll
             for (int g = 0; g < 8; g++) {
-                const int c = g >> 1, h = g & 1, cb = g & 3;
-                {
-                    const int gn = g + PF, nb = gn & 3;
-                    const uint8_t *src = gn < 8 ? xf + ((8 * gn) << 10) : xfn + ((8 * (gn - 8)) << 10);
-#pragma unroll
-                    for (int f = 0; f < 4; f++)
-                        ring[nb][f] = __builtin_bit_cast(
-                            f16x8, ldc(src + ((4 * (f >> 1) + (f & 1)) << 10)));
-                }
-#pragma unroll
-                for (int rb = 0; rb < 2; rb++) {
-                    const u32x4 q = *(const u32x4 *)(wrow[rb] + 16 + 32 * c + 16 * jh);
-                    const float scf = (float)scg[rb][g];
-                    const _Float16 sch = (_Float16)(h ? scf * 0.0625f : scf);
-                    const _Float16 off = (_Float16)(h ? -64.f * scf : -1024.f * scf);
-                    const f16x2 sc2 = {sch, sch}, off2 = {off, off};
-                    const uint32_t mask = h ? cm.hi : cm.lo;
-#pragma unroll
-                    for (int tp = 0; tp < 2; tp++) {
-                        const f16x8 b = codes_b(q, tp, mask, sc2, off2);
-                        tile[rb] = mfma(ring[cb][2 * tp], b, tile[rb]);
-                        tile[rb] = mfma(ring[cb][2 * tp + 1], b, tile[rb]);
-                    }
-                }
-                // keep the loads ahead of this sub-block's work
-                __builtin_amdgcn_sched_barrier(0);
+                uint32_t sc, mn;
+                scale_min(hd[rt], g, sc, mn);
+                mins[rt][g] = (_Float16)(float)mn;
             }
-            // y += d*p*tile - 32*dmin*p*(sum_g m_g * sum_g(x)/32), p per token (D row)
-            const f16x8 am = __builtin_bit_cast(
-                f16x8, ldc(sm + (ts * 2 + th) * 64 * 16 + (size_t)lane * 16));
-            f32x4 pv[4];
 #pragma unroll
-            for (int qd = 0; qd < 4; qd++)
-                pv[qd] = *(const f32x4 *)(ps + ts * TM + 32 * th + 8 * qd + 4 * jh);
+        for (int tt = 0; tt < 2; tt++) {
 #pragma unroll
-            for (int rb = 0; rb < 2; rb++) {
-                const f32x16 mt = mfma(am, mins[rb], f32x16{});
+            for (int rt = 0; rt < 2; rt++) {
+                const f32x16 mt = mfma(am[tt], mins[rt], f32x16{});
+                const float md = -32.f * dm[rt];
 #pragma unroll
-                for (int e = 0; e < 16; e++) {
-                    const float p = pv[e >> 2][e & 3];
-                    acc[rb][e] = fmaf(dd[rb] * p, tile[rb][e], acc[rb][e]);
-                    acc[rb][e] = fmaf(-32.f * dm[rb] * p, mt[e], acc[rb][e]);
-                }
+                for (int e = 0; e < 16; e++)
+                    acc[tt][rt][e] = fmaf(md, mt[e], fmaf(dd[rt], tile[tt][rt][e], acc[tt][rt][e]));
             }
         }
+        };
+    // pairs of super-blocks, then an odd last one: no branch inside the loop
+    // body, so that the compiler's wait counts hold across its iterations
+    int s = wave;
+    for (; s + KW < nsb; s += 2 * KW) {
+        super_block(s, slot0[wave], slot1[wave]);
+        super_block(s + KW, slot1[wave], slot0[wave]);
     }
+    if (s < nsb) super_block(s, slot0[wave], slot1[wave]);
 
-    // Sum the partial tiles of the quarters in order, then store.
-    __syncthreads(); // every wave is done with the staged weights
+    // Sum the four waves' partial tiles in wave order, scale by p, store.
+    __syncthreads(); // every wave is done with its staged bytes
+    // (waves 0-1 write into the first array, 2-3 into the second)
+    float *red0 = (float *)&slot0[0][0], *red1 = (float *)&slot1[0][0];
+    float *mine = (wave < KW / 2 ? red0 : red1) + (size_t)(wave % (KW / 2)) * TM * TN;
 #pragma unroll
-    for (int rb = 0; rb < 2; rb++)
+    for (int tt = 0; tt < 2; tt++)
 #pragma unroll
-        for (int r = 0; r < 16; r++) {
-            const int mm = 32 * th + 8 * (r >> 2) + 4 * jh + (r & 3);
-            red[(kq * TM + mm) * TN + 32 * rb + nl] = acc[rb][r];
-        }
+        for (int rt = 0; rt < 2; rt++)
+#pragma unroll
+            for (int r = 0; r < 16; r++)
+                mine[((tt * 2 + rt) * 16 + r) * 64 + lane] = acc[tt][rt][r];
     __syncthreads();
-    for (int i = tid; i < TM * TN; i += NT) {
-        float v = red[i];
+    // Thread tid takes outputs o = tid + 256 i; the 16 exponents (every padded
+    // token has one) and, when accumulating, the old values are all loaded
+    // before any store.
+    constexpr int PER = TM * TN / NT;
+    int ex[PER];
+    float old[PER];
 #pragma unroll
-        for (int q = 1; q < KQ; q++) v += red[q * TM * TN + i];
-        const int64_t t = t0 + i / TN, j = r0 + i % TN;
-        if (t < m && j < j_end) {
-            float *dst = y + t * n + j;
-            *dst = accumulate ? *dst + v : v;
-        }
+    for (int i = 0; i < PER; i++) {
+        const int o = tid + NT * i;
+        const int ln = o & 63, r = (o >> 6) & 15, rt = (o >> 10) & 1, tt = o >> 11;
+        const int tok = 32 * tt + 8 * (r >> 2) + 4 * (ln >> 5) + (r & 3);
+        const int row = 32 * rt + (ln & 31);
+        const int64_t t = T * TM + tok;
+        ex[i] = pe[t];
+        old[i] = (accumulate && t < m && row < rows) ? y[t * n + r0 + row] : 0.f;
+    }
+#pragma unroll
+    for (int i = 0; i < PER; i++) {
+        const int o = tid + NT * i;
+        float v = red0[o];
+#pragma unroll
+        for (int w = 1; w < KW; w++)
+            v += (w < KW / 2 ? red0 : red1)[(w % (KW / 2)) * TM * TN + o];
+        const int ln = o & 63, r = (o >> 6) & 15, rt = (o >> 10) & 1, tt = o >> 11;
+        const int tok = 32 * tt + 8 * (r >> 2) + 4 * (ln >> 5) + (r & 3);
+        const int row = 32 * rt + (ln & 31);
+        const int64_t t = T * TM + tok;
+        if (t < m && row < rows) y[t * n + r0 + row] = old[i] + ldexpf(v, ex[i]);
     }
 }
 
@@ -421,43 +456,48 @@ bool plan_mfma(int fmt, int64_t k, int64_t rows, int64_t m, int num_cu, MfmaPlan
     if (fmt != FMT_Q4_K || k <= 0 || (k % 256) != 0 || m < 1) return false;
     // the staging copy addresses a 64-row tile with 32-bit offsets
     if ((k / 256) * SBB * TN >= ((int64_t)1 << 31)) return false;
+    // and a token tile's staged x (64 KB per super-block) with 32-bit offsets
+    if ((k / 256) * 65536 >= ((int64_t)1 << 31)) return false;
     if (p) {
         p->fmt = fmt;
         p->tiles_n = (int)((rows + TN - 1) / TN);
         p->tiles_m = (int)((m + TM - 1) / TM);
         p->grid = p->tiles_n * p->tiles_m;
-        p->lds_bytes = LDS_BYTES;
+        p->lds_bytes = (size_t)2 * KW * SLOT;
         (void)num_cu;
     }
     return true;
 }
 
+size_t mfma_scratch_bytes(const MfmaPlan &p, int64_t k) {
+    const int64_t nsb = k / 256;
+    return xs_bytes(p.tiles_m, nsb) + sm_bytes(p.tiles_m, nsb) + pe_bytes(p.tiles_m);
+}
+
+hipError_t launch_mfma_ws(const MfmaPlan &p, const uint8_t *W, const float *x, float *y,
+                          int64_t k, int64_t n, int64_t m, int64_t row_bytes, int64_t j_start,
+                          int64_t j_end, int accumulate, void *scratch, hipStream_t stream) {
+    if (p.fmt != FMT_Q4_K) return hipErrorInvalidValue;
+    const int64_t nsb = k / 256;
+    if (p.tiles_m > 65535 || (int64_t)p.tiles_m * TM > 0x7fffffff) return hipErrorInvalidConfiguration;
+    uint8_t *xs = (uint8_t *)scratch, *sm = xs + xs_bytes(p.tiles_m, nsb);
+    int *pe = (int *)(sm + sm_bytes(p.tiles_m, nsb));
+    hipLaunchKernelGGL(qmv_mfma_prep_x, dim3((unsigned)((nsb + 1) / 2), (unsigned)(p.tiles_m * TM)),
+                       dim3(64), 0, stream, x, k, m, xs, sm, pe);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(qmv_mfma_q4_k, dim3(p.tiles_n, p.tiles_m), dim3(NT), 0, stream, W,
+                       xs, sm, pe, y, k, n, m, row_bytes, j_start, j_end, accumulate);
+    return hipGetLastError();
+}
+
 hipError_t launch_mfma(const MfmaPlan &p, const uint8_t *W, const float *x, float *y, int64_t k,
                        int64_t n, int64_t m, int64_t row_bytes, int64_t j_start, int64_t j_end,
                        int accumulate, hipStream_t stream) {
-    if (p.fmt != FMT_Q4_K) return hipErrorInvalidValue;
-    const int64_t nsb = k / 256;
-    if (p.tiles_m > 65535 || nsb > 0x7fffffff) return hipErrorInvalidConfiguration;
-    static const hipError_t attr =
-        hipFuncSetAttribute((const void *)qmv_mfma_q4_k,
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)LDS_BYTES);
-    if (attr != hipSuccess) return attr;
-    const size_t bx = xs_bytes(p.tiles_m, nsb), bs = sm_bytes(p.tiles_m, nsb),
-                 bp = ps_bytes(p.tiles_m, nsb);
     void *buf = nullptr;
-    hipError_t e = hipMallocAsync(&buf, bx + bs + bp, stream);
+    hipError_t e = hipMallocAsync(&buf, mfma_scratch_bytes(p, k), stream);
     if (e != hipSuccess) return e;
-    uint8_t *xs = (uint8_t *)buf, *sm = xs + bx;
-    float *ps = (float *)(sm + bs);
-    hipLaunchKernelGGL(qmv_mfma_prep_x, dim3((unsigned)nsb, p.tiles_m, TM / 4), dim3(64), 0, stream,
-                       x, k, m, xs, sm, ps);
-    e = hipGetLastError();
-    if (e == hipSuccess) {
-        hipLaunchKernelGGL(qmv_mfma_q4_k, dim3(p.tiles_n, p.tiles_m), dim3(NT), LDS_BYTES,
-                           stream, W, xs, sm, ps, y, k, n, m, row_bytes, j_start, j_end,
-                           accumulate);
-        e = hipGetLastError();
-    }
+    e = launch_mfma_ws(p, W, x, y, k, n, m, row_bytes, j_start, j_end, accumulate, buf, stream);
     const hipError_t f = hipFreeAsync(buf, stream);
     return e != hipSuccess ? e : f;
 }
