@@ -60,6 +60,8 @@ def load(path: str | None = None):
         lib.qmv_run.restype = ci
         lib.qmv_run_ex.argtypes = run_args + [ci]
         lib.qmv_run_ex.restype = ci
+        lib.qmv_run_noalloc.argtypes = run_args + [ci]
+        lib.qmv_run_noalloc.restype = ci
         lib.qmv_weight_bytes.argtypes = [ci, i64, i64]
         lib.qmv_weight_bytes.restype = i64
         lib.qmv_last_error.argtypes = []
@@ -112,6 +114,13 @@ def qmv_run_ex(format: int, W: int, x: int, y: int, k: int, n: int, m_tokens: in
                algo: int) -> int:
     return int(load().qmv_run_ex(format, W, x, y, k, n, m_tokens, j_start, j_end, accumulate,
                                  stream, algo))
+
+
+def qmv_run_noalloc(format: int, W: int, x: int, y: int, k: int, n: int, m_tokens: int,
+                    j_start: int, j_end: int, accumulate: int, stream: int,
+                    algo: int = QMV_ALGO_AUTO) -> int:
+    return int(load().qmv_run_noalloc(format, W, x, y, k, n, m_tokens, j_start, j_end,
+                                      accumulate, stream, algo))
 
 
 def qmv_run_t(format: int, W: int, dy: int, dx: int, k: int, n: int, m_tokens: int,

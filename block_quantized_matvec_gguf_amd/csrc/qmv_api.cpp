@@ -2,7 +2,11 @@
 // argument validation (rullama 0.5.0, src/backend/matmul.rs, the checks at the
 // top of each matmul_* function: block-multiple k, even k for the 16-bit
 // formats, the expected weight byte count), kernel selection and launch on the
-// caller's stream. Nothing here synchronises or allocates device memory.
+// caller's stream. Nothing here synchronises. Of the launches it calls, two
+// take stream-ordered scratch (hipMallocAsync / hipFreeAsync on the caller's
+// stream): the matrix-core prefill (qmv_mfma.hip) and the streaming transposed
+// product (qmv_gemv_t.hip); qmv_run_noalloc gives the first a fixed
+// per-device buffer instead. Everything else allocates nothing.
 #include "qmv.h"
 #include "qmv_internal.h"
 
@@ -16,11 +20,15 @@
 #include <string>
 #include <vector>
 
+static_assert(QMV_NOALLOC_SCRATCH_BYTES == qmv::STATIC_SCRATCH_BYTES,
+              "the header states the size of the fixed scratch");
+
 namespace {
 
 struct DevInfo {
     bool gfx950;
     int num_cu;
+    void *scratch; // this device's copy of the fixed scratch (qmv_run_noalloc)
 };
 
 std::mutex g_mu;
@@ -138,6 +146,14 @@ int qmv_create(void) {
         any = any || devs[d].gfx950;
     }
     if (!any) return fail(QMV_ERR_UNSUPPORTED_ARCH, "qmv_create: no gfx950 device visible");
+    for (int d = 0; d < count; d++) {
+        devs[d].scratch = nullptr;
+        if (!devs[d].gfx950) continue;
+        e = qmv::static_scratch_init(d, &devs[d].scratch);
+        if (e != hipSuccess)
+            return fail(QMV_ERR_HIP, "qmv_create: scratch address on device %d: %s", d,
+                        hipGetErrorString(e));
+    }
     g_dev = devs;
     g_refs = 1;
     return QMV_OK;
@@ -205,9 +221,16 @@ int qmv_gemv_geometry(int format, int64_t k, int64_t rows, int64_t m_tokens, int
     return QMV_OK;
 }
 
-int qmv_run_ex(int format, const void *W, const float *x, float *y, int64_t k, int64_t n,
-               int64_t m_tokens, int64_t j_start, int64_t j_end, int accumulate, void *stream,
-               int algo) {
+} // extern "C"
+
+namespace {
+
+// qmv_run_ex and qmv_run_noalloc: the same validation and kernels; with
+// fixed_scratch the matrix-core staging goes to the device's fixed scratch
+// instead of stream-ordered memory.
+int run_impl(int format, const void *W, const float *x, float *y, int64_t k, int64_t n,
+             int64_t m_tokens, int64_t j_start, int64_t j_end, int accumulate, void *stream,
+             int algo, bool fixed_scratch) {
     t_err.clear();
     // ---- host-side validation: nothing is enqueued on failure
     const int64_t qk = block_elems(format);
@@ -276,7 +299,20 @@ int qmv_run_ex(int format, const void *W, const float *x, float *y, int64_t k, i
         qmv::MfmaPlan p;
         if (!qmv::plan_mfma(format, k, rows, m_tokens, num_cu, &p))
             return fail(QMV_ERR_UNSUPPORTED, "mfma plan failed");
-        e = qmv::launch_mfma(p, Wb, x, y, k, n, m_tokens, rb, j_start, j_end, accumulate, s);
+        if (fixed_scratch) {
+            const size_t need = qmv::mfma_scratch_bytes(p, k);
+            if (need > qmv::STATIC_SCRATCH_BYTES)
+                return fail(QMV_ERR_UNSUPPORTED,
+                            "qmv_run_noalloc: the matrix-core path needs %zu bytes of scratch "
+                            "for m=%lld k=%lld, above the fixed %zu",
+                            need, (long long)m_tokens, (long long)k, qmv::STATIC_SCRATCH_BYTES);
+            void *ws = g_dev[(size_t)dev].scratch;
+            if (!ws) return fail(QMV_ERR_NOT_INITIALIZED, "no fixed scratch on device %d", dev);
+            e = qmv::launch_mfma_ws(p, Wb, x, y, k, n, m_tokens, rb, j_start, j_end, accumulate,
+                                    ws, s);
+        } else {
+            e = qmv::launch_mfma(p, Wb, x, y, k, n, m_tokens, rb, j_start, j_end, accumulate, s);
+        }
         if (e != hipSuccess) return fail(QMV_ERR_HIP, "mfma launch: %s", hipGetErrorString(e));
         return QMV_OK;
     }
@@ -292,6 +328,24 @@ int qmv_run_ex(int format, const void *W, const float *x, float *y, int64_t k, i
         t0 += p.MT;
     }
     return QMV_OK;
+}
+
+} // namespace
+
+extern "C" {
+
+int qmv_run_ex(int format, const void *W, const float *x, float *y, int64_t k, int64_t n,
+               int64_t m_tokens, int64_t j_start, int64_t j_end, int accumulate, void *stream,
+               int algo) {
+    return run_impl(format, W, x, y, k, n, m_tokens, j_start, j_end, accumulate, stream, algo,
+                    false);
+}
+
+int qmv_run_noalloc(int format, const void *W, const float *x, float *y, int64_t k, int64_t n,
+                    int64_t m_tokens, int64_t j_start, int64_t j_end, int accumulate,
+                    void *stream, int algo) {
+    return run_impl(format, W, x, y, k, n, m_tokens, j_start, j_end, accumulate, stream, algo,
+                    true);
 }
 
 int qmv_run(int format, const void *W, const float *x, float *y, int64_t k, int64_t n,

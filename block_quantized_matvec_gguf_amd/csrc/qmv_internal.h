@@ -119,4 +119,10 @@ hipError_t launch_mfma_ws(const MfmaPlan &p, const uint8_t *W, const float *x, f
                           int64_t k, int64_t n, int64_t m, int64_t row_bytes, int64_t j_start,
                           int64_t j_end, int accumulate, void *scratch, hipStream_t stream);
 
+// Bytes of the fixed per-device scratch of qmv_run_noalloc, and its set-up:
+// *ptr becomes the device address of `device`'s copy, looked up with that
+// device current (the caller's current device is restored afterwards).
+constexpr size_t STATIC_SCRATCH_BYTES = (size_t)16 << 20;
+hipError_t static_scratch_init(int device, void **ptr);
+
 } // namespace qmv

@@ -502,6 +502,25 @@ hipError_t launch_mfma(const MfmaPlan &p, const uint8_t *W, const float *x, floa
     return e != hipSuccess ? e : f;
 }
 
+// Fixed scratch for callers that cannot allocate (qmv_run_noalloc): one copy
+// in every device's memory, held until the process ends. Host code never
+// passes `scratch` itself (its host-side name is no device address): set-up
+// looks up each device's copy with hipGetSymbolAddress and the launches take
+// that address.
+static __device__ __align__(256) uint8_t scratch[STATIC_SCRATCH_BYTES];
+
+hipError_t static_scratch_init(int device, void **ptr) {
+    *ptr = nullptr;
+    int cur = 0;
+    hipError_t e = hipGetDevice(&cur);
+    if (e != hipSuccess) return e;
+    e = hipSetDevice(device);
+    if (e == hipSuccess) e = hipGetSymbolAddress(ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) *ptr = nullptr;
+    const hipError_t r = hipSetDevice(cur);
+    return e != hipSuccess ? e : r;
+}
+
 const char *mfma_kernel_name(const MfmaPlan &p) {
     return p.fmt == FMT_Q4_K ? "qmv_mfma<q4_k>" : "";
 }

@@ -23,7 +23,9 @@
  * All pointers are device pointers (memory from hipMalloc or a torch CUDA
  * tensor) unless stated. The caller owns every buffer; the library keeps no
  * pointer after a call returns. The GEMV and per-row families allocate no
- * memory; the matrix-core family takes stream-ordered scratch (qmv_run_ex).
+ * memory; the matrix-core family (qmv_run_ex) and the streaming transposed
+ * family (qmv_run_t_ex) take stream-ordered scratch; qmv_run_noalloc runs the
+ * forward families with no allocation at all.
  */
 #ifndef QMV_H
 #define QMV_H
@@ -120,6 +122,22 @@ int qmv_run(int format, const void *W, const float *x, float *y, int64_t k, int6
 int qmv_run_ex(int format, const void *W, const float *x, float *y, int64_t k, int64_t n,
                int64_t m_tokens, int64_t j_start, int64_t j_end, int accumulate,
                void *stream, int algo);
+
+/* qmv_run_ex that allocates nothing, for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc. Same arguments, validation, kernels and results (bit for
+ * bit) as qmv_run_ex. The one family that needs scratch, QMV_ALGO_MFMA, uses a
+ * fixed buffer of QMV_NOALLOC_SCRATCH_BYTES in each device's memory, set up by
+ * qmv_create and held until the process ends; a call whose staging would need
+ * more (about m_tokens*k*4.2 bytes, m_tokens rounded up to 64) fails with
+ * QMV_ERR_UNSUPPORTED before anything is enqueued. Every call on a device
+ * shares that device's buffer and leaves its contents behind (each call
+ * rewrites all it reads): matrix-core calls that overlap in time on one
+ * device, e.g. on two streams, race and give wrong results. */
+#define QMV_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+int qmv_run_noalloc(int format, const void *W, const float *x, float *y, int64_t k, int64_t n,
+                    int64_t m_tokens, int64_t j_start, int64_t j_end, int accumulate,
+                    void *stream, int algo);
 
 /* Enqueue the transposed (backward-input) product over a row range on
  * `stream`, kernel family chosen automatically:

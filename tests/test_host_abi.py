@@ -31,7 +31,7 @@ def test_header_declares_the_boundary():
     for need in ("qmv_create", "qmv_run", "qmv_destroy", "qmv_run_ex", "qmv_weight_bytes",
                  "qmv_last_error", "qmv_run_t", "qmv_run_t_ex", "qmv_t_kernel_name",
                  "qmv_run_moe", "qmv_run_moe_ex", "qmv_moe_kernel_name", "qmv_run_affine",
-                 "qmv_affine_kernel_name"):
+                 "qmv_affine_kernel_name", "qmv_run_noalloc"):
         assert need in names
 
 
@@ -196,6 +196,26 @@ def test_argument_errors_are_host_side(lib):
     assert _run(x=0x2002) == qb.QMV_ERR_MISALIGNED
     assert _run(y=0x3001) == qb.QMV_ERR_MISALIGNED
     assert qb.qmv_last_error()
+
+
+def test_noalloc_argument_errors_are_host_side(lib):
+    def run(**kw):
+        a = dict(format=qb.QMV_FMT_Q4_K, W=0x1000, x=0x2000, y=0x3000, k=256, n=8, m_tokens=64,
+                 j_start=0, j_end=8, accumulate=0, stream=None, algo=qb.QMV_ALGO_MFMA)
+        a.update(kw)
+        return qb.qmv_run_noalloc(a["format"], a["W"], a["x"], a["y"], a["k"], a["n"],
+                                  a["m_tokens"], a["j_start"], a["j_end"], a["accumulate"],
+                                  a["stream"], a["algo"])
+    E = qb.QMV_ERR_INVALID_ARGUMENT
+    assert run(format=0) == E
+    assert run(k=300) == E
+    assert run(j_start=5, j_end=4) == E
+    assert run(accumulate=2) == E
+    assert run(algo=7) == E
+    assert run(y=0) == E
+    assert run(W=0x1001) == qb.QMV_ERR_MISALIGNED
+    # valid arguments reach the initialisation check (no device is set up here)
+    assert run() == qb.QMV_ERR_NOT_INITIALIZED
 
 
 def test_run_before_create(lib):
