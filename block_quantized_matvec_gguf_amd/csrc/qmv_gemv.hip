@@ -74,15 +74,17 @@ __device__ __forceinline__ void x_prefetch(const float *x, int nt4, int tid, int
 }
 
 // x into LDS, transposed so that piece i of unit u of token t sits at
-// [t*n4 + i*U + u]: the per-lane reads are then consecutive across lanes.
-template <class F>
+// [t*n4 + i*U + u]: the per-lane reads are then consecutive across lanes. With
+// UNITS the pieces of a unit sit together instead, at [t*n4 + 16u + i] (read
+// one piece per lane by the shared integer-plane pass).
+template <class F, bool UNITS = false>
 __device__ __forceinline__ void x_to_lds(const float *x, f32x4 *xl, int n4, int nt4, int U,
                                          int tid, int T, const f32x4 xa[4]) {
     auto put = [&](int q, f32x4 v) {
         const int t = q / n4, r = q - t * n4;
         int u, i;
         F::x4_slot(r, U, u, i);
-        xl[t * n4 + i * U + u] = v;
+        xl[t * n4 + (UNITS ? 16 * u + i : i * U + u)] = v;
     };
 #pragma unroll
     for (int s = 0; s < 4; s++)
@@ -101,6 +103,21 @@ __device__ __forceinline__ void x_units_from_lds(typename F::X (&xu)[MT][UPL], c
 #pragma unroll
             for (int p = 0; p < 16; p++) F::put_x(xu[t][i], p, xl[t * n4 + p * U + ulod[i]]);
             F::finish_x(xu[t][i]);
+        }
+}
+
+// Integer-plane units: every lane's unit from the workgroup's shared records
+// and planes in LDS.
+template <class F, int MT, int UPL>
+__device__ __forceinline__ void x_units_from_planes(typename F::X (&xu)[MT][UPL], const XRec *rec,
+                                                    const uint32_t *pl, int U,
+                                                    const int (&ulod)[UPL]) {
+#pragma unroll
+    for (int i = 0; i < UPL; i++)
+#pragma unroll
+        for (int t = 0; t < MT; t++) {
+            x_from_planes(xu[t][i], rec, pl, t, ulod[i], U);
+            F::finish_shared(xu[t][i]);
         }
 }
 
@@ -385,10 +402,19 @@ __device__ __forceinline__ void staged_body(const uint8_t *__restrict__ W, int64
     if (XL) x_prefetch(x, nt4, ln.tid, ln.T, xa);
     copy(base, 0); // every workgroup has a first batch: the grid never exceeds the batch count
     f32x4 *xl = (f32x4 *)smem;
-    if (XL) x_to_lds<F>(x, xl, n4, nt4, U, ln.tid, ln.T, xa);
+    if (XL) x_to_lds<F, true>(x, xl, n4, nt4, U, ln.tid, ln.T, xa);
     if (accumulate) yp.stash(ybuf, P, ln.tid, ln.T);
     lds_barrier();
-    if (XL) x_units_from_lds<F, MT, UPL>(xu, xl, n4, U, ln.ulod);
+    if constexpr (XL) {
+        // the units' integer planes, computed once per workgroup after the
+        // reductions' area: [records][plane dwords] (see xplanes_lds_bytes)
+        const size_t pofs = ((size_t)((ybuf + 2 * nq) - smem) * sizeof(float) + 15) & ~(size_t)15;
+        XRec *rec = (XRec *)((uint8_t *)smem + pofs);
+        uint32_t *pl = (uint32_t *)(rec + MT * U);
+        x_shared_planes(xl, rec, pl, U, MT, ln.tid, ln.T);
+        lds_barrier();
+        x_units_from_planes<F, MT, UPL>(xu, rec, pl, U, ln.ulod);
+    }
 
     int cur = 0;
     int64_t prev = -1; // batch whose group sums wait in LDS
@@ -536,6 +562,13 @@ static bool staged_format(int fmt) {
 
 static constexpr size_t LDS_BUDGET = 80 * 1024; // weight buffers + reductions
 
+// LDS for the shared integer planes of the staged (block-format) kernels with
+// x in LDS: 15 bytes of alignment, a 16-byte record and 192 bytes of planes
+// per unit and token.
+static size_t xplanes_lds_bytes(int MT, int U) {
+    return 15 + (size_t)MT * U * (sizeof(XRec) + 192);
+}
+
 bool plan_gemv(int fmt, int64_t k, int64_t rows, int mt_max, int num_cu, GemvPlan *p) {
     if (k <= 0 || k % 64 != 0) return false;
     const int64_t U64 = k / 64;
@@ -640,7 +673,9 @@ bool plan_gemv(int fmt, int64_t k, int64_t rows, int mt_max, int num_cu, GemvPla
     // x goes through LDS when everything fits in 96 KB; otherwise each lane
     // reads its x units straight from global memory
     g.x_in_lds = (xb + wbuf + red <= 96 * 1024) ? 1 : 0;
-    g.lds_bytes = (g.x_in_lds ? xb : (g.staged ? 16 : 0)) + wbuf + red;
+    g.lds_bytes = (g.x_in_lds ? xb + (g.staged ? xplanes_lds_bytes(g.MT, g.U) : 0)
+                              : (g.staged ? 16 : 0)) +
+                  wbuf + red;
     if (g.lds_bytes > 160 * 1024) return false;
     *p = g;
     return true;
@@ -703,7 +738,9 @@ static hipError_t launch_direct_rb(const GemvPlan &p, const uint8_t *W, const fl
 // LDS copy moves 16-byte pieces).
 static bool use_x_lds(GemvPlan &p, const float *x, int64_t k) {
     if (p.x_in_lds && ((uintptr_t)x & 15) == 0) return true;
-    if (p.x_in_lds) p.lds_bytes -= (size_t)k * p.MT * sizeof(float) - (p.staged ? 16 : 0);
+    if (p.x_in_lds)
+        p.lds_bytes -= (size_t)k * p.MT * sizeof(float) +
+                       (p.staged ? xplanes_lds_bytes(p.MT, p.U) : 0) - (p.staged ? 16 : 0);
     p.x_in_lds = 0;
     return false;
 }

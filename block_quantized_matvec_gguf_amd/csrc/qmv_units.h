@@ -107,6 +107,36 @@ struct XI {
     float sum[2];      // Q4_K: f32 sums of pieces 0..7 and 8..15
 };
 
+// Digits of four values at exponent E: X = rint(v * 2^-E) (|X| <= 2^22) as
+// balanced base-256 digits X = x2*65536 + x1*256 + x0, byte b of d[j] being
+// digit j of value b.
+__device__ __forceinline__ void x_digits4(f32x4 v, int E, uint32_t (&d)[3]) {
+    const float f[4] = {v.x, v.y, v.z, v.w};
+    d[0] = d[1] = d[2] = 0u;
+#pragma unroll
+    for (int b = 0; b < 4; b++) {
+        const int X = (int)rintf(ldexpf(f[b], -E));
+        const int x0 = (int)((uint32_t)X << 24) >> 24;
+        const int r = (X - x0) >> 8;
+        const int x1 = (int)((uint32_t)r << 24) >> 24;
+        const int x2 = (r - x1) >> 8; // |x2| <= 65
+        d[0] |= ((uint32_t)x0 & 0xffu) << (8 * b);
+        d[1] |= ((uint32_t)x1 & 0xffu) << (8 * b);
+        d[2] |= ((uint32_t)x2 & 0xffu) << (8 * b);
+    }
+}
+
+// The unit's exponent E = e2 - 22 for max|x| in [2^(e2-1), 2^e2) (0 when all
+// are zero) and format constant 1 (NaN when any value is not finite).
+__device__ __forceinline__ void x_scale(float mx, bool finite, int &E, float &c) {
+    int e2 = 0;
+    if (mx > 0.f) (void)frexpf(mx, &e2);
+    E = e2 - 22;
+    c = finite ? 1.f : __builtin_nanf("");
+}
+
+// The unit's planes, exponent, constant and the f32 sums of values 0..31 and
+// 32..63 (in order), from its 64 values in x.f.
 __device__ __forceinline__ void x_planes(XI &x) {
     float mx = 0.f;
     bool finite = true;
@@ -116,29 +146,88 @@ __device__ __forceinline__ void x_planes(XI &x) {
         finite = finite && (a <= 3.4028235e38f); // false for NaN and infinities
         mx = fmaxf(mx, a);
     }
-    int e2 = 0;
-    if (mx > 0.f) (void)frexpf(mx, &e2); // mx in [2^(e2-1), 2^e2)
-    const int E = e2 - 22;
-    x.e = E;
-    x.c = finite ? 1.f : __builtin_nanf("");
+    x_scale(mx, finite, x.e, x.c);
+    // sums of values 0..31 and 32..63: each piece's four in order, then the
+    // eight piece sums pairwise (the order of the shared pass below)
+    float ps[16];
+#pragma unroll
+    for (int i = 0; i < 16; i++) ps[i] = ((x.f[4 * i] + x.f[4 * i + 1]) + x.f[4 * i + 2]) + x.f[4 * i + 3];
+#pragma unroll
+    for (int h = 0; h < 2; h++) {
+        const float *q = ps + 8 * h;
+        x.sum[h] = ((q[0] + q[1]) + (q[2] + q[3])) + ((q[4] + q[5]) + (q[6] + q[7]));
+    }
 #pragma unroll
     for (int i = 0; i < 16; i++) {
-        uint32_t d0 = 0, d1 = 0, d2 = 0;
-#pragma unroll
-        for (int b = 0; b < 4; b++) {
-            const int X = (int)rintf(ldexpf(x.f[4 * i + b], -E)); // |X| <= 2^22
-            const int x0 = (int)((uint32_t)X << 24) >> 24;        // balanced base-256 digits
-            const int r = (X - x0) >> 8;
-            const int x1 = (int)((uint32_t)r << 24) >> 24;
-            const int x2 = (r - x1) >> 8;                          // |x2| <= 65
-            d0 |= ((uint32_t)x0 & 0xffu) << (8 * b);
-            d1 |= ((uint32_t)x1 & 0xffu) << (8 * b);
-            d2 |= ((uint32_t)x2 & 0xffu) << (8 * b);
-        }
-        x.p[0][i] = d0;
-        x.p[1][i] = d1;
-        x.p[2][i] = d2;
+        uint32_t d[3];
+        x_digits4(f32x4{x.f[4 * i], x.f[4 * i + 1], x.f[4 * i + 2], x.f[4 * i + 3]}, x.e, d);
+        x.p[0][i] = d[0];
+        x.p[1][i] = d[1];
+        x.p[2][i] = d[2];
     }
+}
+
+// The same, computed once per workgroup from x staged in LDS unit by unit
+// (piece i of unit u of token t at xl[(t*U + u)*16 + i]) and shared through
+// LDS: each aligned group of 16 threads (the complete ones; the plans give at
+// least 33 threads) takes one unit at a time, one piece per lane, exchanging
+// maxima and sums by shuffles within the group; its first lane writes the
+// unit's record.
+struct XRec {
+    int e;
+    float c, sum0, sum1;
+};
+// plane dword i of digit d of unit u, token t: pl[(((t*3 + d)*4 + i/4)*U + u)*4 + i%4]
+// (a lane's four consecutive dwords are one 16-byte read; lanes of
+// consecutive units read consecutive 16 bytes)
+__device__ __forceinline__ void x_shared_planes(const f32x4 *xl, XRec *rec, uint32_t *pl, int U,
+                                                int MT, int tid, int T) {
+    const int g16 = tid >> 4, ng = T >> 4, i = tid & 15;
+    if (g16 >= ng) return;
+    for (int q = g16; q < MT * U; q += ng) { // q = t*U + u
+        const f32x4 v = xl[16 * q + i];
+        float mx = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
+        int bad = !(fabsf(v.x) <= 3.4028235e38f && fabsf(v.y) <= 3.4028235e38f &&
+                    fabsf(v.z) <= 3.4028235e38f && fabsf(v.w) <= 3.4028235e38f);
+        float ps = ((v.x + v.y) + v.z) + v.w;
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) {
+            mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+            bad |= __shfl_xor(bad, o, 64);
+            if (o < 8) ps += __shfl_xor(ps, o, 64); // lanes 0-7: pieces 0..7, 8-15: 8..15
+        }
+        const float s1 = __shfl_down(ps, 8, 16);
+        XRec r;
+        x_scale(mx, !bad, r.e, r.c);
+        uint32_t d[3];
+        x_digits4(v, r.e, d);
+        const int t = q / U, u = q - t * U;
+#pragma unroll
+        for (int j = 0; j < 3; j++) pl[(((t * 3 + j) * 4 + (i >> 2)) * U + u) * 4 + (i & 3)] = d[j];
+        if (i == 0) {
+            r.sum0 = ps;
+            r.sum1 = s1;
+            rec[q] = r;
+        }
+    }
+}
+__device__ __forceinline__ void x_from_planes(XI &x, const XRec *rec, const uint32_t *pl, int t,
+                                              int u, int U) {
+    const XRec r = rec[t * U + u];
+    x.e = r.e;
+    x.c = r.c;
+    x.sum[0] = r.sum0;
+    x.sum[1] = r.sum1;
+#pragma unroll
+    for (int j = 0; j < 3; j++)
+#pragma unroll
+        for (int i4 = 0; i4 < 4; i4++) {
+            const u32x4 w = *(const u32x4 *)(pl + (((t * 3 + j) * 4 + i4) * U + u) * 4);
+            x.p[j][4 * i4] = w.x;
+            x.p[j][4 * i4 + 1] = w.y;
+            x.p[j][4 * i4 + 2] = w.z;
+            x.p[j][4 * i4 + 3] = w.w;
+        }
 }
 
 // Sum of the signed digit bytes of plane dwords [i0, i1).
@@ -474,11 +563,6 @@ struct UQ4_K {
     // 128 * sum(x) over the high pieces, which gives 16 * sum q x. The min
     // term dmin * m * sum(x) uses the f32 sums of the two halves.
     static __device__ __forceinline__ void finish_xi(XI &x) {
-        float a = 0.f, b = 0.f;
-        for (int i = 0; i < 32; i++) a += x.f[i];
-        for (int i = 32; i < 64; i++) b += x.f[i];
-        x.sum[0] = a;
-        x.sum[1] = b;
         x.c *= 0.0625f;
 #pragma unroll
         for (int d = 0; d < 3; d++) x.ofs[0][d] = 128 * plane_sum(x, d, 8, 16);
@@ -748,6 +832,8 @@ struct IntX {
         x_planes(x);
         U::finish_xi(x);
     }
+    // after x_from_planes
+    static __device__ __forceinline__ void finish_shared(X &x) { U::finish_xi(x); }
     static __device__ __forceinline__ float dot(const Raw &r, const X &x, int u) {
         return U::dot_i(r, x, u);
     }
