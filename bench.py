@@ -195,6 +195,10 @@ def main():
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain copy of --calib-bytes (counter calibration)")
     ap.add_argument("--calib-bytes", type=int, default=512 * 1024 * 1024)
+    ap.add_argument("--rotate-bytes", type=float, default=1.1e9,
+                    help="bytes of weight copies the steps rotate over (default 1.1 GB: more "
+                         "than the 256 MB last-level cache; counter runs use less, since every "
+                         "copy is one more dispatch under the profiler)")
     ap.add_argument("--summarize-pmc", nargs="*", default=None)
     args = ap.parse_args()
 
@@ -233,7 +237,7 @@ def main():
     tiles = args.tiles if args.tiles is not None else spec.get("tiles", 8)
     algo = qb.ALGOS[args.algo]
     wbytes = W.nbytes
-    copies = max(1, int(np.ceil(1.1e9 / wbytes)))
+    copies = max(1, int(np.ceil(args.rotate_bytes / wbytes)))
     if op_moe:
         E, top_k = spec["experts"], spec["top_k"]
         slab = W.nbytes // E
@@ -244,7 +248,7 @@ def main():
         id_sets = [perm[s_ * top_k * m:(s_ + 1) * top_k * m].astype(np.int32)
                    for s_ in range(nsets)]
         wbytes = len(np.unique(id_sets[0])) * slab       # weight bytes one call reads
-        copies = max(1, int(np.ceil(1.1e9 / (wbytes * nsets))))
+        copies = max(1, int(np.ceil(args.rotate_bytes / (wbytes * nsets))))
     dev = torch.device("cuda:0")
     Wd = [torch.from_numpy(W).to(dev)]
     for _ in range(copies - 1):
