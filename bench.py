@@ -48,8 +48,12 @@ FAMILY_SOURCES = {"gemv": ["block_quantized_matvec_gguf_amd/csrc/qmv_gemv.hip",
                   "simple": ["block_quantized_matvec_gguf_amd/csrc/qmv_simple.hip"]}
 # the dispatches whose counters and durations are the family's (not x staging
 # or the partial-sum reduction)
-MAIN_KERNEL = {"gemv": "qmv_gemv", "gemv_t": "qmv_gemv_t_staged", "mfma": "qmv_mfma_q4_k",
+MAIN_KERNEL = {"gemv": "qmv_gemv", "gemv_t": "qmv_gemv_t_staged", "mfma": "qmv_mfma_",
                "simple": "qmv_simple", "affine": "qmv_affine_gemv"}
+
+
+def is_main_kernel(family: str, name: str) -> bool:
+    return MAIN_KERNEL[family] in name and "prep_x" not in name
 METRIC = "effective weight-read GB/s and % of MI355X HBM peak for quantized GEMV"
 
 
@@ -107,12 +111,11 @@ def summarize_pmc(args):
     fmt_ = spec["bits"] if args.op == "affine" else synth.fmt_id(spec["fmt"])
     family = kernel_family(kernel_name_of(qb, fmt_, spec["k"], spec["m"], qb.ALGOS[args.algo],
                                           args.op))
-    main_kernel = MAIN_KERNEL[family]
     per = {}
     for path in args.summarize_pmc:
         for r in csv.DictReader(open(path)):
             name = r["Kernel_Name"]
-            key = "gemv" if main_kernel in name else ("copy" if "neg_kernel" in name or
+            key = "gemv" if is_main_kernel(family, name) else ("copy" if "neg_kernel" in name or
                                                       ("elementwise" in name and "neg" in name)
                                                       else None)
             if key is None:
@@ -350,13 +353,16 @@ def main():
            "algorithmic_bytes_per_launch": alg_bytes, "launch_us": round(launch_s * 1e6, 3)}
     if kname.startswith("qmv_mfma"):
         # matrix-core kernel: 2*m*k*n algorithmic flops against the dense f16
-        # peak (x enters as two f16 terms, so the units execute twice that)
+        # (bf16) peak; x enters as two terms, and the weights of the scaled
+        # formats as two more (no lo*lo product), so the units execute two or
+        # three times that
         flops = 2.0 * m * k * n
+        terms = 2 if fmt in (synth.F16, synth.BF16, synth.Q4_K) else 3
         tf = flops / launch_s / 1e12
         roofline = {"bound": "mfma", "achieved": round(tf, 2), "peak": MFMA_F16_PEAK_TFS,
                     "unit": "TFLOP/s", "frac": round(tf / MFMA_F16_PEAK_TFS, 4),
                     "traffic": traffic_bytes, "algorithmic_flops_per_launch": flops,
-                    "executed_mfma_flops_per_launch": 2 * flops,
+                    "executed_mfma_flops_per_launch": terms * flops,
                     "launch_us": round(launch_s * 1e6, 3),
                     "hbm": {k_: hbm[k_] for k_ in ("achieved", "peak", "unit", "frac",
                                                    "algorithmic_bytes_per_launch")}}

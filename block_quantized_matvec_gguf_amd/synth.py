@@ -199,6 +199,12 @@ WORKLOADS = {
     "q4_k_vocab": dict(id=11, fmt="q4_k", k=2560, n=262144, m=1, tiles=8),
     "q8_0_vocab": dict(id=12, fmt="q8_0", k=2560, n=262144, m=1, tiles=8),
     "bf16_vocab": dict(id=13, fmt="bf16", k=2560, n=262144, m=1, tiles=8),
+    # the prefill shape in the other formats (matrix-core path)
+    "q6_k_prefill": dict(id=14, fmt="q6_k", k=4096, n=14336, m=64),
+    "q4_0_prefill": dict(id=15, fmt="q4_0", k=4096, n=14336, m=64),
+    "q8_0_prefill": dict(id=16, fmt="q8_0", k=4096, n=14336, m=64),
+    "bf16_prefill": dict(id=17, fmt="bf16", k=4096, n=14336, m=64),
+    "f16_prefill": dict(id=18, fmt="f16", k=4096, n=14336, m=64),
 }
 
 

@@ -76,10 +76,16 @@ def test_kernel_names(lib):
     assert qb.qmv_kernel_name(qb.QMV_FMT_Q4_K, 4096, 64) == "qmv_mfma<q4_k>"
     assert qb.qmv_kernel_name(qb.QMV_FMT_Q4_K, 4096, 15) == "qmv_gemv_staged<q4_k>"
     assert qb.qmv_kernel_name(qb.QMV_FMT_Q4_K, 256, 1, qb.QMV_ALGO_MFMA) == "qmv_mfma<q4_k>"
-    assert qb.qmv_kernel_name(qb.QMV_FMT_BF16, 4096, 64, qb.QMV_ALGO_MFMA) == ""
+    # every format has the matrix-core path for k a multiple of 256
+    for f, name in ((qb.QMV_FMT_BF16, "bf16"), (qb.QMV_FMT_F16, "f16"), (qb.QMV_FMT_Q4_0, "q4_0"),
+                    (qb.QMV_FMT_Q5_0, "q5_0"), (qb.QMV_FMT_Q8_0, "q8_0"),
+                    (qb.QMV_FMT_Q6_K, "q6_k")):
+        assert qb.qmv_kernel_name(f, 4096, 64, qb.QMV_ALGO_MFMA) == "qmv_mfma<%s>" % name
+        assert qb.qmv_kernel_name(f, 2560, 16) == "qmv_mfma<%s>" % name
+    assert qb.qmv_kernel_name(qb.QMV_FMT_BF16, 2496, 64, qb.QMV_ALGO_MFMA) == ""
     assert qb.qmv_kernel_name(qb.QMV_FMT_Q8_0, 2560, 1) == "qmv_gemv_staged<q8_0>"
     assert qb.qmv_kernel_name(qb.QMV_FMT_Q5_0, 2560, 1) == "qmv_gemv_staged<q5_0>"
-    assert qb.qmv_kernel_name(qb.QMV_FMT_Q5_0, 2560, 64) == "qmv_gemv_staged<q5_0>"
+    assert qb.qmv_kernel_name(qb.QMV_FMT_Q5_0, 2560, 15) == "qmv_gemv_staged<q5_0>"
     assert qb.qmv_kernel_name(qb.QMV_FMT_Q8_0, 32, 1) == "qmv_simple"
 
 
