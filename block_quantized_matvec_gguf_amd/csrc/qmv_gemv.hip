@@ -406,14 +406,24 @@ __device__ __forceinline__ void staged_body(const uint8_t *__restrict__ W, int64
     if (accumulate) yp.stash(ybuf, P, ln.tid, ln.T);
     lds_barrier();
     if constexpr (XL) {
-        // the units' integer planes, computed once per workgroup after the
-        // reductions' area: [records][plane dwords] (see xplanes_lds_bytes)
-        const size_t pofs = ((size_t)((ybuf + 2 * nq) - smem) * sizeof(float) + 15) & ~(size_t)15;
-        XRec *rec = (XRec *)((uint8_t *)smem + pofs);
+        // the units' integer planes, computed once per workgroup: [records]
+        // [plane dwords] in weight buffer 1 when they fit there (it is free until
+        // the loop's first copy, which waits for every wave to have read its
+        // planes), else after the reductions' area (see xplanes_lds_bytes)
+        uint8_t *pb;
+        if (xplanes_in_buffer(MT, U, buf_bytes)) {
+            pb = wb + buf_bytes;
+        } else {
+            const size_t pofs =
+                ((size_t)((ybuf + 2 * nq) - smem) * sizeof(float) + 15) & ~(size_t)15;
+            pb = (uint8_t *)smem + pofs;
+        }
+        XRec *rec = (XRec *)pb;
         uint32_t *pl = (uint32_t *)(rec + MT * U);
         x_shared_planes(xl, rec, pl, U, MT, ln.tid, ln.T);
         lds_barrier();
         x_units_from_planes<F, MT, UPL>(xu, rec, pl, U, ln.ulod);
+        lds_barrier();
     }
 
     int cur = 0;
@@ -563,10 +573,11 @@ static bool staged_format(int fmt) {
 static constexpr size_t LDS_BUDGET = 80 * 1024; // weight buffers + reductions
 
 // LDS for the shared integer planes of the staged (block-format) kernels with
-// x in LDS: 15 bytes of alignment, a 16-byte record and 192 bytes of planes
-// per unit and token.
-static size_t xplanes_lds_bytes(int MT, int U) {
-    return 15 + (size_t)MT * U * (sizeof(XRec) + 192);
+// x in LDS: a 16-byte record and 192 bytes of planes per unit and token, in
+// weight buffer 1 when they fit there, else in 15 bytes of alignment plus
+// that much more.
+static size_t xplanes_lds_bytes(int MT, int U, int buf_bytes) {
+    return xplanes_in_buffer(MT, U, buf_bytes) ? 0 : 15 + (size_t)MT * U * (sizeof(XRec) + 192);
 }
 
 bool plan_gemv(int fmt, int64_t k, int64_t rows, int mt_max, int num_cu, GemvPlan *p) {
@@ -673,7 +684,7 @@ bool plan_gemv(int fmt, int64_t k, int64_t rows, int mt_max, int num_cu, GemvPla
     // x goes through LDS when everything fits in 96 KB; otherwise each lane
     // reads its x units straight from global memory
     g.x_in_lds = (xb + wbuf + red <= 96 * 1024) ? 1 : 0;
-    g.lds_bytes = (g.x_in_lds ? xb + (g.staged ? xplanes_lds_bytes(g.MT, g.U) : 0)
+    g.lds_bytes = (g.x_in_lds ? xb + (g.staged ? xplanes_lds_bytes(g.MT, g.U, g.buf_bytes) : 0)
                               : (g.staged ? 16 : 0)) +
                   wbuf + red;
     if (g.lds_bytes > 160 * 1024) return false;
@@ -740,7 +751,8 @@ static bool use_x_lds(GemvPlan &p, const float *x, int64_t k) {
     if (p.x_in_lds && ((uintptr_t)x & 15) == 0) return true;
     if (p.x_in_lds)
         p.lds_bytes -= (size_t)k * p.MT * sizeof(float) +
-                       (p.staged ? xplanes_lds_bytes(p.MT, p.U) : 0) - (p.staged ? 16 : 0);
+                       (p.staged ? xplanes_lds_bytes(p.MT, p.U, p.buf_bytes) : 0) -
+                       (p.staged ? 16 : 0);
     p.x_in_lds = 0;
     return false;
 }

@@ -211,6 +211,10 @@ __device__ __forceinline__ void x_shared_planes(const f32x4 *xl, XRec *rec, uint
         }
     }
 }
+// Whether a workgroup's records and planes fit in one weight buffer.
+__host__ __device__ constexpr bool xplanes_in_buffer(int MT, int U, int buf_bytes) {
+    return (long long)MT * U * (sizeof(XRec) + 192) <= (long long)buf_bytes;
+}
 __device__ __forceinline__ void x_from_planes(XI &x, const XRec *rec, const uint32_t *pl, int t,
                                               int u, int U) {
     const XRec r = rec[t * U + u];
