@@ -48,11 +48,6 @@ namespace qmv {
 
 // Sum over aligned groups of G lanes (G a power of two <= 16); every lane of
 // a group ends with the group sum. Order of additions is fixed.
-template <int CTRL>
-__device__ __forceinline__ float dpp_mov(float v) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
-                                         0, __builtin_bit_cast(int, v), CTRL, 0xf, 0xf, false));
-}
 __device__ __forceinline__ float group_sum(float v, int G) {
     if (G >= 2) v += dpp_mov<0xb1>(v);  // quad_perm [1,0,3,2]
     if (G >= 4) v += dpp_mov<0x4e>(v);  // quad_perm [2,3,0,1]
@@ -325,6 +320,13 @@ __device__ __forceinline__ void direct_body(const uint8_t *__restrict__ W,
 }
 
 // ------------------------------------------------------- staged kernel
+// LDS of the staged kernel: [x part][buffer 0][buffer 1][2 x nq*(NG+1) floats
+// of group sums and old y][sink]; the x part and the buffers are multiples of
+// 16 bytes, the sink starts at the next multiple of 16.
+constexpr int STAGED_SINK_BYTES = 1024;
+__host__ __device__ constexpr int staged_sink_offset(int x_part, int buf_bytes, int nq_ng1) {
+    return (x_part + 2 * buf_bytes + 2 * nq_ng1 * 4 + 15) & ~15;
+}
 // Block formats. The byte range of a batch, [base*row_bytes,
 // end*row_bytes), is copied in 16-byte pieces aligned down to 16 bytes of
 // the 16-byte aligned base pointer (so
@@ -337,8 +339,11 @@ __device__ __forceinline__ void direct_body(const uint8_t *__restrict__ W,
 // it. The batch start is the scalar base of a buffer descriptor sized to the
 // batch; lanes whose piece lies past the batch issue no copy (the
 // descriptor's range check is a second guard), so a buffer holds exactly the
-// largest batch. The copy of batch i+1 runs while batch i is decoded and is
-// waited for at the end-of-batch barrier. XL: x goes through LDS.
+// largest batch. Batches 0 and 1 are copied at the start, both buffers at
+// once; afterwards the copy of batch i+1 runs while batch i is decoded and is
+// waited for at the end-of-batch barrier. XL: the units' records and integer
+// planes are shared through LDS (else each lane converts its own from global
+// memory).
 
 // Single-token, one-row-per-slot instances fit in 128 registers without
 // spilling, i.e. 4 waves per SIMD; the others are left to the compiler.
@@ -354,83 +359,114 @@ __device__ __forceinline__ void staged_body(const uint8_t *__restrict__ W, int64
                                             const float *__restrict__ x, float *__restrict__ y,
                                             int64_t k, int64_t n, int64_t row_bytes,
                                             int64_t j_start, int64_t j_end, int accumulate,
-                                            int U, int L, int P, int G, int buf_bytes) {
+                                            int U, int L, int P, int G, int buf_bytes, int T) {
     extern __shared__ float smem[];
-    const Lanes<UPL> ln(U, L, G);
+    const Lanes<UPL> ln(U, L, G, T);
     const int64_t rows_per_batch = (int64_t)P * RB;
     const int64_t stride = (int64_t)gridDim.x * rows_per_batch;
-    const int n4 = (int)(k >> 2), nt4 = n4 * MT;
+    const int n4 = (int)(k >> 2);
     const int nq = P * RB * MT;
     const int rbytes = (int)row_bytes; // a row of one batch fits in LDS, so in 32 bits
     const int wave = __builtin_amdgcn_readfirstlane(ln.tid >> 6); // in a scalar register
-    // LDS: [x][weight buffer 0][weight buffer 1][2 x group sums][2 x old y]
-    // (without x in front, 16 bytes of padding: unit reads may touch the
-    // dword before a row)
-    uint8_t *wb = (uint8_t *)(smem + (XL ? k * MT : 4));
+    // LDS: [x records and planes][weight buffer 0][weight buffer 1][2 x group
+    // sums][2 x old y][1 KB sink] (without x in LDS, 16 bytes of padding in
+    // front instead: unit reads may touch the dword before a row)
+    XRec *rec = (XRec *)smem;
+    uint32_t *pl = (uint32_t *)(rec + MT * U);
+    uint8_t *wb = (uint8_t *)smem + (XL ? xplanes_bytes(MT, U) : 16);
     float *red = (float *)(wb + 2 * buf_bytes);
     float *ybuf = red + 2 * nq * ln.NG;
+    uint8_t *sink = (uint8_t *)smem + staged_sink_offset(XL ? (int)xplanes_bytes(MT, U) : 16,
+                                                         buf_bytes, nq * (ln.NG + 1));
 
-    YPrefetch<MT, RB> yp;
-    // Start copying batch b into weight buffer bi (and read its old y).
-    auto copy = [&](int64_t b, int bi) {
+    // Start copying batch b into weight buffer bi; b at or past j_end copies
+    // nothing. The per-lane offset carries the whole piece number and the
+    // descriptor covers exactly the batch's pieces, so lanes past them read
+    // nothing (range check) and write at most 63 pieces past the batch's last
+    // one, into the buffer's slack. A wave whose pieces all lie past the
+    // batch skips its instruction (scalar branch), or with `all` still issues
+    // it with its LDS writes pointed at the sink: then every wave issues all
+    // NPT copy instructions whatever b is, and the compiler's load counts
+    // stay exact.
+    auto copy = [&](int64_t b, int bi, bool all) {
+        const bool any = b < j_end;
         const int64_t r1 = b + rows_per_batch < j_end ? b + rows_per_batch : j_end;
         const int64_t s0 = w_off + b * row_bytes, s1 = w_off + r1 * row_bytes;
-        const int64_t a0 = s0 & ~(int64_t)15;
-        const int np = (int)((((s1 + 15) & ~(int64_t)15) - a0) >> 4);
+        const int64_t a0 = any ? s0 & ~(int64_t)15 : 0;
+        const int np = any ? (int)((((s1 + 15) & ~(int64_t)15) - a0) >> 4) : 0;
         const __amdgpu_buffer_rsrc_t rs = batch_rsrc(W + a0, 16 * np);
-        const int last = 16 * (np - 1);
         uint8_t *dst = wb + bi * buf_bytes;
-        const int voff = 16 * ln.tid;
 #pragma unroll
         for (int s = 0; s < NPT; s++) {
-            // lane l of this wave writes piece s*T + 64*wave + l; the piece's
-            // byte offset is 16*tid (per lane) + 16*s*T (scalar)
-            const int soff = 16 * s * ln.T;
-            uint8_t *slot = dst + 16 * (s * ln.T + 64 * wave);
-            if (voff <= last - soff) // the buffer holds exactly the batch's pieces
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                    rs, (__attribute__((address_space(3))) void *)slot, 16, voff, soff, 0,
-                    2 /* nontemporal */);
+            // lane l of this wave copies piece s*T + 64*wave + l
+            const int first = s * ln.T + 64 * wave; // wave-uniform
+            if (!all && first >= np) break;
+            uint8_t *slot = first < np ? dst + 16 * first : sink;
+            const int voff = 16 * (s * ln.T + ln.tid);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rs, (__attribute__((address_space(3))) void *)slot, 16, voff, 0, 0,
+                2 /* nontemporal */);
         }
-        if (accumulate) yp.fetch(y, n, b, j_end, P, ln.tid, ln.T);
     };
 
     typename F::X xu[MT][UPL];
     if (!XL) x_units_from_global<F, MT, UPL>(xu, x, k, U, ln.ulod);
     int64_t base = j_start + (int64_t)blockIdx.x * rows_per_batch;
-    f32x4 xa[4];
-    if (XL) x_prefetch(x, nt4, ln.tid, ln.T, xa);
-    copy(base, 0); // every workgroup has a first batch: the grid never exceeds the batch count
-    f32x4 *xl = (f32x4 *)smem;
-    if (XL) x_to_lds<F, true>(x, xl, n4, nt4, U, ln.tid, ln.T, xa);
-    if (accumulate) yp.stash(ybuf, P, ln.tid, ln.T);
-    lds_barrier();
-    if constexpr (XL) {
-        // the units' integer planes, computed once per workgroup: [records]
-        // [plane dwords] in weight buffer 1 when they fit there (it is free until
-        // the loop's first copy, which waits for every wave to have read its
-        // planes), else after the reductions' area (see xplanes_lds_bytes)
-        uint8_t *pb;
-        if (xplanes_in_buffer(MT, U, buf_bytes)) {
-            pb = wb + buf_bytes;
-        } else {
-            const size_t pofs =
-                ((size_t)((ybuf + 2 * nq) - smem) * sizeof(float) + 15) & ~(size_t)15;
-            pb = (uint8_t *)smem + pofs;
+    const int64_t b1 = base + stride;
+    // Start-up: the first pieces of x and the old y of the first two batches
+    // (accumulating) are requested, then both weight buffers are filled
+    // (batches 0 and 1), and the x units are turned into their shared
+    // records and planes while those copies are in flight. Every workgroup
+    // has a first batch: the grid never exceeds the batch count.
+    constexpr int XR = 4; // x pieces per thread loaded ahead of the copies
+    const int g16 = ln.tid >> 4, ng = ln.T >> 4, pi = ln.tid & 15, nu = MT * U;
+    f32x4 xr[XR];
+    const f32x4 *x4 = (const f32x4 *)x;
+    auto x_piece = [&](int q) { // piece pi of unit q = t*U + u
+        const int t = q / U, u = q - t * U;
+        return x4[t * n4 + F::x4_index(u, pi, U)];
+    };
+    if (XL) {
+#pragma unroll
+        for (int r = 0; r < XR; r++) {
+            const int q = g16 + r * ng;
+            xr[r] = x_piece(q < nu ? q : nu - 1);
         }
-        XRec *rec = (XRec *)pb;
-        uint32_t *pl = (uint32_t *)(rec + MT * U);
-        x_shared_planes(xl, rec, pl, U, MT, ln.tid, ln.T);
-        lds_barrier();
-        x_units_from_planes<F, MT, UPL>(xu, rec, pl, U, ln.ulod);
-        lds_barrier();
     }
+    YPrefetch<MT, RB> yp, yp1;
+    if (accumulate) {
+        yp.fetch(y, n, base, j_end, P, ln.tid, ln.T);
+        yp1.fetch(y, n, b1, j_end, P, ln.tid, ln.T);
+    }
+    copy(base, 0, true);
+    copy(b1, 1, true);
+    if (XL) {
+        if (g16 < ng) {
+#pragma unroll
+            for (int r = 0; r < XR; r++)
+                if (g16 + r * ng < nu) x_unit_planes(xr[r], g16 + r * ng, pi, U, rec, pl);
+            for (int q = g16 + XR * ng; q < nu; q += ng) x_unit_planes(x_piece(q), q, pi, U, rec, pl);
+        }
+    }
+    if (accumulate) {
+        yp.stash(ybuf, P, ln.tid, ln.T);
+        yp1.stash(ybuf + nq, P, ln.tid, ln.T);
+    }
+    // Wait for this wave's copy of batch 0 (the NPT copy instructions of
+    // batch 1, issued after it, may still be in flight) and its LDS writes,
+    // then for the other waves: batch 0 and the planes are then in LDS. (No
+    // compiler fence here: it would also wait for batch 1.)
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(NPT) : "memory");
+    if (XL) x_units_from_planes<F, MT, UPL>(xu, rec, pl, U, ln.ulod);
 
     int cur = 0;
     int64_t prev = -1; // batch whose group sums wait in LDS
-    for (; base < j_end; base += stride) {
+    for (bool first = true; base < j_end; base += stride, first = false) {
         const int64_t nb = base + stride;
-        if (nb < j_end) copy(nb, cur ^ 1);
+        // batch 1 is already on its way; later, the next batch
+        const bool fetch_next = !first && nb < j_end;
+        if (accumulate) yp.fetch(y, n, nb, j_end, P, ln.tid, ln.T);
+        if (fetch_next) copy(nb, cur ^ 1, false);
         if (ln.NG > 1 && prev >= 0)
             finish_batch<MT, RB>(red + (cur ^ 1) * nq * ln.NG, ybuf + (cur ^ 1) * nq, ln.NG,
                                  P, ln.tid, ln.T, prev, j_end, y, n, accumulate);
@@ -455,7 +491,7 @@ __device__ __forceinline__ void staged_body(const uint8_t *__restrict__ W, int64
         }
         reduce_batch<MT, RB, UPL>(part, ln, G, P, red + cur * nq * ln.NG, ybuf + cur * nq, base,
                                   j_end, y, n, accumulate);
-        if (accumulate && nb < j_end) yp.stash(ybuf + (cur ^ 1) * nq, P, ln.tid, ln.T);
+        if (accumulate && fetch_next) yp.stash(ybuf + (cur ^ 1) * nq, P, ln.tid, ln.T);
         lds_barrier(); // also waits for the copy of the next batch
         prev = base;
         cur ^= 1;
@@ -473,7 +509,7 @@ __global__ __launch_bounds__(512) void qmv_gemv_direct(const uint8_t *__restrict
                                                         int64_t n, int64_t row_bytes,
                                                         int64_t j_start, int64_t j_end,
                                                         int accumulate, int U, int L, int P,
-                                                        int G, int) {
+                                                        int G, int, int) {
     direct_body<F, MT, UPL, RB, XL>(W, x, y, k, n, row_bytes, j_start, j_end, accumulate, U, L,
                                     P, G, typename F::Aux{});
 }
@@ -487,9 +523,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(
                                                                   int64_t row_bytes,
                                                                   int64_t j_start, int64_t j_end,
                                                                   int accumulate, int U, int L,
-                                                                  int P, int G, int buf_bytes) {
+                                                                  int P, int G, int buf_bytes,
+                                                                  int T) {
     staged_body<F, MT, UPL, RB, NPT, XL>(W, 0, x, y, k, n, row_bytes, j_start, j_end,
-                                         accumulate, U, L, P, G, buf_bytes);
+                                         accumulate, U, L, P, G, buf_bytes, T);
 }
 
 // Expert-indexed product (rullama 0.5.0, src/backend/dispatch/mod.rs, the
@@ -516,7 +553,7 @@ __global__ __launch_bounds__(512) void qmv_gemv_moe_direct(const uint8_t *__rest
                                                             int64_t n, int64_t row_bytes,
                                                             int64_t n_experts, int top_k,
                                                             int accumulate, int U, int L, int P,
-                                                            int G, int) {
+                                                            int G, int, int) {
     uint32_t e;
     if (!moe_pair(ids, n_experts, n, y, e)) return;
     direct_body<F, 1, UPL, RB, XL>(W + (int64_t)e * n * row_bytes,
@@ -530,13 +567,13 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(
     StagedOccupancy<1, UPL, RB, NPT>::waves))) void qmv_gemv_moe_staged(
     const uint8_t *__restrict__ W, const uint32_t *__restrict__ ids, const float *__restrict__ x,
     float *__restrict__ y, int64_t k, int64_t n, int64_t row_bytes, int64_t n_experts, int top_k,
-    int accumulate, int U, int L, int P, int G, int buf_bytes) {
+    int accumulate, int U, int L, int P, int G, int buf_bytes, int T) {
     uint32_t e;
     if (!moe_pair(ids, n_experts, n, y, e)) return;
     staged_body<F, 1, UPL, RB, NPT, XL>(W, (int64_t)e * n * row_bytes,
                                         x + (int64_t)(blockIdx.y / top_k) * k,
                                         y + (int64_t)blockIdx.y * n, k, n, row_bytes, 0, n,
-                                        accumulate, U, L, P, G, buf_bytes);
+                                        accumulate, U, L, P, G, buf_bytes, T);
 }
 
 // Affine group-64 rows: the direct body over the code words, with the scales
@@ -571,14 +608,6 @@ static bool staged_format(int fmt) {
 }
 
 static constexpr size_t LDS_BUDGET = 80 * 1024; // weight buffers + reductions
-
-// LDS for the shared integer planes of the staged (block-format) kernels with
-// x in LDS: a 16-byte record and 192 bytes of planes per unit and token, in
-// weight buffer 1 when they fit there, else in 15 bytes of alignment plus
-// that much more.
-static size_t xplanes_lds_bytes(int MT, int U, int buf_bytes) {
-    return xplanes_in_buffer(MT, U, buf_bytes) ? 0 : 15 + (size_t)MT * U * (sizeof(XRec) + 192);
-}
 
 bool plan_gemv(int fmt, int64_t k, int64_t rows, int mt_max, int num_cu, GemvPlan *p) {
     if (k <= 0 || k % 64 != 0) return false;
@@ -659,10 +688,10 @@ bool plan_gemv(int fmt, int64_t k, int64_t rows, int mt_max, int num_cu, GemvPla
             npt = need <= 2 ? 2 : need <= 4 ? 4 : need <= 8 ? 8 : 0;
             if (npt == 0) continue;
         }
-        // exactly the batch's pieces (rounded to 64 bytes): the copy skips
-        // lanes past the last piece
-        const int64_t buf = g.staged ? ((((g.P * cand * rb + 30 + 15) / 16) * 16 + 63) & ~(int64_t)63)
-                                     : 0;
+        // the batch's pieces plus 63 (the slack the last copying wave may
+        // write into), rounded to 64 bytes
+        const int64_t buf =
+            g.staged ? ((((g.P * cand * rb + 30 + 15) / 16 + 63) * 16 + 63) & ~(int64_t)63) : 0;
         const int64_t red = (int64_t)2 * g.P * cand * g.MT * (g.NG + 1) * 4;
         if (2 * buf + red > budget) continue;
         if ((int64_t)g.P * cand * g.MT > 2 * (int64_t)g.T) continue; // y prefetch: 2 per thread
@@ -678,15 +707,18 @@ bool plan_gemv(int fmt, int64_t k, int64_t rows, int mt_max, int num_cu, GemvPla
     g.grid = (int)(batches < ((int64_t)1 << 30) ? batches : ((int64_t)1 << 30));
     if (g.grid < 1) g.grid = 1;
     g.num_cu = num_cu;
-    const size_t xb = (size_t)k * g.MT * sizeof(float);
+    // x in LDS: the staged kernels keep each unit's record and integer planes
+    // there, the direct ones x itself
+    const size_t xb = g.staged ? (size_t)xplanes_bytes(g.MT, g.U) : (size_t)k * g.MT * sizeof(float);
     const size_t red = (size_t)2 * g.P * g.RB * g.MT * (g.NG + 1) * sizeof(float);
     const size_t wbuf = (size_t)2 * g.buf_bytes;
     // x goes through LDS when everything fits in 96 KB; otherwise each lane
     // reads its x units straight from global memory
     g.x_in_lds = (xb + wbuf + red <= 96 * 1024) ? 1 : 0;
-    g.lds_bytes = (g.x_in_lds ? xb + (g.staged ? xplanes_lds_bytes(g.MT, g.U, g.buf_bytes) : 0)
-                              : (g.staged ? 16 : 0)) +
-                  wbuf + red;
+    g.lds_bytes = g.staged ? staged_sink_offset(g.x_in_lds ? (int)xb : 16, g.buf_bytes,
+                                                (int)(red / (2 * sizeof(float)))) +
+                                 STAGED_SINK_BYTES
+                           : (g.x_in_lds ? xb : 0) + wbuf + red;
     if (g.lds_bytes > 160 * 1024) return false;
     *p = g;
     return true;
@@ -705,7 +737,7 @@ static hipError_t launch_k(K kernel, const GemvPlan &p, const uint8_t *W, const 
     const int64_t cap = (int64_t)p.num_cu * res;
     const int grid = (int)(p.grid < cap ? p.grid : cap);
     hipLaunchKernelGGL(kernel, dim3(grid), dim3(p.T), p.lds_bytes, s, W, x, y, k, n, row_bytes,
-                       j0, j1, acc, p.U, p.L, p.P, p.G, p.buf_bytes);
+                       j0, j1, acc, p.U, p.L, p.P, p.G, p.buf_bytes, p.T);
     return hipGetLastError();
 }
 
@@ -745,14 +777,15 @@ static hipError_t launch_direct_rb(const GemvPlan &p, const uint8_t *W, const fl
     return launch_k(qmv_gemv_direct<F, MT, UPL, 1, XL>, p, W, x, y, k, n, rb, j0, j1, acc, s);
 }
 
-// x goes through LDS when the plan allows it and x is 16-byte aligned (the
-// LDS copy moves 16-byte pieces).
+// x goes through LDS when the plan allows it and x is 16-byte aligned (x is
+// read in 16-byte pieces).
 static bool use_x_lds(GemvPlan &p, const float *x, int64_t k) {
     if (p.x_in_lds && ((uintptr_t)x & 15) == 0) return true;
     if (p.x_in_lds)
-        p.lds_bytes -= (size_t)k * p.MT * sizeof(float) +
-                       (p.staged ? xplanes_lds_bytes(p.MT, p.U, p.buf_bytes) : 0) -
-                       (p.staged ? 16 : 0);
+        p.lds_bytes -= p.staged ? (size_t)xplanes_bytes(p.MT, p.U) - 16
+                                : (size_t)k * p.MT * sizeof(float);
+    // (the staged layout's parts after x are multiples of 16 bytes, so the
+    // sink offset moves by exactly the difference)
     p.x_in_lds = 0;
     return false;
 }
@@ -860,7 +893,7 @@ static hipError_t launch_moe_k(K kernel, const GemvPlan &p, const uint8_t *W, co
     if (per < 1) per = 1;
     hipLaunchKernelGGL(kernel, dim3((unsigned)per, (unsigned)a.pairs), dim3(p.T), p.lds_bytes, s,
                        W, a.ids, x, y, k, n, rb, a.n_experts, a.top_k, acc, p.U, p.L, p.P, p.G,
-                       p.buf_bytes);
+                       p.buf_bytes, p.T);
     return hipGetLastError();
 }
 

@@ -167,12 +167,10 @@ __device__ __forceinline__ void x_planes(XI &x) {
     }
 }
 
-// The same, computed once per workgroup from x staged in LDS unit by unit
-// (piece i of unit u of token t at xl[(t*U + u)*16 + i]) and shared through
-// LDS: each aligned group of 16 threads (the complete ones; the plans give at
-// least 33 threads) takes one unit at a time, one piece per lane, exchanging
-// maxima and sums by shuffles within the group; its first lane writes the
-// unit's record.
+// The same, computed once per workgroup and shared through LDS: each aligned
+// group of 16 threads (the complete ones; the plans give at least 33 threads)
+// takes one unit at a time, one 4-value piece per lane, exchanging maxima and
+// sums by shuffles within the group; its first lane writes the unit's record.
 struct XRec {
     int e;
     float c, sum0, sum1;
@@ -180,40 +178,54 @@ struct XRec {
 // plane dword i of digit d of unit u, token t: pl[(((t*3 + d)*4 + i/4)*U + u)*4 + i%4]
 // (a lane's four consecutive dwords are one 16-byte read; lanes of
 // consecutive units read consecutive 16 bytes)
-__device__ __forceinline__ void x_shared_planes(const f32x4 *xl, XRec *rec, uint32_t *pl, int U,
-                                                int MT, int tid, int T) {
-    const int g16 = tid >> 4, ng = T >> 4, i = tid & 15;
-    if (g16 >= ng) return;
-    for (int q = g16; q < MT * U; q += ng) { // q = t*U + u
-        const f32x4 v = xl[16 * q + i];
-        float mx = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
-        int bad = !(fabsf(v.x) <= 3.4028235e38f && fabsf(v.y) <= 3.4028235e38f &&
-                    fabsf(v.z) <= 3.4028235e38f && fabsf(v.w) <= 3.4028235e38f);
-        float ps = ((v.x + v.y) + v.z) + v.w;
+// Lane exchange inside rows of 16 lanes (DPP; CTRL: quad_perm, row_ror, row_mirror...).
+template <int CTRL>
+__device__ __forceinline__ int dpp_mov(int v) {
+    return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xf, 0xf, false);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+    return __builtin_bit_cast(float, dpp_mov<CTRL>(__builtin_bit_cast(int, v)));
+}
+// Unit q = t*U + u from its piece i (= this lane's index in the group) v. The
+// group is one 16-lane row of the wave; maxima, flags and sums move by DPP
+// (quad_perm [1,0,3,2], [2,3,0,1], row_half_mirror, row_mirror, row_ror 8).
+__device__ __forceinline__ void x_unit_planes(f32x4 v, int q, int i, int U, XRec *rec,
+                                              uint32_t *pl) {
+    float mx = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
+    int bad = !(fabsf(v.x) <= 3.4028235e38f && fabsf(v.y) <= 3.4028235e38f &&
+                fabsf(v.z) <= 3.4028235e38f && fabsf(v.w) <= 3.4028235e38f);
+    float ps = ((v.x + v.y) + v.z) + v.w;
+    // pairs, then quads, then halves (lanes 0-7: pieces 0..7, 8-15: 8..15),
+    // then (maximum and flag only) the whole row
+    mx = fmaxf(mx, dpp_mov<0xb1>(mx));
+    bad |= dpp_mov<0xb1>(bad);
+    ps += dpp_mov<0xb1>(ps);
+    mx = fmaxf(mx, dpp_mov<0x4e>(mx));
+    bad |= dpp_mov<0x4e>(bad);
+    ps += dpp_mov<0x4e>(ps);
+    mx = fmaxf(mx, dpp_mov<0x141>(mx));
+    bad |= dpp_mov<0x141>(bad);
+    ps += dpp_mov<0x141>(ps);
+    mx = fmaxf(mx, dpp_mov<0x140>(mx));
+    bad |= dpp_mov<0x140>(bad);
+    const float s1 = dpp_mov<0x128>(ps); // lane 0: the sum of pieces 8..15
+    XRec r;
+    x_scale(mx, !bad, r.e, r.c);
+    uint32_t d[3];
+    x_digits4(v, r.e, d);
+    const int t = q / U, u = q - t * U;
 #pragma unroll
-        for (int o = 1; o < 16; o <<= 1) {
-            mx = fmaxf(mx, __shfl_xor(mx, o, 64));
-            bad |= __shfl_xor(bad, o, 64);
-            if (o < 8) ps += __shfl_xor(ps, o, 64); // lanes 0-7: pieces 0..7, 8-15: 8..15
-        }
-        const float s1 = __shfl_down(ps, 8, 16);
-        XRec r;
-        x_scale(mx, !bad, r.e, r.c);
-        uint32_t d[3];
-        x_digits4(v, r.e, d);
-        const int t = q / U, u = q - t * U;
-#pragma unroll
-        for (int j = 0; j < 3; j++) pl[(((t * 3 + j) * 4 + (i >> 2)) * U + u) * 4 + (i & 3)] = d[j];
-        if (i == 0) {
-            r.sum0 = ps;
-            r.sum1 = s1;
-            rec[q] = r;
-        }
+    for (int j = 0; j < 3; j++) pl[(((t * 3 + j) * 4 + (i >> 2)) * U + u) * 4 + (i & 3)] = d[j];
+    if (i == 0) {
+        r.sum0 = ps;
+        r.sum1 = s1;
+        rec[q] = r;
     }
 }
-// Whether a workgroup's records and planes fit in one weight buffer.
-__host__ __device__ constexpr bool xplanes_in_buffer(int MT, int U, int buf_bytes) {
-    return (long long)MT * U * (sizeof(XRec) + 192) <= (long long)buf_bytes;
+// Bytes of a workgroup's records and planes (a multiple of 16).
+__host__ __device__ constexpr long long xplanes_bytes(int MT, int U) {
+    return (long long)MT * U * (sizeof(XRec) + 192);
 }
 __device__ __forceinline__ void x_from_planes(XI &x, const XRec *rec, const uint32_t *pl, int t,
                                               int u, int U) {
@@ -924,9 +936,11 @@ struct Lanes {
     int uid[UPL];  // units owned by this lane
     int ulod[UPL]; // unit actually read: padding lanes re-read a valid unit
     bool uvalid[UPL];
-    __device__ __forceinline__ Lanes(int U, int L, int G) {
+    __device__ __forceinline__ Lanes(int U, int L, int G) : Lanes(U, L, G, blockDim.x) {}
+    // T given: the workgroup size as launched (saves reading it at run time)
+    __device__ __forceinline__ Lanes(int U, int L, int G, int T_) {
         tid = threadIdx.x;
-        T = blockDim.x;
+        T = T_;
         slot = tid / L;
         lane = tid - slot * L;
         NG = L / G;
