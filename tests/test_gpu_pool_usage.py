@@ -1,0 +1,122 @@
+"""Which entry points take device memory per call.
+
+The header states that the single-token and few-token GEMV family, the
+per-row family, the expert-indexed product and the affine product allocate
+nothing, and that the matrix-core family and the streaming transposed
+product take stream-ordered scratch from the device's memory pool. Each call
+below runs with the pool's high-water mark reset before it and read after it;
+the two allocating families are the probe's positive controls.
+"""
+import ctypes
+
+import numpy as np
+import pytest
+import torch
+
+from block_quantized_matvec_gguf_amd import binding as qb
+from block_quantized_matvec_gguf_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+POOL_ATTR_USED_MEM_HIGH = 8  # hipMemPoolAttrUsedMemHigh
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu_context():
+    assert torch.cuda.is_available(), "the GPU tests need a visible GPU"
+    qb.ensure_context()
+    yield
+
+
+def _pool():
+    hip = ctypes.CDLL("libamdhip64.so")
+    device = ctypes.c_int(0)
+    assert hip.hipGetDevice(ctypes.byref(device)) == 0
+    pool = ctypes.c_void_p()
+    assert hip.hipDeviceGetMemPool(ctypes.byref(pool), device) == 0
+    return hip, pool
+
+
+def _high_after(fn):
+    hip, pool = _pool()
+    zero = ctypes.c_uint64(0)
+    torch.cuda.synchronize()
+    assert hip.hipMemPoolSetAttribute(pool, POOL_ATTR_USED_MEM_HIGH, ctypes.byref(zero)) == 0
+    rc = fn()
+    assert rc == qb.QMV_OK, qb.qmv_last_error()
+    torch.cuda.synchronize()
+    high = ctypes.c_uint64(0)
+    assert hip.hipMemPoolGetAttribute(pool, POOL_ATTR_USED_MEM_HIGH, ctypes.byref(high)) == 0
+    return high.value
+
+
+def _stream():
+    return torch.cuda.current_stream().cuda_stream
+
+
+# (format, k, n, m tokens, algo)
+FORWARD = [
+    (synth.Q6_K, 2560, 1024, 1, qb.QMV_ALGO_GEMV),
+    (synth.Q4_K, 2048, 512, 2, qb.QMV_ALGO_GEMV),
+    (synth.BF16, 1024, 512, 1, qb.QMV_ALGO_GEMV),
+    (synth.Q4_0, 96, 40, 3, qb.QMV_ALGO_SIMPLE),
+    (synth.Q8_0, 1024, 300, 1, qb.QMV_ALGO_AUTO),
+]
+
+
+@pytest.mark.parametrize("fmt,k,n,m,algo", FORWARD)
+def test_forward_families_take_no_pool_memory(fmt, k, n, m, algo):
+    print("case pool forward fmt=%d k=%d n=%d m=%d algo=%d" % (fmt, k, n, m, algo), flush=True)
+    rng = np.random.default_rng(31 + fmt)
+    W = torch.from_numpy(synth.gen_weights(fmt, rng, n, k)).cuda()
+    x = torch.from_numpy(synth.gen_x(rng, m, k)).cuda()
+    y = torch.zeros((m, n), dtype=torch.float32, device="cuda")
+    high = _high_after(lambda: qb.qmv_run_ex(fmt, W.data_ptr(), x.data_ptr(), y.data_ptr(), k, n,
+                                             m, 0, n, 0, _stream(), algo))
+    assert high == 0
+
+
+def test_expert_indexed_takes_no_pool_memory():
+    k, n, E, n_pos, top_k = 512, 96, 6, 2, 2
+    print("case pool expert-indexed q4_k k=%d n=%d E=%d" % (k, n, E), flush=True)
+    rng = np.random.default_rng(41)
+    W = torch.from_numpy(synth.gen_weights(synth.Q4_K, rng, n * E, k)).cuda()
+    ids = torch.tensor([0, 5, 3, 3], dtype=torch.int32, device="cuda")
+    x = torch.from_numpy(synth.gen_x(rng, n_pos, k)).cuda()
+    y = torch.zeros((n_pos * top_k, n), dtype=torch.float32, device="cuda")
+    high = _high_after(lambda: qb.qmv_run_moe(synth.Q4_K, W.data_ptr(), ids.data_ptr(), x.data_ptr(),
+                                              y.data_ptr(), k, n, E, n_pos, top_k, 0, _stream()))
+    assert high == 0
+
+
+def test_affine_takes_no_pool_memory():
+    k, n, bits = 512, 200, 4
+    print("case pool affine bits=%d k=%d n=%d" % (bits, k, n), flush=True)
+    rng = np.random.default_rng(43)
+    words, scales, biases = synth.gen_affine(rng, bits, n, k)
+    codes = torch.from_numpy(words).cuda()
+    sc = torch.from_numpy(scales).cuda()
+    bi = torch.from_numpy(biases).cuda()
+    x = torch.from_numpy(synth.gen_x(rng, 1, k)).cuda()
+    y = torch.zeros((1, n), dtype=torch.float32, device="cuda")
+    high = _high_after(lambda: qb.qmv_run_affine(bits, codes.data_ptr(), sc.data_ptr(), bi.data_ptr(),
+                                                 x.data_ptr(), y.data_ptr(), k, n, 1, 0, n, 0,
+                                                 _stream()))
+    assert high == 0
+
+
+def test_matrix_core_and_transposed_take_scratch():
+    # the probe's positive controls: the two families documented as allocating
+    rng = np.random.default_rng(47)
+    k, n, m = 1024, 128, 32
+    print("case pool controls q4_k k=%d n=%d m=%d" % (k, n, m), flush=True)
+    W = torch.from_numpy(synth.gen_weights(synth.Q4_K, rng, n, k)).cuda()
+    x = torch.from_numpy(synth.gen_x(rng, m, k)).cuda()
+    y = torch.zeros((m, n), dtype=torch.float32, device="cuda")
+    assert _high_after(lambda: qb.qmv_run_ex(synth.Q4_K, W.data_ptr(), x.data_ptr(), y.data_ptr(),
+                                             k, n, m, 0, n, 0, _stream(), qb.QMV_ALGO_MFMA)) > 0
+    dy = torch.from_numpy(synth.gen_x(rng, 1, n)).cuda()
+    dx = torch.zeros((1, k), dtype=torch.float32, device="cuda")
+    assert _high_after(lambda: qb.qmv_run_t_ex(synth.Q4_K, W.data_ptr(), dy.data_ptr(),
+                                               dx.data_ptr(), k, n, 1, 0, n, 0, _stream(),
+                                               qb.QMV_ALGO_GEMV)) > 0
