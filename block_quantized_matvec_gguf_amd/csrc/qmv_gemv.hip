@@ -7,14 +7,16 @@
 //
 // Mapping. A row of k weights is cut into U = k/64 "units" of 64 weights. A
 // workgroup holds P row slots of L lanes; lane l of a slot owns units l,
-// l+L, ... (UPL of them) for the whole launch, so the 64 x values of each
-// owned unit sit in registers, loaded once at kernel start from a transposed
-// copy of x in LDS (conflict-free). The workgroup then processes batches of
-// P*RB consecutive rows (slot s takes rows base+s, base+s+P, ...). Per-lane
-// partial sums of a row are reduced with DPP inside aligned groups of G lanes;
-// the L/G group sums of each row go through LDS. Every row's arithmetic and
-// reduction order depend only on k, never on the row range, so any tiling of
-// the rows gives bit-identical outputs.
+// l+L, ... (UPL of them) for the whole launch, and keeps the x of each owned
+// unit in registers: for F16/BF16 the 64 values, loaded once at kernel start
+// from a transposed copy of x in LDS (conflict-free); for the block formats
+// the unit's exponent and three signed 8-bit digit planes, computed once per
+// workgroup straight from x in global memory and shared through LDS. The
+// workgroup then processes batches of P*RB consecutive rows (slot s takes rows
+// base+s, base+s+P, ...). Per-lane partial sums of a row are reduced with DPP
+// inside aligned groups of G lanes; the L/G group sums of each row go through
+// LDS. Every row's arithmetic and reduction order depend only on k, never on
+// the row range, so any tiling of the rows gives bit-identical outputs.
 //
 // Weight streaming. Wave loads must cover whole, contiguous cache lines: a
 // load instruction whose 64 lanes touch scattered 16-byte pieces costs the L1
@@ -24,19 +26,19 @@
 //    ("direct" kernel).
 //  * Block formats (Q4_0, Q4_K, Q6_K, Q8_0, Q5_0) interleave fields of odd
 //    sizes. There each batch's rows, one contiguous byte range, are copied
-//    one batch ahead straight from memory into a double-buffered LDS area
-//    (buffer_load ... lds, one contiguous kilobyte per wave instruction),
-//    from which lanes read their unit's fields ("staged" kernel). One
-//    LDS-only barrier per batch covers the buffer swap and the cross-group
-//    reduction.
+//    straight from memory into a double-buffered LDS area (buffer_load ...
+//    lds, one contiguous kilobyte per wave instruction; batches 0 and 1 at
+//    the start, then one batch ahead), from which lanes read their unit's
+//    fields ("staged" kernel). One LDS-only barrier per batch covers the
+//    buffer swap and the cross-group reduction.
 //
-// Decode. Codes are masked into bytes and converted with one instruction per
-// weight: Q4_0, Q5_0 and Q6_K codes as signed bytes holding a multiple of
-// q-8, q-16 or q-32, Q8_0 codes as they are (SDWA sign-extended
-// v_cvt_f32_i32), Q4_K codes as unsigned bytes (v_cvt_f32_ubyte0..3). Block
-// scales are applied once per group; the Q4_K min term is applied in
-// factored form, dmin*m*sum(x), with the sums of x precomputed per lane. F16
-// weights go through v_fma_mix_f32; BF16 is a shift/mask into f32.
+// Decode. Block formats multiply integer codes (signed bytes holding a
+// multiple of q-8, q-16 or q-32 for Q4_0, Q5_0, Q6_K; Q8_0 codes as they are;
+// Q4_K nibbles) with the digit planes by v_dot4_i32_i8, apply group scales to
+// the three plane sums by 24-bit integer multiply-adds and combine the planes
+// in f32 once per unit; the Q4_K min term is applied in factored form,
+// dmin*m*sum(x). F16 weights go through v_fma_mix_f32; BF16 is a shift/mask
+// into f32.
 #include "qmv_internal.h"
 #include "qmv_units.h"
 
