@@ -2,11 +2,12 @@
 // argument validation (rullama 0.5.0, src/backend/matmul.rs, the checks at the
 // top of each matmul_* function: block-multiple k, even k for the 16-bit
 // formats, the expected weight byte count), kernel selection and launch on the
-// caller's stream. Nothing here synchronises. Of the launches it calls, two
-// take stream-ordered scratch (hipMallocAsync / hipFreeAsync on the caller's
-// stream): the matrix-core prefill (qmv_mfma.hip) and the streaming transposed
-// product (qmv_gemv_t.hip); qmv_run_noalloc gives the first a fixed
-// per-device buffer instead. Everything else allocates nothing.
+// caller's stream. Of the launches it calls, two take scratch: the
+// matrix-core prefill (qmv_mfma.hip) and the streaming transposed product
+// (qmv_gemv_t.hip). It comes from a per-device cache of buffers kept from
+// call to call (ScratchCache below), which allocates only when no kept buffer
+// is large enough; qmv_run_noalloc gives the first a fixed per-device buffer
+// instead. Everything else allocates nothing.
 #include "qmv.h"
 #include "qmv_internal.h"
 
@@ -16,6 +17,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <memory>
 #include <mutex>
 #include <string>
 #include <vector>
@@ -25,10 +27,164 @@ static_assert(QMV_NOALLOC_SCRATCH_BYTES == qmv::STATIC_SCRATCH_BYTES,
 
 namespace {
 
+// Scratch of the matrix-core and streaming transposed launches on one device:
+// a few buffers kept from call to call, so that a call neither allocates nor
+// frees device memory once the cache holds a buffer large enough (the
+// stream-ordered allocator makes the host wait for the device at every
+// allocate/free pair).
+//
+// While every call has come from one stream, the stream's own order keeps a
+// buffer's uses apart and nothing else is tracked. The first call from a
+// second stream (or from the per-thread default stream, whose handle names a
+// different stream in each thread) waits on the host once for the device to
+// go idle, and from then on each buffer carries the stream of its last use
+// and an event bound to that use's last kernel. A call then takes, in this
+// order, a free buffer large enough last used on its own stream, one whose
+// last use has completed, or any free one large enough, with its stream made
+// to wait on the device for that buffer's event.
+//
+// Failing all of these, the call allocates a buffer of its size into an empty
+// slot, or in place of the smallest free buffer after waiting on the host for
+// that buffer's last use. With every slot lent out to concurrent calls, or
+// with the stream under graph capture, it falls back to stream-ordered
+// allocation. Stream handles identify streams: a stream must not be destroyed
+// while library work on it is pending.
+class ScratchCache final : public qmv::ScratchLender {
+  public:
+    // The destructor frees nothing: it may run at process exit, after the HIP
+    // runtime is gone. qmv_destroy calls clear() first.
+    explicit ScratchCache(int device) : device_(device) {}
+
+    hipError_t acquire(size_t bytes, hipStream_t s, void **buf, hipEvent_t *done) override {
+        *done = nullptr;
+        if (bytes == 0) bytes = 1;
+        hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+        hipError_t e = hipStreamIsCapturing(s, &cs);
+        if (e != hipSuccess) return e;
+        if (cs != hipStreamCaptureStatusNone) return hipMallocAsync(buf, bytes, s);
+        std::lock_guard<std::mutex> lk(mu_);
+        if (!shared_) {
+            if (!sole_seen_) {
+                sole_ = s;
+                sole_seen_ = true;
+            }
+            if (s != sole_ || s == hipStreamPerThread) {
+                // every use so far, all on sole_, has completed after this
+                e = hipDeviceSynchronize();
+                if (e != hipSuccess) return e;
+                shared_ = true;
+            }
+        }
+        const bool own_order = s != hipStreamPerThread;
+        int pick = -1;
+        for (int i = 0; i < SLOTS && pick < 0; i++)
+            if (fits(i, bytes) && (!shared_ || (own_order && slot_[i].last == s))) pick = i;
+        for (int i = 0; i < SLOTS && pick < 0; i++)
+            if (fits(i, bytes) && hipEventQuery(slot_[i].done) == hipSuccess) pick = i;
+        (void)hipGetLastError(); // hipEventQuery reports hipErrorNotReady as an error
+        for (int i = 0; i < SLOTS && pick < 0; i++)
+            if (fits(i, bytes)) {
+                e = hipStreamWaitEvent(s, slot_[i].done, 0);
+                if (e != hipSuccess) return e;
+                pick = i;
+            }
+        if (pick < 0) {
+            // an empty slot, else the smallest free buffer, is (re)allocated
+            for (int i = 0; i < SLOTS && pick < 0; i++)
+                if (!slot_[i].ptr) pick = i;
+            for (int i = 0; i < SLOTS; i++)
+                if (slot_[i].ptr && !slot_[i].lent &&
+                    (pick < 0 || (slot_[pick].ptr && slot_[i].bytes < slot_[pick].bytes)))
+                    pick = i;
+            if (pick < 0) return hipMallocAsync(buf, bytes, s); // every slot is lent out
+            Slot &z = slot_[pick];
+            if (z.ptr) {
+                // the buffer's last use: its event, or sole_'s order before sharing
+                e = shared_ ? hipEventSynchronize(z.done) : hipStreamSynchronize(sole_);
+                if (e != hipSuccess) return e;
+                e = hipFree(z.ptr);
+                z.ptr = nullptr;
+                z.bytes = 0;
+                z.last = nullptr;
+                if (e != hipSuccess) return e;
+            }
+            if (!z.done) {
+                e = hipEventCreateWithFlags(&z.done, hipEventDisableTiming);
+                if (e != hipSuccess) {
+                    z.done = nullptr;
+                    return e;
+                }
+            }
+            e = hipMalloc(&z.ptr, bytes);
+            if (e != hipSuccess) {
+                z.ptr = nullptr;
+                return e;
+            }
+            z.bytes = bytes;
+        }
+        slot_[pick].lent = true;
+        *buf = slot_[pick].ptr;
+        if (shared_) *done = slot_[pick].done;
+        return hipSuccess;
+    }
+
+    hipError_t release(void *buf, hipStream_t s, bool bound) override {
+        {
+            std::lock_guard<std::mutex> lk(mu_);
+            for (Slot &z : slot_)
+                if (z.lent && z.ptr == buf) {
+                    z.lent = false;
+                    z.last = s;
+                    // sharing may have begun while this buffer was lent out
+                    return shared_ && !bound ? hipEventRecord(z.done, s) : hipSuccess;
+                }
+        }
+        return hipFreeAsync(buf, s); // came from a fallback allocation
+    }
+
+    // Waits for the device to finish, then frees buffers and events.
+    void clear() {
+        std::lock_guard<std::mutex> lk(mu_);
+        int cur = -1;
+        const bool have_cur = hipGetDevice(&cur) == hipSuccess;
+        if (hipSetDevice(device_) == hipSuccess) (void)hipDeviceSynchronize();
+        for (Slot &z : slot_) {
+            if (z.done) (void)hipEventDestroy(z.done);
+            if (z.ptr) (void)hipFree(z.ptr);
+            z = Slot();
+        }
+        shared_ = false;
+        sole_seen_ = false;
+        sole_ = nullptr;
+        if (have_cur) (void)hipSetDevice(cur);
+        (void)hipGetLastError();
+    }
+
+  private:
+    static constexpr int SLOTS = 4;
+    struct Slot {
+        void *ptr = nullptr;
+        size_t bytes = 0;
+        hipEvent_t done = nullptr; // bound to or recorded after the last use (once shared)
+        hipStream_t last = nullptr;
+        bool lent = false;
+    };
+    bool fits(int i, size_t bytes) const {
+        return slot_[i].ptr && !slot_[i].lent && slot_[i].bytes >= bytes;
+    }
+    int device_;
+    std::mutex mu_;
+    bool shared_ = false;    // a second stream has used the cache
+    bool sole_seen_ = false; // sole_ holds the one stream seen so far
+    hipStream_t sole_ = nullptr;
+    Slot slot_[SLOTS];
+};
+
 struct DevInfo {
     bool gfx950;
     int num_cu;
     void *scratch; // this device's copy of the fixed scratch (qmv_run_noalloc)
+    std::shared_ptr<ScratchCache> cache;
 };
 
 std::mutex g_mu;
@@ -153,6 +309,7 @@ int qmv_create(void) {
         if (e != hipSuccess)
             return fail(QMV_ERR_HIP, "qmv_create: scratch address on device %d: %s", d,
                         hipGetErrorString(e));
+        devs[d].cache = std::make_shared<ScratchCache>(d);
     }
     g_dev = devs;
     g_refs = 1;
@@ -162,7 +319,12 @@ int qmv_create(void) {
 void qmv_destroy(void) {
     std::lock_guard<std::mutex> lk(g_mu);
     if (g_refs.load() <= 0) return;
-    if (--g_refs == 0) g_dev.clear();
+    if (--g_refs == 0) {
+        // each cache waits for the last use of its buffers before freeing them
+        for (DevInfo &d : g_dev)
+            if (d.cache) d.cache->clear();
+        g_dev.clear();
+    }
 }
 
 int64_t qmv_weight_bytes(int format, int64_t k, int64_t n) {
@@ -311,7 +473,8 @@ int run_impl(int format, const void *W, const float *x, float *y, int64_t k, int
             e = qmv::launch_mfma_ws(p, Wb, x, y, k, n, m_tokens, rb, j_start, j_end, accumulate,
                                     ws, s);
         } else {
-            e = qmv::launch_mfma(p, Wb, x, y, k, n, m_tokens, rb, j_start, j_end, accumulate, s);
+            e = qmv::launch_mfma(p, Wb, x, y, k, n, m_tokens, rb, j_start, j_end, accumulate,
+                                 *g_dev[(size_t)dev].cache, s);
         }
         if (e != hipSuccess) return fail(QMV_ERR_HIP, "mfma launch: %s", hipGetErrorString(e));
         return QMV_OK;
@@ -436,7 +599,8 @@ int qmv_run_t_ex(int format, const void *W, const float *dy, float *dx, int64_t 
     qmv::GemvTPlan p;
     if (!qmv::plan_gemv_t(format, k, j_end - j_start, num_cu, &p))
         return fail(QMV_ERR_UNSUPPORTED, "transposed plan failed");
-    e = qmv::launch_gemv_t(p, Wb, dy, dx, k, n, m_tokens, rb, j_start, j_end, accumulate, s);
+    e = qmv::launch_gemv_t(p, Wb, dy, dx, k, n, m_tokens, rb, j_start, j_end, accumulate,
+                           *g_dev[(size_t)dev].cache, s);
     if (e != hipSuccess) return fail(QMV_ERR_HIP, "transposed launch: %s", hipGetErrorString(e));
     return QMV_OK;
 }

@@ -19,8 +19,8 @@
 //     and the workgroup writes its partial dx (k floats) to scratch.
 //  2. qmv_gemv_t_reduce: adds the partials of all workgroups in a fixed order
 //     (64 interleaved running sums, then a fixed tree) and writes or adds dx.
-// Scratch (grid * k floats) comes from the stream's memory pool
-// (hipMallocAsync / hipFreeAsync). Rows are assigned to workgroups by the
+// Scratch (grid * k floats) is lent by the library's per-device scratch cache
+// (reused across calls; see qmv_api.cpp). Rows are assigned to workgroups by the
 // row range and the grid size only, so a launch is deterministic run to run.
 #include "qmv_internal.h"
 #include "qmv_units.h"
@@ -252,7 +252,8 @@ namespace {
 template <class F, int UPL, int NPT>
 hipError_t launch_t_k(const GemvTPlan &p, const uint8_t *W, const float *dy, float *dx,
                       int64_t k, int64_t n, int64_t m, int64_t row_bytes, int64_t j_start,
-                      int64_t j_end, int accumulate, hipStream_t s) {
+                      int64_t j_end, int accumulate, ScratchLender &lender,
+                      hipStream_t s) {
     auto kernel = qmv_gemv_t_staged<F, UPL, NPT>;
     if (p.lds_bytes > 64 * 1024 &&
         hipFuncSetAttribute((const void *)kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -263,7 +264,8 @@ hipError_t launch_t_k(const GemvTPlan &p, const uint8_t *W, const float *dy, flo
     const int64_t cap = (int64_t)p.num_cu * res;
     const int grid = (int)(p.grid < cap ? p.grid : cap);
     void *buf = nullptr;
-    hipError_t e = hipMallocAsync(&buf, (size_t)grid * k * sizeof(float), s);
+    hipEvent_t done = nullptr;
+    hipError_t e = lender.acquire((size_t)grid * k * sizeof(float), s, &buf, &done);
     if (e != hipSuccess) return e;
     float *part = (float *)buf;
     for (int64_t t = 0; t < m && e == hipSuccess; t++) {
@@ -271,50 +273,51 @@ hipError_t launch_t_k(const GemvTPlan &p, const uint8_t *W, const float *dy, flo
                            row_bytes, j_start, j_end, p.U, p.L, p.P, p.buf_bytes);
         e = hipGetLastError();
         if (e != hipSuccess) break;
-        hipLaunchKernelGGL(qmv_gemv_t_reduce, dim3((unsigned)(k / 16)), dim3(256), 0, s, part,
-                           dx + t * k, k, grid, accumulate);
+        // the last reduce is the buffer's last reader
+        launch_stop(qmv_gemv_t_reduce, dim3((unsigned)(k / 16)), dim3(256), 0, s,
+                    t + 1 == m ? done : nullptr, part, dx + t * k, k, grid, accumulate);
         e = hipGetLastError();
     }
-    const hipError_t f = hipFreeAsync(buf, s);
+    const hipError_t f = lender.release(buf, s, e == hipSuccess && done && m > 0);
     return e != hipSuccess ? e : f;
 }
 
 template <class F>
 hipError_t launch_t_f(const GemvTPlan &p, const uint8_t *W, const float *dy, float *dx,
                       int64_t k, int64_t n, int64_t m, int64_t rb, int64_t j0, int64_t j1,
-                      int acc, hipStream_t s) {
+                      int acc, ScratchLender &lender, hipStream_t s) {
     if (p.UPL == 2) {
-        if (p.npt == 2) return launch_t_k<F, 2, 2>(p, W, dy, dx, k, n, m, rb, j0, j1, acc, s);
-        if (p.npt == 4) return launch_t_k<F, 2, 4>(p, W, dy, dx, k, n, m, rb, j0, j1, acc, s);
-        return launch_t_k<F, 2, 8>(p, W, dy, dx, k, n, m, rb, j0, j1, acc, s);
+        if (p.npt == 2) return launch_t_k<F, 2, 2>(p, W, dy, dx, k, n, m, rb, j0, j1, acc, lender, s);
+        if (p.npt == 4) return launch_t_k<F, 2, 4>(p, W, dy, dx, k, n, m, rb, j0, j1, acc, lender, s);
+        return launch_t_k<F, 2, 8>(p, W, dy, dx, k, n, m, rb, j0, j1, acc, lender, s);
     }
-    if (p.npt == 2) return launch_t_k<F, 1, 2>(p, W, dy, dx, k, n, m, rb, j0, j1, acc, s);
-    if (p.npt == 4) return launch_t_k<F, 1, 4>(p, W, dy, dx, k, n, m, rb, j0, j1, acc, s);
-    return launch_t_k<F, 1, 8>(p, W, dy, dx, k, n, m, rb, j0, j1, acc, s);
+    if (p.npt == 2) return launch_t_k<F, 1, 2>(p, W, dy, dx, k, n, m, rb, j0, j1, acc, lender, s);
+    if (p.npt == 4) return launch_t_k<F, 1, 4>(p, W, dy, dx, k, n, m, rb, j0, j1, acc, lender, s);
+    return launch_t_k<F, 1, 8>(p, W, dy, dx, k, n, m, rb, j0, j1, acc, lender, s);
 }
 
 } // namespace
 
 hipError_t launch_gemv_t(const GemvTPlan &p, const uint8_t *W, const float *dy, float *dx,
                          int64_t k, int64_t n, int64_t m, int64_t row_bytes, int64_t j_start,
-                         int64_t j_end, int accumulate, hipStream_t s) {
+                         int64_t j_end, int accumulate, ScratchLender &lender, hipStream_t s) {
     switch (p.fmt) {
     case FMT_Q4_0:
-        return launch_t_f<UQ4_0>(p, W, dy, dx, k, n, m, row_bytes, j_start, j_end, accumulate, s);
+        return launch_t_f<UQ4_0>(p, W, dy, dx, k, n, m, row_bytes, j_start, j_end, accumulate, lender, s);
     case FMT_Q4_K:
-        return launch_t_f<UQ4_K>(p, W, dy, dx, k, n, m, row_bytes, j_start, j_end, accumulate, s);
+        return launch_t_f<UQ4_K>(p, W, dy, dx, k, n, m, row_bytes, j_start, j_end, accumulate, lender, s);
     case FMT_Q6_K:
-        return launch_t_f<UQ6_K>(p, W, dy, dx, k, n, m, row_bytes, j_start, j_end, accumulate, s);
+        return launch_t_f<UQ6_K>(p, W, dy, dx, k, n, m, row_bytes, j_start, j_end, accumulate, lender, s);
     case FMT_Q8_0:
-        return launch_t_f<UQ8_0>(p, W, dy, dx, k, n, m, row_bytes, j_start, j_end, accumulate, s);
+        return launch_t_f<UQ8_0>(p, W, dy, dx, k, n, m, row_bytes, j_start, j_end, accumulate, lender, s);
     case FMT_Q5_0:
-        return launch_t_f<UQ5_0>(p, W, dy, dx, k, n, m, row_bytes, j_start, j_end, accumulate, s);
+        return launch_t_f<UQ5_0>(p, W, dy, dx, k, n, m, row_bytes, j_start, j_end, accumulate, lender, s);
     case FMT_BF16:
         return launch_t_f<UHalf<true>>(p, W, dy, dx, k, n, m, row_bytes, j_start, j_end,
-                                       accumulate, s);
+                                       accumulate, lender, s);
     case FMT_F16:
         return launch_t_f<UHalf<false>>(p, W, dy, dx, k, n, m, row_bytes, j_start, j_end,
-                                        accumulate, s);
+                                        accumulate, lender, s);
     default: return hipErrorInvalidValue;
     }
 }

@@ -1,6 +1,7 @@
 // Internal declarations shared by the kernel files and the C-ABI layer.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -96,11 +97,40 @@ hipError_t launch_simple_moe(int fmt, const uint8_t *W, const uint32_t *ids, con
                              float *y, int64_t k, int64_t n, int64_t row_bytes, int64_t n_experts,
                              int64_t n_pos, int top_k, int accumulate, hipStream_t stream);
 
+// Device scratch lent to one call by the API layer. acquire() hands out a
+// buffer of at least `bytes` on the current device that work enqueued on `s`
+// may use at once (the lender has already ordered `s` after the buffer's
+// previous user), and in *done an event (or null) that the borrower binds as
+// the stop event of the last launch touching the buffer, which marks the
+// buffer's last use without an event-record packet of its own. release()
+// takes the buffer back once that work is enqueued, told whether the event was
+// bound (if not, the lender records it on `s` itself).
+struct ScratchLender {
+    virtual hipError_t acquire(size_t bytes, hipStream_t s, void **buf, hipEvent_t *done) = 0;
+    virtual hipError_t release(void *buf, hipStream_t s, bool bound) = 0;
+
+  protected:
+    ~ScratchLender() = default;
+};
+
+// A kernel launch on `stream`; with a non-null `stop`, that event is bound to
+// the launch's completion (hipExtLaunchKernel) instead of recorded apart.
+template <class K, class... A>
+void launch_stop(K kernel, dim3 grid, dim3 block, uint32_t lds, hipStream_t stream,
+                 hipEvent_t stop, A... args) {
+    if (stop)
+        hipExtLaunchKernelGGL(kernel, grid, block, lds, stream, nullptr, stop, 0u, args...);
+    else
+        hipLaunchKernelGGL(kernel, grid, block, lds, stream, args...);
+}
+
 // Transposed product dx (=|+=) W^T dy over rows [j_start, j_end), per token.
 bool plan_gemv_t(int fmt, int64_t k, int64_t rows, int num_cu, GemvTPlan *p);
+// lender: supplies the per-workgroup partials
 hipError_t launch_gemv_t(const GemvTPlan &p, const uint8_t *W, const float *dy, float *dx,
                          int64_t k, int64_t n, int64_t m, int64_t row_bytes, int64_t j_start,
-                         int64_t j_end, int accumulate, hipStream_t stream);
+                         int64_t j_end, int accumulate, ScratchLender &lender,
+                         hipStream_t stream);
 const char *gemv_t_kernel_name(const GemvTPlan &p);
 hipError_t launch_simple_t(int fmt, const uint8_t *W, const float *dy, float *dx, int64_t k,
                            int64_t n, int64_t m, int64_t row_bytes, int64_t j_start,
@@ -108,21 +138,27 @@ hipError_t launch_simple_t(int fmt, const uint8_t *W, const float *dy, float *dx
 hipError_t launch_fill_zero_all(float *v, int64_t count, hipStream_t stream);
 
 bool plan_mfma(int fmt, int64_t k, int64_t rows, int64_t m, int num_cu, MfmaPlan *p);
+// lender: supplies the staging buffer
 hipError_t launch_mfma(const MfmaPlan &p, const uint8_t *W, const float *x, float *y,
                        int64_t k, int64_t n, int64_t m, int64_t row_bytes, int64_t j_start,
-                       int64_t j_end, int accumulate, hipStream_t stream);
+                       int64_t j_end, int accumulate, ScratchLender &lender,
+                       hipStream_t stream);
 const char *mfma_kernel_name(const MfmaPlan &p);
 // Bytes of the staging buffer a matrix-core launch uses, and the launch with
 // that buffer supplied by the caller (device memory, 16-byte aligned).
 size_t mfma_scratch_bytes(const MfmaPlan &p, int64_t k);
+// `stop` (or null): an event bound to the matrix-core kernel, the last
+// reader of the buffer.
 hipError_t launch_mfma_ws(const MfmaPlan &p, const uint8_t *W, const float *x, float *y,
                           int64_t k, int64_t n, int64_t m, int64_t row_bytes, int64_t j_start,
-                          int64_t j_end, int accumulate, void *scratch, hipStream_t stream);
+                          int64_t j_end, int accumulate, void *scratch, hipStream_t stream,
+                          hipEvent_t stop = nullptr);
 
 // Bytes of the fixed per-device scratch of qmv_run_noalloc, and its set-up:
 // *ptr becomes the device address of `device`'s copy, looked up with that
 // device current (the caller's current device is restored afterwards).
 constexpr size_t STATIC_SCRATCH_BYTES = (size_t)16 << 20;
 hipError_t static_scratch_init(int device, void **ptr);
+
 
 } // namespace qmv

@@ -833,9 +833,9 @@ QMV_MFMA_HL_KERNEL(qmv_mfma_bf16, DHalf<true>)
 template <class K>
 void launch_hl(K kernel, const MfmaPlan &p, const uint8_t *W, const uint8_t *xs, const int *pe,
                float *y, int64_t k, int64_t n, int64_t m, int64_t row_bytes, int64_t j_start,
-               int64_t j_end, int accumulate, hipStream_t stream) {
-    hipLaunchKernelGGL(kernel, dim3(p.tiles_n, p.tiles_m), dim3(NT), 0, stream, W, xs, pe, y, k,
-                       n, m, row_bytes, j_start, j_end, accumulate);
+               int64_t j_end, int accumulate, hipStream_t stream, hipEvent_t stop) {
+    launch_stop(kernel, dim3(p.tiles_n, p.tiles_m), dim3(NT), 0, stream, stop, W, xs, pe, y, k, n,
+                m, row_bytes, j_start, j_end, accumulate);
 }
 
 } // namespace
@@ -888,7 +888,8 @@ size_t mfma_scratch_bytes(const MfmaPlan &p, int64_t k) {
 
 hipError_t launch_mfma_ws(const MfmaPlan &p, const uint8_t *W, const float *x, float *y,
                           int64_t k, int64_t n, int64_t m, int64_t row_bytes, int64_t j_start,
-                          int64_t j_end, int accumulate, void *scratch, hipStream_t stream) {
+                          int64_t j_end, int accumulate, void *scratch, hipStream_t stream,
+                          hipEvent_t stop) {
     const int64_t nsb = k / 256;
     if (p.tiles_m > 65535 || (int64_t)p.tiles_m * TM > 0x7fffffff) return hipErrorInvalidConfiguration;
     uint8_t *xs = (uint8_t *)scratch, *sm = xs + xs_bytes(p.tiles_m, nsb);
@@ -902,15 +903,15 @@ hipError_t launch_mfma_ws(const MfmaPlan &p, const uint8_t *W, const float *x, f
     if (e != hipSuccess) return e;
     switch (p.fmt) {
     case FMT_Q4_K:
-        hipLaunchKernelGGL(qmv_mfma_q4_k, dim3(p.tiles_n, p.tiles_m), dim3(NT), 0, stream, W, xs,
-                           sm, pe, y, k, n, m, row_bytes, j_start, j_end, accumulate);
+        launch_stop(qmv_mfma_q4_k, dim3(p.tiles_n, p.tiles_m), dim3(NT), 0, stream, stop, W, xs,
+                    sm, pe, y, k, n, m, row_bytes, j_start, j_end, accumulate);
         break;
-    case FMT_Q4_0: launch_hl(qmv_mfma_q4_0, p, W, xs, pe, y, k, n, m, row_bytes, j_start, j_end, accumulate, stream); break;
-    case FMT_Q5_0: launch_hl(qmv_mfma_q5_0, p, W, xs, pe, y, k, n, m, row_bytes, j_start, j_end, accumulate, stream); break;
-    case FMT_Q8_0: launch_hl(qmv_mfma_q8_0, p, W, xs, pe, y, k, n, m, row_bytes, j_start, j_end, accumulate, stream); break;
-    case FMT_Q6_K: launch_hl(qmv_mfma_q6_k, p, W, xs, pe, y, k, n, m, row_bytes, j_start, j_end, accumulate, stream); break;
-    case FMT_F16: launch_hl(qmv_mfma_f16, p, W, xs, pe, y, k, n, m, row_bytes, j_start, j_end, accumulate, stream); break;
-    case FMT_BF16: launch_hl(qmv_mfma_bf16, p, W, xs, pe, y, k, n, m, row_bytes, j_start, j_end, accumulate, stream); break;
+    case FMT_Q4_0: launch_hl(qmv_mfma_q4_0, p, W, xs, pe, y, k, n, m, row_bytes, j_start, j_end, accumulate, stream, stop); break;
+    case FMT_Q5_0: launch_hl(qmv_mfma_q5_0, p, W, xs, pe, y, k, n, m, row_bytes, j_start, j_end, accumulate, stream, stop); break;
+    case FMT_Q8_0: launch_hl(qmv_mfma_q8_0, p, W, xs, pe, y, k, n, m, row_bytes, j_start, j_end, accumulate, stream, stop); break;
+    case FMT_Q6_K: launch_hl(qmv_mfma_q6_k, p, W, xs, pe, y, k, n, m, row_bytes, j_start, j_end, accumulate, stream, stop); break;
+    case FMT_F16: launch_hl(qmv_mfma_f16, p, W, xs, pe, y, k, n, m, row_bytes, j_start, j_end, accumulate, stream, stop); break;
+    case FMT_BF16: launch_hl(qmv_mfma_bf16, p, W, xs, pe, y, k, n, m, row_bytes, j_start, j_end, accumulate, stream, stop); break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -918,12 +919,14 @@ hipError_t launch_mfma_ws(const MfmaPlan &p, const uint8_t *W, const float *x, f
 
 hipError_t launch_mfma(const MfmaPlan &p, const uint8_t *W, const float *x, float *y, int64_t k,
                        int64_t n, int64_t m, int64_t row_bytes, int64_t j_start, int64_t j_end,
-                       int accumulate, hipStream_t stream) {
+                       int accumulate, ScratchLender &lender, hipStream_t stream) {
     void *buf = nullptr;
-    hipError_t e = hipMallocAsync(&buf, mfma_scratch_bytes(p, k), stream);
+    hipEvent_t done = nullptr;
+    hipError_t e = lender.acquire(mfma_scratch_bytes(p, k), stream, &buf, &done);
     if (e != hipSuccess) return e;
-    e = launch_mfma_ws(p, W, x, y, k, n, m, row_bytes, j_start, j_end, accumulate, buf, stream);
-    const hipError_t f = hipFreeAsync(buf, stream);
+    e = launch_mfma_ws(p, W, x, y, k, n, m, row_bytes, j_start, j_end, accumulate, buf, stream,
+                       done);
+    const hipError_t f = lender.release(buf, stream, e == hipSuccess && done);
     return e != hipSuccess ? e : f;
 }
 

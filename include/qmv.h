@@ -24,8 +24,10 @@
  * tensor) unless stated. The caller owns every buffer; the library keeps no
  * pointer after a call returns. The GEMV and per-row families allocate no
  * memory; the matrix-core family (qmv_run_ex) and the streaming transposed
- * family (qmv_run_t_ex) take stream-ordered scratch; qmv_run_noalloc runs the
- * forward families with no allocation at all.
+ * family (qmv_run_t_ex) take scratch from a per-device cache of at most four
+ * buffers that the library keeps from call to call and frees in the last
+ * qmv_destroy (each buffer as large as the largest request it served);
+ * qmv_run_noalloc runs the forward families with no allocation at all.
  */
 #ifndef QMV_H
 #define QMV_H
@@ -81,8 +83,12 @@ int qmv_create(void);
 
 /* Enqueue y (=|+=) x @ W for rows [j_start, j_end) on `stream` (a hipStream_t;
  * NULL is the default stream) of the current device, with the kernel family
- * chosen automatically. Never synchronises; the caller keeps W, x and y alive
- * until the stream work completes.
+ * chosen automatically. Never synchronises, with two exceptions in the
+ * families that take scratch (qmv_run_ex): a call that finds every free
+ * cached buffer too small replaces the smallest one, and waits on the host
+ * for that buffer's last use before freeing it; and the first such call on a
+ * device from a second stream waits for the device to go idle. The caller
+ * keeps W, x and y alive until the stream work completes.
  *
  *   format      one of enum qmv_format.
  *   W           n rows of qmv_weight_bytes(format, k, 1) bytes, 16-byte aligned.
@@ -110,12 +116,22 @@ int qmv_run(int format, const void *W, const float *x, float *y, int64_t k, int6
             void *stream);
 
 /* qmv_run with an explicit kernel family (enum qmv_algo). QMV_ALGO_MFMA
- * supports Q4_K with k a multiple of 256 (otherwise QMV_ERR_UNSUPPORTED) and
- * needs x 16-byte aligned (otherwise QMV_ERR_MISALIGNED). It is the one
- * family that uses scratch memory: x is first rewritten into matrix-core
- * operand order in a buffer of about m_tokens*k*4.2 bytes, taken from and
- * returned to the current memory pool of the stream's device with
- * hipMallocAsync / hipFreeAsync on `stream` (QMV_ERR_HIP if that fails).
+ * supports every format with k a multiple of 256 (otherwise
+ * QMV_ERR_UNSUPPORTED) and needs x 16-byte aligned (otherwise
+ * QMV_ERR_MISALIGNED). It is the one forward family that uses scratch memory:
+ * x is first rewritten into matrix-core operand order in a buffer of about
+ * m_tokens*k*4.2 bytes (m_tokens rounded up to 64) from the library's
+ * per-device cache. A call allocates device memory (hipMalloc, QMV_ERR_HIP if
+ * that fails) only when no free cached buffer is large enough. While all
+ * scratch-taking calls on a device come from one stream, its order alone
+ * separates the uses of a buffer; the first such call from another stream
+ * (or from hipStreamPerThread) waits once on the host for the device to go
+ * idle, and from then on a call reuses a buffer last used on its own stream
+ * as is and orders `stream` after the last use of one from another stream
+ * with an event wait on the device. A stream handle identifies a stream:
+ * destroy a stream only after the library's work on it has completed. Under
+ * graph capture of `stream` the call takes the buffer with hipMallocAsync /
+ * hipFreeAsync on `stream` instead.
  * QMV_ALGO_AUTO takes it for m_tokens >= 16 when it applies and x is 16-byte
  * aligned, else the GEMV family. All families meet the same accuracy
  * contract; they may differ in the last bits. */
@@ -160,9 +176,10 @@ int qmv_run_noalloc(int format, const void *W, const float *x, float *y, int64_t
  *               sum (dx = 0, or unchanged when accumulating).
  *
  * Returns QMV_OK after a successful enqueue, else the same codes as qmv_run.
- * The streaming family takes stream-ordered scratch of at most 4 MiB * k /
- * 1024 (one partial dx per workgroup, hipMallocAsync / hipFreeAsync on
- * `stream`; QMV_ERR_HIP if that fails) and is deterministic run to run; a
+ * The streaming family takes scratch of at most 4 MiB * k / 1024 (one
+ * partial dx per workgroup) from the same per-device cache as QMV_ALGO_MFMA
+ * of qmv_run_ex (QMV_ERR_HIP if an allocation fails) and is deterministic
+ * run to run; a
  * split of the range into tiles changes the rounding, not the accuracy
  * contract (|error| <= 1e-4 * sum_j |dy_j * w_j[i]|). */
 int qmv_run_t(int format, const void *W, const float *dy, float *dx, int64_t k, int64_t n,
@@ -236,8 +253,10 @@ int qmv_run_affine(int bits, const void *codes, const void *scales, const void *
 /* Name of the kernel qmv_run_affine launches, or "" for an invalid request. */
 const char *qmv_affine_kernel_name(int bits, int64_t k);
 
-/* Release one reference to the context; the last one frees it. Safe to call
- * when not initialised. Must not race with qmv_run or qmv_create. */
+/* Release one reference to the context; the last one frees it, with the
+ * cached scratch buffers once their last use has completed (the host waits
+ * for that). Safe to call when not initialised. Must not race with qmv_run
+ * or qmv_create. */
 void qmv_destroy(void);
 
 /* Bytes of W for n rows of k weights, or -1 if the format is unknown or k is

@@ -3,9 +3,12 @@
 The header states that the single-token and few-token GEMV family, the
 per-row family, the expert-indexed product and the affine product allocate
 nothing, and that the matrix-core family and the streaming transposed
-product take stream-ordered scratch from the device's memory pool. Each call
-below runs with the pool's high-water mark reset before it and read after it;
-the two allocating families are the probe's positive controls.
+product take their scratch from the library's own per-device cache, which
+allocates with hipMalloc only when no cached buffer is large enough. Each
+call below runs with the device's stream-ordered pool's high-water mark reset
+before it and read after it (the pool a hipMallocAsync on the stream would
+draw from; the probe's positive control is such an allocation of the test's
+own), and the cache's reuse is seen in the device's free memory.
 """
 import ctypes
 
@@ -105,18 +108,94 @@ def test_affine_takes_no_pool_memory():
     assert high == 0
 
 
-def test_matrix_core_and_transposed_take_scratch():
-    # the probe's positive controls: the two families documented as allocating
+def _own_async_allocation(nbytes):
+    hip = ctypes.CDLL("libamdhip64.so")
+    buf = ctypes.c_void_p()
+    s = ctypes.c_void_p(_stream())
+    assert hip.hipMallocAsync(ctypes.byref(buf), ctypes.c_size_t(nbytes), s) == 0
+    assert hip.hipFreeAsync(buf, s) == 0
+    return qb.QMV_OK
+
+
+def test_probe_sees_stream_ordered_allocation():
+    print("case pool probe control", flush=True)
+    assert _high_after(lambda: _own_async_allocation(1 << 20)) >= 1 << 20
+
+
+def test_matrix_core_and_transposed_leave_the_pool_alone():
+    # their scratch comes from the library's cache, not the stream's pool
     rng = np.random.default_rng(47)
     k, n, m = 1024, 128, 32
-    print("case pool controls q4_k k=%d n=%d m=%d" % (k, n, m), flush=True)
+    print("case pool scratch families q4_k k=%d n=%d m=%d" % (k, n, m), flush=True)
     W = torch.from_numpy(synth.gen_weights(synth.Q4_K, rng, n, k)).cuda()
     x = torch.from_numpy(synth.gen_x(rng, m, k)).cuda()
     y = torch.zeros((m, n), dtype=torch.float32, device="cuda")
     assert _high_after(lambda: qb.qmv_run_ex(synth.Q4_K, W.data_ptr(), x.data_ptr(), y.data_ptr(),
-                                             k, n, m, 0, n, 0, _stream(), qb.QMV_ALGO_MFMA)) > 0
+                                             k, n, m, 0, n, 0, _stream(), qb.QMV_ALGO_MFMA)) == 0
     dy = torch.from_numpy(synth.gen_x(rng, 1, n)).cuda()
     dx = torch.zeros((1, k), dtype=torch.float32, device="cuda")
     assert _high_after(lambda: qb.qmv_run_t_ex(synth.Q4_K, W.data_ptr(), dy.data_ptr(),
                                                dx.data_ptr(), k, n, 1, 0, n, 0, _stream(),
-                                               qb.QMV_ALGO_GEMV)) > 0
+                                               qb.QMV_ALGO_GEMV)) == 0
+
+
+def _free_after(fn):
+    torch.cuda.synchronize()
+    rc = fn()
+    assert rc == qb.QMV_OK, qb.qmv_last_error()
+    torch.cuda.synchronize()
+    return torch.cuda.mem_get_info()[0]
+
+
+def test_scratch_cache_grows_once_then_reuses():
+    # a matrix-core request larger than any before it allocates once; the same
+    # request again, and a smaller one, allocate nothing
+    rng = np.random.default_rng(53)
+    k, n, m_small, m_big = 8192, 64, 16, 1024
+    print("case scratch cache q4_k k=%d n=%d m=%d then %d" % (k, n, m_small, m_big), flush=True)
+    W = torch.from_numpy(synth.gen_weights(synth.Q4_K, rng, n, k)).cuda()
+    x = torch.from_numpy(synth.gen_x(rng, m_big, k)).cuda()
+    y = torch.zeros((m_big, n), dtype=torch.float32, device="cuda")
+
+    def call(m):
+        return lambda: qb.qmv_run_ex(synth.Q4_K, W.data_ptr(), x.data_ptr(), y.data_ptr(), k, n,
+                                     m, 0, n, 0, _stream(), qb.QMV_ALGO_MFMA)
+
+    want = torch.empty_like(y)
+    free0 = _free_after(call(m_small))  # kernels loaded, a small buffer cached
+    free1 = _free_after(call(m_big))
+    # about m_big * k * 4.2 bytes of staging were allocated (in an empty slot,
+    # or in place of a smaller buffer that an earlier test left)
+    assert free1 < free0
+    want.copy_(y)
+    for mm in (m_big, m_small, m_big):
+        assert _free_after(call(mm)) == free1
+    assert torch.equal(y.view(torch.int32), want.view(torch.int32))
+
+
+def test_scratch_cache_across_streams():
+    # alternating calls on two streams share the cached buffers; each result
+    # equals the same call made alone
+    rng = np.random.default_rng(59)
+    k, n, m = 4096, 384, 256
+    print("case scratch cache two streams q4_k k=%d n=%d m=%d" % (k, n, m), flush=True)
+    W = torch.from_numpy(synth.gen_weights(synth.Q4_K, rng, n, k)).cuda()
+    xs = [torch.from_numpy(synth.gen_x(rng, m, k)).cuda() for _ in range(4)]
+    alone = []
+    for x in xs:
+        y = torch.zeros((m, n), dtype=torch.float32, device="cuda")
+        assert qb.qmv_run_ex(synth.Q4_K, W.data_ptr(), x.data_ptr(), y.data_ptr(), k, n, m, 0, n,
+                             0, _stream(), qb.QMV_ALGO_MFMA) == qb.QMV_OK
+        alone.append(y)
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    outs = [torch.zeros((m, n), dtype=torch.float32, device="cuda") for _ in range(16)]
+    torch.cuda.synchronize()
+    for i, y in enumerate(outs):
+        x = xs[i % 4]
+        st = streams[i % 2]
+        assert qb.qmv_run_ex(synth.Q4_K, W.data_ptr(), x.data_ptr(), y.data_ptr(), k, n, m, 0, n,
+                             0, st.cuda_stream, qb.QMV_ALGO_MFMA) == qb.QMV_OK, qb.qmv_last_error()
+    torch.cuda.synchronize()
+    for i, y in enumerate(outs):
+        assert torch.equal(y.view(torch.int32), alone[i % 4].view(torch.int32)), i

@@ -4,9 +4,9 @@ through the C ABI.
 Both run the same kernels, so every output must be equal bit for bit (the
 float32 words compared as integers), on two calls in a row with the second
 smaller than the first (the fixed scratch keeps the first call's contents).
-The matrix-core family must take nothing from the device's stream-ordered
-memory pool, and a request whose staging exceeds the fixed scratch is refused
-on the host with y untouched.
+The matrix-core family must allocate no device memory (none from hipMalloc,
+none from the stream's memory pool), and a request whose staging exceeds the
+fixed scratch is refused on the host with y untouched.
 """
 import ctypes
 
@@ -91,15 +91,40 @@ def _used_high_after(hip, pool, fn):
     return high.value
 
 
-def test_noalloc_takes_no_pool_memory():
+def test_noalloc_takes_no_device_memory():
     k, n, m = 2048, 256, 48
-    print("case pool probe q4_k k=%d n=%d m=%d" % (k, n, m), flush=True)
+    print("case allocation probe q4_k k=%d n=%d m=%d" % (k, n, m), flush=True)
     W, x, base = _case(synth.Q4_K, k, n, m, seed=5)
     hip, pool = _pool()
-    args = (synth.Q4_K, W, x, base, k, n, m, qb.QMV_ALGO_MFMA, 0, n, 0)
-    # the probe sees the stream-ordered scratch of the allocating entry point
-    assert _used_high_after(hip, pool, lambda: _call(qb.qmv_run_ex, *args)) > 0
-    assert _used_high_after(hip, pool, lambda: _call(qb.qmv_run_noalloc, *args)) == 0
+    y = base.clone()
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def run(entry, mm):
+        rc = entry(synth.Q4_K, W.data_ptr(), x.data_ptr(), y.data_ptr(), k, n, mm, 0, n, 0,
+                   stream, qb.QMV_ALGO_MFMA)
+        assert rc == qb.QMV_OK, qb.qmv_last_error()
+
+    def free_after(fn):
+        torch.cuda.synchronize()
+        fn()
+        torch.cuda.synchronize()
+        return torch.cuda.mem_get_info()[0]
+
+    # the probe's positive control: run_ex with a request larger than any
+    # before it in this process grows the library's scratch cache (hipMalloc);
+    # the fixed scratch serves the same request with no allocation at all,
+    # from hipMalloc or from the stream's pool
+    big = 16384  # about 141 MB of staging, above any earlier request
+    xb = torch.zeros((big, k), dtype=torch.float32, device="cuda")
+    yb = torch.zeros((big, n), dtype=torch.float32, device="cuda")
+    free0 = free_after(lambda: None)
+    free1 = free_after(lambda: qb.qmv_run_ex(synth.Q4_K, W.data_ptr(), xb.data_ptr(),
+                                             yb.data_ptr(), k, n, big, 0, n, 0, stream,
+                                             qb.QMV_ALGO_MFMA))
+    assert free1 < free0
+    run(qb.qmv_run_noalloc, m)  # kernels loaded
+    assert free_after(lambda: run(qb.qmv_run_noalloc, m)) == free_after(lambda: None)
+    assert _used_high_after(hip, pool, lambda: run(qb.qmv_run_noalloc, m)) == 0
 
 
 def test_noalloc_refuses_oversize_staging():
