@@ -266,7 +266,7 @@ __device__ __forceinline__ void direct_body(const uint8_t *__restrict__ W,
     // loads exactly.
     typename F::Raw raw[RB][UPL];
     YPrefetch<MT, RB> yp;
-    int64_t base = j_start + (int64_t)blockIdx.x * rows_per_batch;
+    int64_t base = j_start + (int64_t)xcd_block(blockIdx.x, gridDim.x) * rows_per_batch;
     const uint8_t *last_row = W + (j_end - 1) * row_bytes;
     auto issue = [&](int64_t b) {
 #pragma unroll
@@ -413,7 +413,7 @@ __device__ __forceinline__ void staged_body(const uint8_t *__restrict__ W, int64
 
     typename F::X xu[MT][UPL];
     if (!XL) x_units_from_global<F, MT, UPL>(xu, x, k, U, ln.ulod);
-    int64_t base = j_start + (int64_t)blockIdx.x * rows_per_batch;
+    int64_t base = j_start + (int64_t)xcd_block(blockIdx.x, gridDim.x) * rows_per_batch;
     const int64_t b1 = base + stride;
     // Start-up: the first pieces of x and the old y of the first two batches
     // (accumulating) are requested, then both weight buffers are filled

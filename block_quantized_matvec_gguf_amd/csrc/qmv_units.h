@@ -966,6 +966,18 @@ struct Lanes {
 constexpr int STREAM_PER_CU = 2;
 constexpr int STREAM_PER_CU_4W = 4;
 
+// The dispatcher deals the workgroups of a launch to the 8 XCDs in turn
+// (workgroup b to XCD b % 8), and each XCD has its own L2. The streaming
+// kernels give consecutive batch numbers to workgroups of one XCD: XCD x's
+// workgroups x, x + 8, x + 16, ... become batches x*q + min(x, r), +1, +2, ...
+// (q = G / 8, r = G % 8, a bijection of [0, G)), so the y values of
+// neighbouring batches, which share cache lines, are written through one L2
+// instead of partial lines from several.
+__device__ __forceinline__ int xcd_block(int b, int G) {
+    const int q = G >> 3, r = G & 7, x = b & 7;
+    return x * q + (x < r ? x : r) + (b >> 3);
+}
+
 // Buffer descriptor over [p, p + bytes) (raw buffer loads check the range).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t batch_rsrc(const uint8_t *p, int bytes) {
     return __builtin_amdgcn_make_buffer_rsrc((void *)p, (short)0, bytes, 0x00020000);
