@@ -199,3 +199,88 @@ def test_scratch_cache_across_streams():
     torch.cuda.synchronize()
     for i, y in enumerate(outs):
         assert torch.equal(y.view(torch.int32), alone[i % 4].view(torch.int32)), i
+
+
+def test_scratch_cache_from_two_host_threads():
+    # two host threads, each with its own stream, call the matrix-core and
+    # transposed products at once; every result equals the same call made alone
+    import threading
+
+    rng = np.random.default_rng(61)
+    k, n, m = 2048, 320, 96
+    print("case scratch cache two threads q4_k k=%d n=%d m=%d" % (k, n, m), flush=True)
+    W = torch.from_numpy(synth.gen_weights(synth.Q4_K, rng, n, k)).cuda()
+    xs = [torch.from_numpy(synth.gen_x(rng, m, k)).cuda() for _ in range(2)]
+    dys = [torch.from_numpy(synth.gen_x(rng, 1, n)).cuda() for _ in range(2)]
+
+    def fwd(x, y, s):
+        return qb.qmv_run_ex(synth.Q4_K, W.data_ptr(), x.data_ptr(), y.data_ptr(), k, n, m, 0, n,
+                             0, s, qb.QMV_ALGO_MFMA)
+
+    def bwd(dy, dx, s):
+        return qb.qmv_run_t_ex(synth.Q4_K, W.data_ptr(), dy.data_ptr(), dx.data_ptr(), k, n, 1, 0,
+                               n, 0, s, qb.QMV_ALGO_GEMV)
+
+    alone_y, alone_dx = [], []
+    for i in range(2):
+        y = torch.zeros((m, n), dtype=torch.float32, device="cuda")
+        dx = torch.zeros((1, k), dtype=torch.float32, device="cuda")
+        assert fwd(xs[i], y, _stream()) == qb.QMV_OK
+        assert bwd(dys[i], dx, _stream()) == qb.QMV_OK
+        alone_y.append(y)
+        alone_dx.append(dx)
+    torch.cuda.synchronize()
+    calls = 12
+    outs = [[(torch.zeros((m, n), dtype=torch.float32, device="cuda"),
+              torch.zeros((1, k), dtype=torch.float32, device="cuda")) for _ in range(calls)]
+            for _ in range(2)]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    torch.cuda.synchronize()
+    errors = []
+
+    def worker(i):
+        try:
+            s = streams[i].cuda_stream
+            for y, dx in outs[i]:
+                rc = fwd(xs[i], y, s)
+                assert rc == qb.QMV_OK, qb.qmv_last_error()
+                rc = bwd(dys[i], dx, s)
+                assert rc == qb.QMV_OK, qb.qmv_last_error()
+        except Exception as e:  # reported by the main thread
+            errors.append(e)
+
+    threads = [threading.Thread(target=worker, args=(i,)) for i in range(2)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join(timeout=60)
+    torch.cuda.synchronize()
+    assert not errors, errors
+    for i in range(2):
+        for y, dx in outs[i]:
+            assert torch.equal(y.view(torch.int32), alone_y[i].view(torch.int32))
+            assert torch.equal(dx.view(torch.int32), alone_dx[i].view(torch.int32))
+
+
+def test_scratch_cache_on_per_thread_stream():
+    # hipStreamPerThread names a different stream in each thread: the cache
+    # orders such calls by events rather than by the handle
+    HIP_STREAM_PER_THREAD = 2
+    rng = np.random.default_rng(67)
+    k, n, m = 1024, 200, 64
+    print("case scratch cache per-thread stream q4_k k=%d n=%d m=%d" % (k, n, m), flush=True)
+    W = torch.from_numpy(synth.gen_weights(synth.Q4_K, rng, n, k)).cuda()
+    x = torch.from_numpy(synth.gen_x(rng, m, k)).cuda()
+    want = torch.zeros((m, n), dtype=torch.float32, device="cuda")
+    assert qb.qmv_run_ex(synth.Q4_K, W.data_ptr(), x.data_ptr(), want.data_ptr(), k, n, m, 0, n,
+                         0, _stream(), qb.QMV_ALGO_MFMA) == qb.QMV_OK
+    torch.cuda.synchronize()
+    outs = [torch.zeros((m, n), dtype=torch.float32, device="cuda") for _ in range(4)]
+    torch.cuda.synchronize()
+    for y in outs:
+        rc = qb.qmv_run_ex(synth.Q4_K, W.data_ptr(), x.data_ptr(), y.data_ptr(), k, n, m, 0, n, 0,
+                           HIP_STREAM_PER_THREAD, qb.QMV_ALGO_MFMA)
+        assert rc == qb.QMV_OK, qb.qmv_last_error()
+    torch.cuda.synchronize()
+    for y in outs:
+        assert torch.equal(y.view(torch.int32), want.view(torch.int32))
