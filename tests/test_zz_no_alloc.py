@@ -110,18 +110,21 @@ def test_noalloc_takes_no_device_memory():
         torch.cuda.synchronize()
         return torch.cuda.mem_get_info()[0]
 
-    # the probe's positive control: run_ex with a request larger than any
-    # before it in this process grows the library's scratch cache (hipMalloc);
-    # the fixed scratch serves the same request with no allocation at all,
-    # from hipMalloc or from the stream's pool
-    big = 16384  # about 141 MB of staging, above any earlier request
+    # the probe's positive control: run_ex on an empty scratch cache (the
+    # context released and taken again) grows it (hipMalloc); the fixed scratch
+    # serves the same request with no allocation at all, from hipMalloc or from
+    # the stream's pool
+    big = 16384  # about 141 MB of staging
     xb = torch.zeros((big, k), dtype=torch.float32, device="cuda")
     yb = torch.zeros((big, n), dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
+    qb.qmv_destroy()
+    assert qb.qmv_create() == qb.QMV_OK, qb.qmv_last_error()
     free0 = free_after(lambda: None)
     free1 = free_after(lambda: qb.qmv_run_ex(synth.Q4_K, W.data_ptr(), xb.data_ptr(),
                                              yb.data_ptr(), k, n, big, 0, n, 0, stream,
                                              qb.QMV_ALGO_MFMA))
-    assert free1 < free0
+    assert free0 - free1 >= big * k * 4
     run(qb.qmv_run_noalloc, m)  # kernels loaded
     assert free_after(lambda: run(qb.qmv_run_noalloc, m)) == free_after(lambda: None)
     assert _used_high_after(hip, pool, lambda: run(qb.qmv_run_noalloc, m)) == 0
