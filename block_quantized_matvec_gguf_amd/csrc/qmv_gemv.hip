@@ -633,20 +633,26 @@ bool plan_gemv(int fmt, int64_t k, int64_t rows, int mt_max, int num_cu, GemvPla
     g.per_cu = STREAM_PER_CU;
     // The waves of a workgroup are dealt to the compute unit's four SIMDs in
     // turn, so a workgroup of 4w+1 waves puts two waves of every workgroup on
-    // one SIMD, which then carries twice the decode work of the others. Where
-    // the row slots do not fill whole groups of four waves (e.g. 40 lanes per
-    // row: 8 slots = 5 waves) and the rows make at least 4 batches for each
-    // of 4 workgroups per compute unit, the workgroup is padded to 256
-    // threads with idle lanes past the last slot, if that idles at most 1/8
-    // of them. (Measured: Q6_K k=2560 x 262144 120 -> 113 us; the k=2560 x
-    // 10240 products, a few batches per workgroup, run 1-9% slower padded.)
+    // one SIMD, which then carries twice the decode work of the others, and
+    // every batch's barrier waits for it. Where the row slots do not fill
+    // whole groups of four waves (e.g. 40 lanes per row: 8 slots = 5 waves)
+    // the workgroup is padded with idle lanes past the last slot, if that
+    // idles at most 1/8 of them: to 256 threads (four per compute unit) where
+    // the rows make at least 4 batches for each of 4 workgroups per compute
+    // unit, else, for workgroups of 5-7 waves, to 512 threads (8 waves, two
+    // per SIMD, two workgroups per compute unit). (Measured: Q6_K k=2560 x
+    // 262144 120 -> 113 us with 256; the k=2560 x 10240 products, a few
+    // batches per workgroup, 1-9% slower with 256 and 4-25% faster with 512.)
     if (g.T % 256 != 0 && g.T > 64 && g.L <= 256) {
-        const int P4 = 256 / g.L;
+        const int P4 = 256 / g.L, P8 = 512 / g.L;
         if (P4 >= 1 && (256 - P4 * g.L) * 8 <= 256 &&
             (rows + P4 - 1) / P4 >= 16 * (int64_t)num_cu) {
             g.P = P4;
             g.T = 256;
             g.per_cu = STREAM_PER_CU_4W;
+        } else if (g.T > 256 && P8 >= 1 && (512 - P8 * g.L) * 8 <= 512) {
+            g.P = P8;
+            g.T = 512;
         }
     }
     g.MT = (g.UPL == 1 && mt_max >= 2) ? 2 : 1;

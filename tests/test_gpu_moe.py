@@ -168,3 +168,25 @@ def test_moe_padded_workgroups(fmt):
         qb.matvec(fmt, dev(W[e * slab:(e + 1) * slab]), dev(x[r // top_k]), k, n, y=yr)
         torch.cuda.synchronize()
         assert np.array_equal(yr.cpu().numpy()[0].view(np.uint32), y[r].view(np.uint32)), r
+
+
+@pytest.mark.parametrize("fmt", [Q4_K, BF16], ids=lambda f: synth.FORMAT_NAMES[f])
+def test_moe_eight_wave_workgroups(fmt):
+    """Experts of k=2560 x 4000 rows: a few batches per workgroup, so the
+    launch pads its 5-wave workgroups to 8 waves (12 row slots + 32 idle
+    lanes). Against the oracle, and every row bit-equal to qmv_run on that
+    expert's matrix."""
+    k, n, E, n_pos, top_k = 2560, 4000, 3, 2, 2
+    rc, g = qb.qmv_gemv_geometry(fmt, k, n, 1, 256)
+    assert rc == qb.QMV_OK and g["threads"] == 512 and g["slots"] == 12
+    rng = np.random.default_rng(310 + fmt)
+    W = synth.gen_weights(fmt, rng, n * E, k)
+    ids = [2, 0, 1, 2]
+    x = synth.gen_x(rng, n_pos, k)
+    y, _ = check_moe(fmt, W, ids, x, k, n, E, top_k)
+    slab = qb.qmv_weight_bytes(fmt, k, n)
+    for r, e in enumerate(ids):
+        yr = dev(np.zeros((1, n), np.float32))
+        qb.matvec(fmt, dev(W[e * slab:(e + 1) * slab]), dev(x[r // top_k]), k, n, y=yr)
+        torch.cuda.synchronize()
+        assert np.array_equal(yr.cpu().numpy()[0].view(np.uint32), y[r].view(np.uint32)), r

@@ -317,6 +317,18 @@ def test_padded_workgroups(fmt):
     assert np.array_equal(y_acc.view(np.uint32), (base + y_un).view(np.uint32))
 
 
+@pytest.mark.parametrize("fmt,k,n,m", [(Q6_K, 2560, 3000, 2), (Q4_K, 2560, 5000, 3),
+                                       (BF16, 2560, 4000, 2), (Q8_0, 2560, 3000, 1)],
+                         ids=lambda v: str(v))
+def test_eight_wave_workgroups(fmt, k, n, m):
+    """k=2560 (40 lanes per row) with a few batches per workgroup: the
+    5-wave workgroups are padded to 8 waves (12 row slots + 32 idle lanes),
+    one and several tokens, every output against the oracle."""
+    rc, g = qb.qmv_gemv_geometry(fmt, k, n, min(m, 2), 256)
+    assert rc == qb.QMV_OK and (g["threads"], g["slots"]) == (512, 12)
+    check_case(fmt, k, n, m, algo="gemv", seed=k + n + m)
+
+
 # ------------------------------------------------------- measured workloads
 
 @pytest.mark.parametrize("name", ["bf16_ffn_up", "f16_ffn_up", "q4_k_ffn_up", "q8_0_ffn_up",

@@ -243,7 +243,8 @@ def test_create_without_a_device(lib):
 def test_gemv_geometry(lib):
     """Host-side launch planning of the streaming GEMV family (no device):
     large launches of 40-lane rows pad their workgroups to 4 whole waves and
-    take four per compute unit; small ones keep their row-slot workgroups."""
+    take four per compute unit; small ones pad their 5-wave workgroups to 8
+    waves (two per SIMD) and take two per compute unit."""
     geo = qb.qmv_gemv_geometry
     rc, g = geo(qb.QMV_FMT_Q6_K, 2560, 262144, 1, 256)  # vocabulary projection
     assert rc == qb.QMV_OK
@@ -251,14 +252,14 @@ def test_gemv_geometry(lib):
                      tokens=1, per_cu=4, staged=1)
     rc, g = geo(qb.QMV_FMT_Q4_K, 2560, 10240, 1, 256)  # k=2560 x 10240: a few batches each
     assert rc == qb.QMV_OK
-    assert (g["threads"], g["slots"], g["lanes"], g["per_cu"]) == (320, 8, 40, 2)
+    assert (g["threads"], g["slots"], g["lanes"], g["per_cu"]) == (512, 12, 40, 2)
     rc, g = geo(qb.QMV_FMT_BF16, 2560, 262144, 1, 256)  # direct kernel, same padding
     assert (g["threads"], g["slots"], g["per_cu"], g["staged"]) == (256, 6, 4, 0)
     rc, g = geo(qb.QMV_FMT_Q4_K, 4096, 14336, 2, 256)  # 64 lanes: already whole waves
     assert (g["threads"], g["slots"], g["lanes"], g["tokens"], g["per_cu"]) == (256, 4, 64, 2, 2)
     # the padding threshold: at least 4 batches per workgroup at 4 per compute unit
     assert geo(qb.QMV_FMT_Q6_K, 2560, 6 * 4096, 1, 256)[1]["threads"] == 256
-    assert geo(qb.QMV_FMT_Q6_K, 2560, 6 * 4096 - 6, 1, 256)[1]["threads"] == 320
+    assert geo(qb.QMV_FMT_Q6_K, 2560, 6 * 4096 - 6, 1, 256)[1]["threads"] == 512
     assert geo(qb.QMV_FMT_Q6_K, 2560, 6 * 4096 + 5, 1, 256)[1]["threads"] == 256
     # invariants over shapes
     for fmt in (qb.QMV_FMT_Q4_0, qb.QMV_FMT_Q4_K, qb.QMV_FMT_Q6_K, qb.QMV_FMT_BF16,
@@ -273,8 +274,13 @@ def test_gemv_geometry(lib):
                     assert g["lanes"] * g["units_per_lane"] >= k // 64
                     if g["per_cu"] == 4:
                         assert g["threads"] == 256 and (256 - busy) * 8 <= 256
+                    elif g["threads"] == 512 and busy < 512:
+                        # 5-7 waves of row slots padded to 8 whole waves
+                        assert g["per_cu"] == 2 and (512 - busy) * 8 <= 512 and busy > 256
                     else:
                         assert g["per_cu"] == 2 and g["threads"] == busy
+                    # whole waves, or one partial wave of a workgroup below 256 threads
+                    assert g["threads"] % 256 == 0 or g["threads"] <= 256
     # shapes the streaming kernels do not take, and bad arguments
     assert geo(qb.QMV_FMT_F16, 96, 10, 1, 256)[0] == qb.QMV_ERR_UNSUPPORTED
     assert geo(qb.QMV_FMT_Q4_K, 2560, 0, 1, 256)[0] == qb.QMV_ERR_INVALID_ARGUMENT
