@@ -291,7 +291,9 @@ const char *qmv_moe_kernel_name(int format, int64_t k, int algo);
  * weights are staged through LDS (block formats) else 0. Threads past
  * slots*lanes are idle padding. Returns QMV_OK, QMV_ERR_INVALID_ARGUMENT for a
  * bad format, shape, count or null out, or QMV_ERR_UNSUPPORTED when the
- * streaming kernels do not cover the shape (the per-row kernel then runs). */
+ * streaming kernels do not cover the shape (the per-row kernel then runs). An
+ * expert-indexed launch (qmv_run_moe_ex) is planned with rows = n times the
+ * number of (position, slot) pairs. */
 int qmv_gemv_geometry(int format, int64_t k, int64_t rows, int64_t m_tokens, int num_cu,
                       int64_t *out);
 

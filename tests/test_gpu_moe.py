@@ -177,7 +177,8 @@ def test_moe_eight_wave_workgroups(fmt):
     lanes). Against the oracle, and every row bit-equal to qmv_run on that
     expert's matrix."""
     k, n, E, n_pos, top_k = 2560, 4000, 3, 2, 2
-    rc, g = qb.qmv_gemv_geometry(fmt, k, n, 1, 256)
+    # the launch is planned over all pairs' rows
+    rc, g = qb.qmv_gemv_geometry(fmt, k, n * n_pos * top_k, 1, 256)
     assert rc == qb.QMV_OK and g["threads"] == 512 and g["slots"] == 12
     rng = np.random.default_rng(310 + fmt)
     W = synth.gen_weights(fmt, rng, n * E, k)
