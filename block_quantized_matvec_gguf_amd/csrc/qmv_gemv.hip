@@ -642,7 +642,9 @@ bool plan_gemv(int fmt, int64_t k, int64_t rows, int mt_max, int num_cu, GemvPla
     // unit, else, for workgroups of 5-7 waves, to 512 threads (8 waves, two
     // per SIMD, two workgroups per compute unit). (Measured: Q6_K k=2560 x
     // 262144 120 -> 113 us with 256; the k=2560 x 10240 products, a few
-    // batches per workgroup, 1-9% slower with 256 and 4-25% faster with 512.)
+    // batches per workgroup, 1-9% slower with 256 and 4-25% faster with 512;
+    // k=2560 x 2560 and x 6144 13-25% faster with 512, x 4096 3-4% slower
+    // without the busy-units condition below.)
     if (g.T % 256 != 0 && g.T > 64 && g.L <= 256) {
         const int P4 = 256 / g.L, P8 = 512 / g.L;
         if (P4 >= 1 && (256 - P4 * g.L) * 8 <= 256 &&
@@ -651,8 +653,14 @@ bool plan_gemv(int fmt, int64_t k, int64_t rows, int mt_max, int num_cu, GemvPla
             g.T = 256;
             g.per_cu = STREAM_PER_CU_4W;
         } else if (g.T > 256 && P8 >= 1 && (512 - P8 * g.L) * 8 <= 512) {
-            g.P = P8;
-            g.T = 512;
+            // only where it keeps every compute unit busy: at least two
+            // batches per compute unit, or one round of workgroups where the
+            // unpadded slots needed a second
+            const int64_t b8 = (rows + P8 - 1) / P8, bp = (rows + g.P - 1) / g.P;
+            if (b8 >= 2 * (int64_t)num_cu || (b8 <= num_cu && bp > num_cu)) {
+                g.P = P8;
+                g.T = 512;
+            }
         }
     }
     g.MT = (g.UPL == 1 && mt_max >= 2) ? 2 : 1;

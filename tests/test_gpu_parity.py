@@ -317,8 +317,8 @@ def test_padded_workgroups(fmt):
     assert np.array_equal(y_acc.view(np.uint32), (base + y_un).view(np.uint32))
 
 
-@pytest.mark.parametrize("fmt,k,n,m", [(Q6_K, 2560, 3000, 2), (Q4_K, 2560, 5000, 3),
-                                       (BF16, 2560, 4000, 2), (Q8_0, 2560, 3000, 1)],
+@pytest.mark.parametrize("fmt,k,n,m", [(Q6_K, 2560, 3000, 2), (Q4_K, 2560, 6200, 3),
+                                       (BF16, 2560, 2600, 2), (Q8_0, 2560, 3000, 1)],
                          ids=lambda v: str(v))
 def test_eight_wave_workgroups(fmt, k, n, m):
     """k=2560 (40 lanes per row) with a few batches per workgroup: the
