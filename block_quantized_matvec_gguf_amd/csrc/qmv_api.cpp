@@ -241,6 +241,23 @@ const char *fmt_name(int fmt) {
     }
 }
 
+// Tokens from which AUTO takes the matrix-core family. The GEMV family reads
+// W once per two tokens, so its time grows with m, where the matrix-core
+// call costs about the same for 1 to 64 tokens; these are the smallest counts
+// at which the matrix cores win or come within ~10% on every shape measured
+// (k x n = 2560 x 10240, 2048 x 1536, 4096 x 4096, 4096 x 14336, 2560 x
+// 262144), e.g. Q4_K k=4096 x 14336 with 8 tokens: 69.5 us on the GEMV family,
+// 27.7 us on the matrix cores.
+int mfma_min_tokens(int fmt) {
+    switch (fmt) {
+    case qmv::FMT_Q4_K: return 5;
+    case qmv::FMT_Q8_0:
+    case qmv::FMT_F16:
+    case qmv::FMT_BF16: return 6;
+    default: return 8; // Q6_K, Q4_0, Q5_0: the costlier weight terms on the matrix cores
+    }
+}
+
 // Which kernel family a request resolves to; -1 when the explicit choice
 // cannot serve the shape.
 int resolve_algo(int fmt, int64_t k, int64_t m, int algo) {
@@ -249,7 +266,7 @@ int resolve_algo(int fmt, int64_t k, int64_t m, int algo) {
     const bool gemv_ok = qmv::plan_gemv(fmt, k, 1, 2, 256, &gp);
     switch (algo) {
     case QMV_ALGO_AUTO:
-        if (m >= 16 && mfma_ok) return QMV_ALGO_MFMA;
+        if (m >= mfma_min_tokens(fmt) && mfma_ok) return QMV_ALGO_MFMA;
         return gemv_ok ? QMV_ALGO_GEMV : QMV_ALGO_SIMPLE;
     case QMV_ALGO_GEMV: return gemv_ok ? QMV_ALGO_GEMV : -1;
     case QMV_ALGO_MFMA: return mfma_ok ? QMV_ALGO_MFMA : -1;

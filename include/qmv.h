@@ -132,8 +132,9 @@ int qmv_run(int format, const void *W, const float *x, float *y, int64_t k, int6
  * destroy a stream only after the library's work on it has completed. Under
  * graph capture of `stream` the call takes the buffer with hipMallocAsync /
  * hipFreeAsync on `stream` instead.
- * QMV_ALGO_AUTO takes it for m_tokens >= 16 when it applies and x is 16-byte
- * aligned, else the GEMV family. All families meet the same accuracy
+ * QMV_ALGO_AUTO takes it when it applies, x is 16-byte aligned and m_tokens is
+ * at least 5 (Q4_K), 6 (Q8_0, F16, BF16) or 8 (Q6_K, Q4_0, Q5_0), else the
+ * GEMV family (which reads W once per two tokens). All families meet the same accuracy
  * contract; they may differ in the last bits. */
 int qmv_run_ex(int format, const void *W, const float *x, float *y, int64_t k, int64_t n,
                int64_t m_tokens, int64_t j_start, int64_t j_end, int accumulate,
