@@ -468,6 +468,14 @@ int run_impl(int format, const void *W, const float *x, float *y, int64_t k, int
         a = resolve_algo(format, k, 1, QMV_ALGO_AUTO);
     }
     const int64_t rows = j_end - j_start;
+    if (a == QMV_ALGO_MFMA && fixed_scratch && algo == QMV_ALGO_AUTO) {
+        // AUTO under the fixed scratch: a staging buffer that does not fit
+        // sends the request to the GEMV family instead of failing
+        qmv::MfmaPlan p;
+        if (qmv::plan_mfma(format, k, rows, m_tokens, num_cu, &p) &&
+            qmv::mfma_scratch_bytes(p, k) > qmv::STATIC_SCRATCH_BYTES)
+            a = resolve_algo(format, k, 1, QMV_ALGO_AUTO);
+    }
     if (a == QMV_ALGO_SIMPLE) {
         e = qmv::launch_simple(format, Wb, x, y, k, n, m_tokens, rb, j_start, j_end,
                                accumulate, s);

@@ -147,7 +147,8 @@ int qmv_run_ex(int format, const void *W, const float *x, float *y, int64_t k, i
  * fixed buffer of QMV_NOALLOC_SCRATCH_BYTES in each device's memory, set up by
  * qmv_create and held until the process ends; a call whose staging would need
  * more (about m_tokens*k*4.2 bytes, m_tokens rounded up to 64) fails with
- * QMV_ERR_UNSUPPORTED before anything is enqueued. Every call on a device
+ * QMV_ERR_UNSUPPORTED before anything is enqueued when QMV_ALGO_MFMA was asked
+ * for; QMV_ALGO_AUTO then runs the GEMV family instead. Every call on a device
  * shares that device's buffer and leaves its contents behind (each call
  * rewrites all it reads): matrix-core calls that overlap in time on one
  * device, e.g. on two streams, race and give wrong results. */

@@ -146,3 +146,15 @@ def test_noalloc_refuses_oversize_staging():
     assert "scratch" in qb.qmv_last_error()
     torch.cuda.synchronize()
     assert bool((y == SENTINEL).all())
+
+
+def test_noalloc_auto_falls_back_when_staging_does_not_fit():
+    # 8 tokens of k=65536 would need about 17.6 MB of matrix-core staging, more
+    # than the fixed scratch: AUTO then runs the GEMV family, bit for bit
+    # what qmv_run_ex gives with QMV_ALGO_GEMV
+    k, n, m = 65536, 40, 8
+    print("case auto fallback q4_k k=%d n=%d m=%d" % (k, n, m), flush=True)
+    W, x, base = _case(synth.Q4_K, k, n, m, seed=13)
+    want = _call(qb.qmv_run_ex, synth.Q4_K, W, x, base, k, n, m, qb.QMV_ALGO_GEMV, 0, n, 0)
+    got = _call(qb.qmv_run_noalloc, synth.Q4_K, W, x, base, k, n, m, qb.QMV_ALGO_AUTO, 0, n, 0)
+    assert torch.equal(got.view(torch.int32), want.view(torch.int32))
