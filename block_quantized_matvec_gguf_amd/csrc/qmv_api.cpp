@@ -243,18 +243,21 @@ const char *fmt_name(int fmt) {
 
 // Tokens from which AUTO takes the matrix-core family. The GEMV family reads
 // W once per two tokens, so its time grows with m, where the matrix-core
-// call costs about the same for 1 to 64 tokens; these are the smallest counts
-// at which the matrix cores win or come within ~10% on every shape measured
-// (k x n = 2560 x 10240, 2048 x 1536, 4096 x 4096, 4096 x 14336, 2560 x
-// 262144), e.g. Q4_K k=4096 x 14336 with 8 tokens: 69.5 us on the GEMV family,
-// 27.7 us on the matrix cores.
+// call costs about the same for 1 to 32 tokens (one 32-token tile per
+// workgroup) and again for 33 to 64; these are the smallest counts at which
+// the matrix cores win or come within ~10% on every shape measured (k x n =
+// 2560 x 10240, 2048 x 1536, 4096 x 4096, 4096 x 14336, 2560 x 262144), e.g.
+// Q4_K k=4096 x 14336 with 3 tokens: 29.5 us on the GEMV family, 21 us on the
+// matrix cores; with 8 tokens 69.5 and 21 us.
 int mfma_min_tokens(int fmt) {
     switch (fmt) {
-    case qmv::FMT_Q4_K: return 5;
+    case qmv::FMT_Q4_K: return 3;
     case qmv::FMT_Q8_0:
     case qmv::FMT_F16:
-    case qmv::FMT_BF16: return 6;
-    default: return 8; // Q6_K, Q4_0, Q5_0: the costlier weight terms on the matrix cores
+    case qmv::FMT_BF16: return 5;
+    case qmv::FMT_Q4_0:
+    case qmv::FMT_Q5_0: return 6;
+    default: return 8; // Q6_K: its weights take three matrix-core terms and a costlier decode
     }
 }
 

@@ -278,6 +278,9 @@ __device__ __forceinline__ void scale_min(const u32x4 &h, int g, uint32_t &sc, u
     }
 }
 
+// TT: 32-token tiles per workgroup (2; 1 when the call has at most 32 tokens,
+// which skips the operand loads and MFMAs of the empty second half)
+template <int TT>
 __global__ __launch_bounds__(NT, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) void qmv_mfma_q4_k(const uint8_t *__restrict__ W,
                                                        const uint8_t *__restrict__ xs,
                                                        const uint8_t *__restrict__ sm,
@@ -328,9 +331,9 @@ __global__ __launch_bounds__(NT, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) v
                 poff[i], ok ? SBB * s : 0, 0, 2 /* nontemporal */);
     };
 
-    f32x16 acc[2][2];
+    f32x16 acc[TT][2];
 #pragma unroll
-    for (int a = 0; a < 2; a++)
+    for (int a = 0; a < TT; a++)
 #pragma unroll
         for (int b = 0; b < 2; b++)
 #pragma unroll
@@ -346,11 +349,11 @@ __global__ __launch_bounds__(NT, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) v
         (void *)(xs + (size_t)T * nsb * 65536), (short)0, nsb * 65536, 0x00020000);
     const __amdgpu_buffer_rsrc_t sr = __builtin_amdgcn_make_buffer_rsrc(
         (void *)(sm + (size_t)T * nsb * 2048), (short)0, nsb * 2048, 0x00020000);
-    f16x8 ring[RING][2][2];
+    f16x8 ring[RING][TT][2];
     auto load_a = [&](int s, int j, int bi) {
         const bool ok = s >= 0;
 #pragma unroll
-        for (int a = 0; a < 4; a++)
+        for (int a = 0; a < 2 * TT; a++)
             ring[bi][a >> 1][a & 1] = __builtin_bit_cast(
                 f16x8, __builtin_amdgcn_raw_buffer_load_b128(ok ? xr : rnull, lane * 16,
                                                              ok ? s * 65536 + 4096 * j + 1024 * a : 0, 0));
@@ -362,15 +365,15 @@ __global__ __launch_bounds__(NT, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) v
         for (int j = 0; j < PF; j++) load_a(s0, j, j);
     }
     auto super_block = [&](int s, const uint8_t *cur_slot, uint8_t *nxt) {
-        // this super-block's bytes have landed once at most the 4*PF operand
+        // this super-block's bytes have landed once at most the 2*TT*PF operand
         // loads issued after its copy are outstanding (loads complete in order)
-        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(4 * PF) : "memory");
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * TT * PF) : "memory");
         const int sn = s + KW < nsb ? s + KW : -1;
         copy_sb(sn, nxt);
         // the sub-block sums of x for the min term, needed at the end
-        f16x8 am[2];
+        f16x8 am[TT];
 #pragma unroll
-        for (int tt = 0; tt < 2; tt++)
+        for (int tt = 0; tt < TT; tt++)
             am[tt] = __builtin_bit_cast(
                 f16x8, __builtin_amdgcn_raw_buffer_load_b128(sr, lane * 16, s * 2048 + 1024 * tt, 0));
         const uint8_t *wsb = cur_slot;
@@ -383,7 +386,7 @@ __global__ __launch_bounds__(NT, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) v
             dd[rt] = h2f(hd[rt][0]);
             dm[rt] = h2f(hd[rt][0] >> 16);
         }
-        f32x16 tile[2][2];
+        f32x16 tile[TT][2];
 #pragma unroll
         for (int g = 0; g < 8; g++) {
             const int c = g >> 1, hn = g & 1;
@@ -419,7 +422,7 @@ __global__ __launch_bounds__(NT, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) v
 #pragma unroll
                 for (int h = 0; h < 2; h++)
 #pragma unroll
-                    for (int tt = 0; tt < 2; tt++)
+                    for (int tt = 0; tt < TT; tt++)
 #pragma unroll
                         for (int rt = 0; rt < 2; rt++)
                             tile[tt][rt] = mfma(ring[cur][tt][h], b[rt],
@@ -437,7 +440,7 @@ __global__ __launch_bounds__(NT, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) v
                 mins[rt][g] = (_Float16)(float)mn;
             }
 #pragma unroll
-        for (int tt = 0; tt < 2; tt++) {
+        for (int tt = 0; tt < TT; tt++) {
 #pragma unroll
             for (int rt = 0; rt < 2; rt++) {
                 const f32x16 mt = mfma(am[tt], mins[rt], f32x16{});
@@ -463,12 +466,13 @@ __global__ __launch_bounds__(NT, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) v
     float *red0 = (float *)&slot0[0][0], *red1 = (float *)&slot1[0][0];
     float *mine = (wave < KW / 2 ? red0 : red1) + (size_t)(wave % (KW / 2)) * TM * TN;
 #pragma unroll
-    for (int tt = 0; tt < 2; tt++)
+    for (int tt = 0; tt < TT; tt++)
 #pragma unroll
         for (int rt = 0; rt < 2; rt++)
 #pragma unroll
             for (int r = 0; r < 16; r++)
                 mine[((tt * 2 + rt) * 16 + r) * 64 + lane] = acc[tt][rt][r];
+    // (with TT = 1 the second half's slots hold nothing: no token there is stored)
     __syncthreads();
     tile_store(red0, red1, pe, y, T, n, m, r0, rows, accumulate, tid);
 }
@@ -676,7 +680,8 @@ __device__ __forceinline__ f32x16 mfma_bf(u32x4 a, u32x4 b, f32x16 c) {
 // ..., copies its chunk's 64 rows into one of its two LDS slots (NP 16-byte
 // pieces per row, one chunk ahead) and loads its A operands six K-steps ahead
 // from the staged x; the four waves' tiles are summed in LDS at the end.
-template <class D>
+// TT: 32-token tiles per workgroup (as for Q4_K)
+template <class D, int TT>
 __device__ __forceinline__ void hl_body(const uint8_t *__restrict__ W, const uint8_t *__restrict__ xs,
                                         const int *__restrict__ pe, float *__restrict__ y,
                                         int64_t k, int64_t n, int64_t m, int64_t row_bytes,
@@ -730,20 +735,21 @@ __device__ __forceinline__ void hl_body(const uint8_t *__restrict__ W, const uin
     // in-piece offset of this lane's two rows' chunk c
     const int rb0 = lead + nl * (int)row_bytes, rb1 = rb0 + 32 * (int)row_bytes;
 
-    f32x16 acc[2][2];
+    f32x16 acc[TT][2];
 #pragma unroll
-    for (int a = 0; a < 2; a++)
+    for (int a = 0; a < TT; a++)
 #pragma unroll
         for (int b = 0; b < 2; b++) acc[a][b] = f32x16{};
 
-    // staged x: 4 KB per K-step (both token tiles, hi and lo), K-steps in order
+    // staged x: 4 KB per K-step (both token tiles, hi and lo), K-steps in
+    // order; with TT = 1 only the first 2 KB of each are read
     const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
         (void *)(xs + (size_t)T * (k >> 4) * 4096), (short)0, (int)((k >> 4) * 4096), 0x00020000);
-    u32x4 ring[RING][2][2];
+    u32x4 ring[RING][TT][2];
     auto load_a = [&](int c, int j, int bi) {
         const bool ok = c >= 0;
 #pragma unroll
-        for (int a = 0; a < 4; a++)
+        for (int a = 0; a < 2 * TT; a++)
             ring[bi][a >> 1][a & 1] = __builtin_bit_cast(
                 u32x4, __builtin_amdgcn_raw_buffer_load_b128(
                            ok ? xr : rnull, lane * 16, ok ? (c * NJ + j) * 4096 + 1024 * a : 0, 0));
@@ -755,9 +761,9 @@ __device__ __forceinline__ void hl_body(const uint8_t *__restrict__ W, const uin
         for (int j = 0; j < PF; j++) load_a(c0, j, j);
     }
     auto chunk = [&](int c, const uint8_t *cur_slot, uint8_t *nxt) {
-        // this chunk's bytes have landed once at most the 4*PF operand loads
-        // issued after its copy are outstanding (loads complete in order)
-        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(4 * PF) : "memory");
+        // this chunk's bytes have landed once at most the 2*TT*PF operand
+        // loads issued after its copy are outstanding (loads complete in order)
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * TT * PF) : "memory");
         const int cn = c + KW < nch ? c + KW : -1;
         copy_chunk(cn, nxt);
         const uint8_t *rowp[2] = {cur_slot + nl * RS, cur_slot + (nl + 32) * RS};
@@ -779,7 +785,7 @@ __device__ __forceinline__ void hl_body(const uint8_t *__restrict__ W, const uin
 #pragma unroll
             for (int term = 0; term < (D::LO ? 3 : 2); term++)
 #pragma unroll
-                for (int tt = 0; tt < 2; tt++)
+                for (int tt = 0; tt < TT; tt++)
 #pragma unroll
                     for (int rt = 0; rt < 2; rt++) {
                         const u32x4 av = ring[cur][tt][term == 1 ? 1 : 0];
@@ -805,22 +811,24 @@ __device__ __forceinline__ void hl_body(const uint8_t *__restrict__ W, const uin
     float *red0 = (float *)&slot0[0][0], *red1 = (float *)&slot1[0][0];
     float *mine = (wave < KW / 2 ? red0 : red1) + (size_t)(wave % (KW / 2)) * TM * TN;
 #pragma unroll
-    for (int tt = 0; tt < 2; tt++)
+    for (int tt = 0; tt < TT; tt++)
 #pragma unroll
         for (int rt = 0; rt < 2; rt++)
 #pragma unroll
             for (int r = 0; r < 16; r++)
                 mine[((tt * 2 + rt) * 16 + r) * 64 + lane] = acc[tt][rt][r];
+    // (with TT = 1 the second half's slots hold nothing: no token there is stored)
     __syncthreads();
     tile_store(red0, red1, pe, y, T, n, m, r0, rows, accumulate, tid);
 }
 
 #define QMV_MFMA_HL_KERNEL(NAME, D)                                                              \
+    template <int TT>                                                                            \
     __global__ __launch_bounds__(NT, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) void NAME(    \
         const uint8_t *__restrict__ W, const uint8_t *__restrict__ xs,                           \
         const int *__restrict__ pe, float *__restrict__ y, int64_t k, int64_t n, int64_t m,      \
         int64_t row_bytes, int64_t j_start, int64_t j_end, int accumulate) {                     \
-        hl_body<D>(W, xs, pe, y, k, n, m, row_bytes, j_start, j_end, accumulate);                \
+        hl_body<D, TT>(W, xs, pe, y, k, n, m, row_bytes, j_start, j_end, accumulate);            \
     }
 QMV_MFMA_HL_KERNEL(qmv_mfma_q4_0, DQ4_0)
 QMV_MFMA_HL_KERNEL(qmv_mfma_q5_0, DQ5_0)
@@ -901,17 +909,29 @@ hipError_t launch_mfma_ws(const MfmaPlan &p, const uint8_t *W, const float *x, f
         hipLaunchKernelGGL(qmv_mfma_prep_x<false>, pg, dim3(64), 0, stream, x, k, m, xs, sm, pe);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    // one 32-token tile per workgroup when the call has at most 32 tokens
+    const bool one = m <= TM / 2;
     switch (p.fmt) {
     case FMT_Q4_K:
-        launch_stop(qmv_mfma_q4_k, dim3(p.tiles_n, p.tiles_m), dim3(NT), 0, stream, stop, W, xs,
-                    sm, pe, y, k, n, m, row_bytes, j_start, j_end, accumulate);
+        if (one)
+            launch_stop(qmv_mfma_q4_k<1>, dim3(p.tiles_n, p.tiles_m), dim3(NT), 0, stream, stop, W,
+                        xs, sm, pe, y, k, n, m, row_bytes, j_start, j_end, accumulate);
+        else
+            launch_stop(qmv_mfma_q4_k<2>, dim3(p.tiles_n, p.tiles_m), dim3(NT), 0, stream, stop, W,
+                        xs, sm, pe, y, k, n, m, row_bytes, j_start, j_end, accumulate);
         break;
-    case FMT_Q4_0: launch_hl(qmv_mfma_q4_0, p, W, xs, pe, y, k, n, m, row_bytes, j_start, j_end, accumulate, stream, stop); break;
-    case FMT_Q5_0: launch_hl(qmv_mfma_q5_0, p, W, xs, pe, y, k, n, m, row_bytes, j_start, j_end, accumulate, stream, stop); break;
-    case FMT_Q8_0: launch_hl(qmv_mfma_q8_0, p, W, xs, pe, y, k, n, m, row_bytes, j_start, j_end, accumulate, stream, stop); break;
-    case FMT_Q6_K: launch_hl(qmv_mfma_q6_k, p, W, xs, pe, y, k, n, m, row_bytes, j_start, j_end, accumulate, stream, stop); break;
-    case FMT_F16: launch_hl(qmv_mfma_f16, p, W, xs, pe, y, k, n, m, row_bytes, j_start, j_end, accumulate, stream, stop); break;
-    case FMT_BF16: launch_hl(qmv_mfma_bf16, p, W, xs, pe, y, k, n, m, row_bytes, j_start, j_end, accumulate, stream, stop); break;
+#define QMV_HL(K)                                                                                \
+    (one ? launch_hl(K<1>, p, W, xs, pe, y, k, n, m, row_bytes, j_start, j_end, accumulate,       \
+                     stream, stop)                                                                \
+         : launch_hl(K<2>, p, W, xs, pe, y, k, n, m, row_bytes, j_start, j_end, accumulate,       \
+                     stream, stop))
+    case FMT_Q4_0: QMV_HL(qmv_mfma_q4_0); break;
+    case FMT_Q5_0: QMV_HL(qmv_mfma_q5_0); break;
+    case FMT_Q8_0: QMV_HL(qmv_mfma_q8_0); break;
+    case FMT_Q6_K: QMV_HL(qmv_mfma_q6_k); break;
+    case FMT_F16: QMV_HL(qmv_mfma_f16); break;
+    case FMT_BF16: QMV_HL(qmv_mfma_bf16); break;
+#undef QMV_HL
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

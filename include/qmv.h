@@ -133,7 +133,7 @@ int qmv_run(int format, const void *W, const float *x, float *y, int64_t k, int6
  * graph capture of `stream` the call takes the buffer with hipMallocAsync /
  * hipFreeAsync on `stream` instead.
  * QMV_ALGO_AUTO takes it when it applies, x is 16-byte aligned and m_tokens is
- * at least 5 (Q4_K), 6 (Q8_0, F16, BF16) or 8 (Q6_K, Q4_0, Q5_0), else the
+ * at least 3 (Q4_K), 5 (Q8_0, F16, BF16), 6 (Q4_0, Q5_0) or 8 (Q6_K), else the
  * GEMV family (which reads W once per two tokens). All families meet the same accuracy
  * contract; they may differ in the last bits. */
 int qmv_run_ex(int format, const void *W, const float *x, float *y, int64_t k, int64_t n,

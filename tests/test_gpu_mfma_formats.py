@@ -115,3 +115,19 @@ def test_mfma_format_agrees_with_gemv(fmt):
     yref, sref = oracle.gemv(fmt, W, x, k, n)
     assert oracle.check_parity(y_m, yref, sref)["ok"]
     assert oracle.check_parity(y_g, yref, sref)["ok"]
+
+
+@pytest.mark.parametrize("fmt", [synth.Q4_K] + FORMATS, ids=names)
+def test_mfma_one_token_tile_equals_two(fmt):
+    """Calls of at most 32 tokens run one 32-token tile per workgroup; each
+    token's sums are the same operations as in a two-tile call, so the 20
+    tokens of a 20-token call equal, bit for bit, the first 20 of a 40-token
+    call on the same x (within tolerance of the oracle through the other
+    tests)."""
+    k, n = 2560, 200
+    print("case one tile fmt=%s k=%d n=%d" % (names(fmt), k, n), flush=True)
+    W, x = gen(fmt, k, n, 40, 900 + fmt)
+    Wd = dev(W)
+    y40 = run_gpu(fmt, W, x, k, n, np.zeros((40, n), np.float32), algo="mfma", Wd=Wd)
+    y20 = run_gpu(fmt, W, x[:20].copy(), k, n, np.zeros((20, n), np.float32), algo="mfma", Wd=Wd)
+    assert np.array_equal(y20.view(np.uint32), y40[:20].view(np.uint32))

@@ -74,12 +74,16 @@ def test_kernel_names(lib):
     assert qb.qmv_kernel_name(qb.QMV_FMT_Q4_K, 300, 1) == ""
     # prefill-sized token counts go to the matrix-core kernel where it applies
     assert qb.qmv_kernel_name(qb.QMV_FMT_Q4_K, 4096, 64) == "qmv_mfma<q4_k>"
-    # AUTO moves to the matrix cores from 5 (Q4_K), 6 (Q8_0, F16, BF16) or 8 tokens
-    assert qb.qmv_kernel_name(qb.QMV_FMT_Q4_K, 4096, 4) == "qmv_gemv_staged<q4_k>"
-    assert qb.qmv_kernel_name(qb.QMV_FMT_Q4_K, 4096, 5) == "qmv_mfma<q4_k>"
-    assert qb.qmv_kernel_name(qb.QMV_FMT_Q8_0, 4096, 5) == "qmv_gemv_staged<q8_0>"
-    assert qb.qmv_kernel_name(qb.QMV_FMT_Q8_0, 4096, 6) == "qmv_mfma<q8_0>"
-    assert qb.qmv_kernel_name(qb.QMV_FMT_BF16, 4096, 6) == "qmv_mfma<bf16>"
+    # AUTO moves to the matrix cores from 3 (Q4_K), 5 (Q8_0, F16, BF16), 6 (Q4_0,
+    # Q5_0) or 8 (Q6_K) tokens
+    assert qb.qmv_kernel_name(qb.QMV_FMT_Q4_K, 4096, 2) == "qmv_gemv_staged<q4_k>"
+    assert qb.qmv_kernel_name(qb.QMV_FMT_Q4_K, 4096, 3) == "qmv_mfma<q4_k>"
+    assert qb.qmv_kernel_name(qb.QMV_FMT_Q8_0, 4096, 4) == "qmv_gemv_staged<q8_0>"
+    assert qb.qmv_kernel_name(qb.QMV_FMT_Q8_0, 4096, 5) == "qmv_mfma<q8_0>"
+    assert qb.qmv_kernel_name(qb.QMV_FMT_BF16, 4096, 4) == "qmv_gemv_direct<bf16>"
+    assert qb.qmv_kernel_name(qb.QMV_FMT_BF16, 4096, 5) == "qmv_mfma<bf16>"
+    assert qb.qmv_kernel_name(qb.QMV_FMT_Q4_0, 4096, 5) == "qmv_gemv_staged<q4_0>"
+    assert qb.qmv_kernel_name(qb.QMV_FMT_Q4_0, 4096, 6) == "qmv_mfma<q4_0>"
     assert qb.qmv_kernel_name(qb.QMV_FMT_Q6_K, 4096, 7) == "qmv_gemv_staged<q6_k>"
     assert qb.qmv_kernel_name(qb.QMV_FMT_Q6_K, 4096, 8) == "qmv_mfma<q6_k>"
     assert qb.qmv_kernel_name(qb.QMV_FMT_Q4_K, 256, 1, qb.QMV_ALGO_MFMA) == "qmv_mfma<q4_k>"
@@ -92,8 +96,8 @@ def test_kernel_names(lib):
     assert qb.qmv_kernel_name(qb.QMV_FMT_BF16, 2496, 64, qb.QMV_ALGO_MFMA) == ""
     assert qb.qmv_kernel_name(qb.QMV_FMT_Q8_0, 2560, 1) == "qmv_gemv_staged<q8_0>"
     assert qb.qmv_kernel_name(qb.QMV_FMT_Q5_0, 2560, 1) == "qmv_gemv_staged<q5_0>"
-    assert qb.qmv_kernel_name(qb.QMV_FMT_Q5_0, 2560, 7) == "qmv_gemv_staged<q5_0>"
-    assert qb.qmv_kernel_name(qb.QMV_FMT_Q5_0, 2560, 8) == "qmv_mfma<q5_0>"
+    assert qb.qmv_kernel_name(qb.QMV_FMT_Q5_0, 2560, 5) == "qmv_gemv_staged<q5_0>"
+    assert qb.qmv_kernel_name(qb.QMV_FMT_Q5_0, 2560, 6) == "qmv_mfma<q5_0>"
     assert qb.qmv_kernel_name(qb.QMV_FMT_Q8_0, 32, 1) == "qmv_simple"
 
 
