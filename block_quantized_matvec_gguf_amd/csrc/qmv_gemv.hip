@@ -637,30 +637,34 @@ bool plan_gemv(int fmt, int64_t k, int64_t rows, int mt_max, int num_cu, GemvPla
     // every batch's barrier waits for it. Where the row slots do not fill
     // whole groups of four waves (e.g. 40 lanes per row: 8 slots = 5 waves)
     // the workgroup is padded with idle lanes past the last slot, if that
-    // idles at most 1/8 of them: to 256 threads (four per compute unit) where
-    // the rows make at least 4 batches for each of 4 workgroups per compute
-    // unit, else, for workgroups of 5-7 waves, to 512 threads (8 waves, two
-    // per SIMD, two workgroups per compute unit). (Measured: Q6_K k=2560 x
-    // 262144 120 -> 113 us with 256; the k=2560 x 10240 products, a few
-    // batches per workgroup, 1-9% slower with 256 and 4-25% faster with 512;
-    // k=2560 x 2560 and x 6144 13-25% faster with 512, x 4096 3-4% slower
-    // without the busy-units condition below.)
+    // idles at most 1/8 of them: workgroups of 5-7 waves to 512 threads (8
+    // waves, two per SIMD, two workgroups per compute unit) where that keeps
+    // every compute unit busy (at least two batches per compute unit, or one
+    // round of workgroups where the unpadded slots needed two); the direct
+    // kernel's launches with at least 4 batches for each of 4 workgroups per
+    // compute unit to 256 threads instead (four per compute unit). Measured,
+    // k=2560 (40 lanes): the vocabulary products (262144 rows) Q6_K 120 us
+    // unpadded, 113 with 256, 89.7-90.0 against 92.3-92.5 us with 512 rather
+    // than 256 (Q4_K 70.1 against 73.3-74.6; BF16 with 512: 8 tiles 3%
+    // slower); the 10240-row products 1-9% slower with 256 and 4-25% faster
+    // with 512; 2560 and 6144 rows 13-25% faster with 512, 4096 rows 3-4%
+    // slower without the busy-units condition.
     if (g.T % 256 != 0 && g.T > 64 && g.L <= 256) {
         const int P4 = 256 / g.L, P8 = 512 / g.L;
-        if (P4 >= 1 && (256 - P4 * g.L) * 8 <= 256 &&
-            (rows + P4 - 1) / P4 >= 16 * (int64_t)num_cu) {
+        const bool many = P4 >= 1 && (256 - P4 * g.L) * 8 <= 256 &&
+                          (rows + P4 - 1) / P4 >= 16 * (int64_t)num_cu;
+        bool pad8 = g.T > 256 && P8 >= 1 && (512 - P8 * g.L) * 8 <= 512;
+        if (pad8) {
+            const int64_t b8 = (rows + P8 - 1) / P8, bp = (rows + g.P - 1) / g.P;
+            pad8 = b8 >= 2 * (int64_t)num_cu || (b8 <= num_cu && bp > num_cu);
+        }
+        if (pad8 && (staged_format(fmt) || !many)) {
+            g.P = P8;
+            g.T = 512;
+        } else if (many) {
             g.P = P4;
             g.T = 256;
             g.per_cu = STREAM_PER_CU_4W;
-        } else if (g.T > 256 && P8 >= 1 && (512 - P8 * g.L) * 8 <= 512) {
-            // only where it keeps every compute unit busy: at least two
-            // batches per compute unit, or one round of workgroups where the
-            // unpadded slots needed a second
-            const int64_t b8 = (rows + P8 - 1) / P8, bp = (rows + g.P - 1) / g.P;
-            if (b8 >= 2 * (int64_t)num_cu || (b8 <= num_cu && bp > num_cu)) {
-                g.P = P8;
-                g.T = 512;
-            }
         }
     }
     g.MT = (g.UPL == 1 && mt_max >= 2) ? 2 : 1;

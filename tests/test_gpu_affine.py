@@ -132,7 +132,8 @@ def test_affine_ffn_workload():
 @pytest.mark.parametrize("bits", [4, 8])
 def test_affine_padded_workgroups(bits):
     """k=2560 with enough rows that the launch pads its workgroups to 256
-    threads (6 row slots + 16 idle lanes): every output against the oracle,
+    threads (6 row slots + 16 idle lanes; the direct body's layout for 4096+
+    batches): every output against the oracle,
     and every bit equal to row tiles of 2048 (unpadded launches)."""
     k, n, m = 2560, 6 * 4096 + 5, 1
     arrays = gen_a(bits, k, n, m, 31 + bits)

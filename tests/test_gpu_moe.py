@@ -153,8 +153,9 @@ def test_moe_decode_workload():
 
 @pytest.mark.parametrize("fmt", [Q6_K, BF16], ids=lambda f: synth.FORMAT_NAMES[f])
 def test_moe_padded_workgroups(fmt):
-    """Experts of k=2560 x 24581 rows: the launch pads its workgroups to 256
-    threads (6 row slots + 16 idle lanes). Against the oracle, and every row
+    """Experts of k=2560 x 24581 rows: the launch pads its workgroups (Q6_K:
+    512 threads, 12 row slots + 32 idle lanes; BF16: 256 threads, 6 slots +
+    16 idle lanes). Against the oracle, and every row
     bit-equal to qmv_run on that expert's matrix."""
     k, n, E, n_pos, top_k = 2560, 6 * 4096 + 5, 2, 1, 2
     rng = np.random.default_rng(300 + fmt)

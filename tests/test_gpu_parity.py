@@ -292,8 +292,9 @@ def test_run_to_run_determinism():
 @pytest.mark.parametrize("fmt", ALL_FORMATS, ids=lambda f: synth.FORMAT_NAMES[f])
 def test_padded_workgroups(fmt):
     """k=2560 (40 lanes per row) with enough rows that the streaming kernels
-    pad their workgroups to 256 threads (6 row slots + 16 idle lanes; 4096+
-    batches): sampled rows against the oracle, every bit equal to row tiles of
+    pad their workgroups (block formats: 512 threads, 12 row slots + 32 idle
+    lanes; the direct kernel, 4096+ batches: 256 threads, 6 slots + 16 idle
+    lanes): sampled rows against the oracle, every bit equal to row tiles of
     2048 (unpadded launches), and accumulate over the full range equal to
     base + untiled."""
     k, n, m = 2560, 6 * 4096 + 5, 1

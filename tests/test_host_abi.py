@@ -254,25 +254,30 @@ def test_create_without_a_device(lib):
 
 def test_gemv_geometry(lib):
     """Host-side launch planning of the streaming GEMV family (no device):
-    large launches of 40-lane rows pad their workgroups to 4 whole waves and
-    take four per compute unit; small ones pad their 5-wave workgroups to 8
-    waves (two per SIMD) and take two per compute unit."""
+    5-wave workgroups of 40-lane rows are padded to 8 waves (two per SIMD, two
+    per compute unit) where every compute unit stays busy; the direct kernel's
+    large launches pad to 4 waves instead and take four per compute unit."""
     geo = qb.qmv_gemv_geometry
     rc, g = geo(qb.QMV_FMT_Q6_K, 2560, 262144, 1, 256)  # vocabulary projection
     assert rc == qb.QMV_OK
-    assert g == dict(threads=256, slots=6, lanes=40, units_per_lane=1, rows_per_slot=1,
-                     tokens=1, per_cu=4, staged=1)
+    assert g == dict(threads=512, slots=12, lanes=40, units_per_lane=1, rows_per_slot=1,
+                     tokens=1, per_cu=2, staged=1)
     rc, g = geo(qb.QMV_FMT_Q4_K, 2560, 10240, 1, 256)  # k=2560 x 10240: a few batches each
     assert rc == qb.QMV_OK
     assert (g["threads"], g["slots"], g["lanes"], g["per_cu"]) == (512, 12, 40, 2)
-    rc, g = geo(qb.QMV_FMT_BF16, 2560, 262144, 1, 256)  # direct kernel, same padding
+    rc, g = geo(qb.QMV_FMT_BF16, 2560, 262144, 1, 256)  # direct kernel: 4-wave padding
     assert (g["threads"], g["slots"], g["per_cu"], g["staged"]) == (256, 6, 4, 0)
     rc, g = geo(qb.QMV_FMT_Q4_K, 4096, 14336, 2, 256)  # 64 lanes: already whole waves
     assert (g["threads"], g["slots"], g["lanes"], g["tokens"], g["per_cu"]) == (256, 4, 64, 2, 2)
-    # the padding threshold: at least 4 batches per workgroup at 4 per compute unit
-    assert geo(qb.QMV_FMT_Q6_K, 2560, 6 * 4096, 1, 256)[1]["threads"] == 256
-    assert geo(qb.QMV_FMT_Q6_K, 2560, 6 * 4096 - 6, 1, 256)[1]["threads"] == 512
-    assert geo(qb.QMV_FMT_Q6_K, 2560, 6 * 4096 + 5, 1, 256)[1]["threads"] == 256
+    # the direct kernel's 4-wave threshold: at least 4 batches per workgroup at
+    # 4 per compute unit
+    assert geo(qb.QMV_FMT_BF16, 2560, 6 * 4096, 1, 256)[1]["threads"] == 256
+    assert geo(qb.QMV_FMT_BF16, 2560, 6 * 4096 - 6, 1, 256)[1]["threads"] == 512
+    assert geo(qb.QMV_FMT_BF16, 2560, 6 * 4096 + 5, 1, 256)[1]["threads"] == 256
+    assert geo(qb.QMV_FMT_Q6_K, 2560, 6 * 4096 + 5, 1, 256)[1]["threads"] == 512
+    # 8-wave padding only where every compute unit stays busy
+    assert geo(qb.QMV_FMT_Q4_K, 2560, 4096, 1, 256)[1]["threads"] == 320
+    assert geo(qb.QMV_FMT_Q4_K, 2560, 2560, 1, 256)[1]["threads"] == 512
     # invariants over shapes
     for fmt in (qb.QMV_FMT_Q4_0, qb.QMV_FMT_Q4_K, qb.QMV_FMT_Q6_K, qb.QMV_FMT_BF16,
                 qb.QMV_FMT_Q8_0, qb.QMV_FMT_Q5_0):
