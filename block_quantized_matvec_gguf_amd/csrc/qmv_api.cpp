@@ -712,8 +712,10 @@ int qmv_run_moe_ex(int format, const void *W, const uint32_t *ids, const float *
     // planned over the launch's rows, all pairs together: planned per expert,
     // the rule that gives small products fewer row slots per workgroup cut a
     // 1536-row expert to 2-wave workgroups (Q4_K k=2048 x 1536, 8 experts:
-    // 10.8 -> 9.1 us; k=2560: 12.0 -> 8.8 us; outputs bit-identical)
-    const bool stream_ok = qmv::plan_gemv(format, k, n * pairs, 1, num_cu, &p);
+    // 10.8 -> 9.1 us; k=2560: 12.0 -> 8.8 us; outputs bit-identical); 32-lane
+    // rows (k=2048) that fill 4 waves exactly run 8 waves per workgroup, as
+    // wider rows do in every launch (Q4_K k=2048 x 1536, 8 experts: 9.3 -> 8.4 us)
+    const bool stream_ok = qmv::plan_gemv(format, k, n * pairs, 1, num_cu, &p, 32);
     if (algo == QMV_ALGO_GEMV && !stream_ok)
         return fail(QMV_ERR_UNSUPPORTED, "algo %d cannot serve %s with k=%lld", algo,
                     fmt_name(format), (long long)k);

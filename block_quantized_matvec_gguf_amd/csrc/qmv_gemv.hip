@@ -611,7 +611,8 @@ static bool staged_format(int fmt) {
 
 static constexpr size_t LDS_BUDGET = 80 * 1024; // weight buffers + reductions
 
-bool plan_gemv(int fmt, int64_t k, int64_t rows, int mt_max, int num_cu, GemvPlan *p) {
+bool plan_gemv(int fmt, int64_t k, int64_t rows, int mt_max, int num_cu, GemvPlan *p,
+               int pair_lanes) {
     if (k <= 0 || k % 64 != 0) return false;
     const int64_t U64 = k / 64;
     if (U64 > 1024) return false;
@@ -631,18 +632,44 @@ bool plan_gemv(int fmt, int64_t k, int64_t rows, int mt_max, int num_cu, GemvPla
     while (g.P > 1 && g.P * g.L > 64 && (rows + g.P - 1) / g.P < num_cu) g.P /= 2;
     g.T = g.P * g.L;
     g.per_cu = STREAM_PER_CU;
+    // Row slots that fill 4 waves exactly (64, 128 or 256 lanes per row: k =
+    // 4096, 8192, 16384): 8 waves of them where that leaves at least two
+    // batches per compute unit, which halves the batches, barriers and
+    // reductions per row and doubles the waves resident per compute unit.
+    // Measured (one token), 4 -> 8 waves: k=4096, 128256 rows: Q6_K 81.7 ->
+    // 67.1 us, Q4_K 70.6 -> 52.7, Q4_0 68.1 -> 51.5, Q5_0 80.9 -> 64.0, BF16
+    // 154 -> 152, Q8_0 unchanged (91.9); 14336 rows: Q4_K 12.9 -> 11.1, Q4_0
+    // 11.8 -> 10.8, BF16 21.5 -> 21.1; k=8192, 8192 rows: Q4_K 15.8 -> 12.5;
+    // 28672 rows: BF16 71.9 -> 68.5; 3072 rows: Q4_K 10.3 -> 9.6. Four 4-wave
+    // workgroups per compute unit instead: Q6_K 73 us, Q4_K k=8192 16.7.
+    // Narrower rows lose (k=2048 x 12288, Q4_K: 7.1 -> 7.9 us; k=1024 x 16384:
+    // 5.4 -> 6.4), except in the expert-indexed launch (k=2048, 8 x 1536
+    // rows: 9.3 -> 8.4 us), which passes pair_lanes = 32. The affine rows gain
+    // with 4-bit codes (k=4096 x 128256: 79.5 -> 65.0 us; x 14336: 13.1 ->
+    // 12.1) and lose with 8-bit ones (x 14336: 22.5 -> 23.6; k=8192 x 28672:
+    // 72.1 -> 75.4), which keep 4 waves.
+    if (g.T == 256 && g.L >= pair_lanes && fmt != FMT_AFFINE8 &&
+        (rows + 2 * g.P - 1) / (2 * g.P) >= 2 * (int64_t)num_cu) {
+        g.P *= 2;
+        g.T = 512;
+    }
     // The waves of a workgroup are dealt to the compute unit's four SIMDs in
     // turn, so a workgroup of 4w+1 waves puts two waves of every workgroup on
     // one SIMD, which then carries twice the decode work of the others, and
     // every batch's barrier waits for it. Where the row slots do not fill
     // whole groups of four waves (e.g. 40 lanes per row: 8 slots = 5 waves)
     // the workgroup is padded with idle lanes past the last slot, if that
-    // idles at most 1/8 of them: workgroups of 5-7 waves to 512 threads (8
-    // waves, two per SIMD, two workgroups per compute unit) where that keeps
-    // every compute unit busy (at least two batches per compute unit, or one
-    // round of workgroups where the unpadded slots needed two); the direct
-    // kernel's launches with at least 4 batches for each of 4 workgroups per
-    // compute unit to 256 threads instead (four per compute unit). Measured,
+    // idles at most 1/8 of them: workgroups of 5-7 waves (block formats: 3
+    // and 5-7) to 512 threads (8 waves, two per SIMD, two workgroups per
+    // compute unit) where that keeps every compute unit busy (at least two
+    // batches per compute unit, or one round of workgroups where the unpadded
+    // slots needed two); the direct kernel's launches with at least 4 batches
+    // for each of 4 workgroups per compute unit to 256 threads instead (four
+    // per compute unit). 3 waves to 8, measured: k=3072 (48 lanes) x 8192
+    // rows, Q4_K 8.8 -> 8.1 us, Q6_K 9.3 -> 8.9; x 128256 (from 4 waves, four
+    // per compute unit) Q4_K 43.5 -> 40.0, Q6_K 55.0 -> 52.4; k=6144 (96
+    // lanes) x 16384, Q4_K 23.9 -> 16.0; BF16 k=3072 x 8192 10.0 -> 11.1,
+    // hence the block formats only. Measured,
     // k=2560 (40 lanes): the vocabulary products (262144 rows) Q6_K 120 us
     // unpadded, 113 with 256, 89.7-90.0 against 92.3-92.5 us with 512 rather
     // than 256 (Q4_K 70.1 against 73.3-74.6; BF16 with 512: 8 tiles 3%
@@ -653,7 +680,8 @@ bool plan_gemv(int fmt, int64_t k, int64_t rows, int mt_max, int num_cu, GemvPla
         const int P4 = 256 / g.L, P8 = 512 / g.L;
         const bool many = P4 >= 1 && (256 - P4 * g.L) * 8 <= 256 &&
                           (rows + P4 - 1) / P4 >= 16 * (int64_t)num_cu;
-        bool pad8 = g.T > 256 && P8 >= 1 && (512 - P8 * g.L) * 8 <= 512;
+        bool pad8 = (g.T > 256 || (g.T > 128 && staged_format(fmt))) && P8 >= 1 &&
+                    (512 - P8 * g.L) * 8 <= 512;
         if (pad8) {
             const int64_t b8 = (rows + P8 - 1) / P8, bp = (rows + g.P - 1) / g.P;
             pad8 = b8 >= 2 * (int64_t)num_cu || (b8 <= num_cu && bp > num_cu);

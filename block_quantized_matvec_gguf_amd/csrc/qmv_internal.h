@@ -66,7 +66,10 @@ struct GemvTPlan {
 
 // Fill the geometry for a GEMV launch of up to mt_max tokens over `rows` rows.
 // Returns false when the shape is outside what the streaming kernel covers.
-bool plan_gemv(int fmt, int64_t k, int64_t rows, int mt_max, int num_cu, GemvPlan *p);
+// Row slots of at least pair_lanes lanes that fill 4 waves exactly are taken
+// 8 waves at a time where there are enough batches.
+bool plan_gemv(int fmt, int64_t k, int64_t rows, int mt_max, int num_cu, GemvPlan *p,
+               int pair_lanes = 64);
 
 hipError_t launch_gemv(const GemvPlan &p, const uint8_t *W, const float *x, float *y,
                        int64_t k, int64_t n, int64_t row_bytes, int64_t j_start,

@@ -295,7 +295,9 @@ const char *qmv_moe_kernel_name(int format, int64_t k, int algo);
  * bad format, shape, count or null out, or QMV_ERR_UNSUPPORTED when the
  * streaming kernels do not cover the shape (the per-row kernel then runs). An
  * expert-indexed launch (qmv_run_moe_ex) is planned with rows = n times the
- * number of (position, slot) pairs. */
+ * number of (position, slot) pairs, except that 4-wave workgroups of 32-lane
+ * rows (k = 2048) become 8-wave ones there on the terms that rows of 64 lanes
+ * and more meet here (at least two 8-wave batches per compute unit). */
 int qmv_gemv_geometry(int format, int64_t k, int64_t rows, int64_t m_tokens, int num_cu,
                       int64_t *out);
 

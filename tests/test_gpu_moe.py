@@ -145,7 +145,8 @@ def test_moe_bad_ids_and_shapes():
 
 def test_moe_decode_workload():
     """The measured expert-indexed decode shape: Q4_K, 64 experts of
-    k=2048 x n=1536, top_k=8, one position; every output against the oracle."""
+    k=2048 x n=1536, top_k=8, one position (8-wave workgroups of 16 row
+    slots of 32 lanes); every output against the oracle."""
     f, W, x, spec = synth.workload("q4_k_moe_decode")
     ids = synth.moe_ids(spec)
     check_moe(f, W, ids, x, spec["k"], spec["n"], spec["experts"], spec["top_k"])
@@ -184,6 +185,30 @@ def test_moe_eight_wave_workgroups(fmt):
     rng = np.random.default_rng(310 + fmt)
     W = synth.gen_weights(fmt, rng, n * E, k)
     ids = [2, 0, 1, 2]
+    x = synth.gen_x(rng, n_pos, k)
+    y, _ = check_moe(fmt, W, ids, x, k, n, E, top_k)
+    slab = qb.qmv_weight_bytes(fmt, k, n)
+    for r, e in enumerate(ids):
+        yr = dev(np.zeros((1, n), np.float32))
+        qb.matvec(fmt, dev(W[e * slab:(e + 1) * slab]), dev(x[r // top_k]), k, n, y=yr)
+        torch.cuda.synchronize()
+        assert np.array_equal(yr.cpu().numpy()[0].view(np.uint32), y[r].view(np.uint32)), r
+
+
+@pytest.mark.parametrize("fmt", [Q6_K, BF16], ids=lambda f: synth.FORMAT_NAMES[f])
+def test_moe_narrow_rows_eight_waves(fmt):
+    """Experts of k=2048 (32 lanes per row) x 2100 rows, 4 pairs: the
+    expert-indexed launch takes its whole 4-wave workgroups of 8 row slots
+    as 8-wave ones of 16 (a plain product of that many rows keeps 4 waves).
+    Against the oracle, and every row bit-equal to qmv_run on that expert's
+    matrix."""
+    k, n, E, n_pos, top_k = 2048, 2100, 4, 2, 2
+    rc, g = qb.qmv_gemv_geometry(fmt, k, n * n_pos * top_k, 1, 256)
+    assert rc == qb.QMV_OK and (g["threads"], g["slots"], g["lanes"]) == (256, 8, 32)
+    assert (n * n_pos * top_k + 15) // 16 >= 2 * 256
+    rng = np.random.default_rng(320 + fmt)
+    W = synth.gen_weights(fmt, rng, n * E, k)
+    ids = [3, 1, 0, 3]
     x = synth.gen_x(rng, n_pos, k)
     y, _ = check_moe(fmt, W, ids, x, k, n, E, top_k)
     slab = qb.qmv_weight_bytes(fmt, k, n)

@@ -330,6 +330,35 @@ def test_eight_wave_workgroups(fmt, k, n, m):
     check_case(fmt, k, n, m, algo="gemv", seed=k + n + m)
 
 
+@pytest.mark.parametrize("fmt,k,n,m,slots", [
+    (Q4_K, 4096, 4100, 2, 8), (Q6_K, 4096, 4100, 1, 8), (Q4_0, 4096, 4100, 3, 8),
+    (Q5_0, 4096, 4103, 1, 8), (Q8_0, 4096, 4100, 2, 8), (BF16, 4096, 4100, 2, 8),
+    (Q4_K, 8192, 2060, 1, 4), (F16, 8192, 2061, 3, 4), (Q6_K, 16384, 1030, 2, 2)],
+    ids=lambda v: str(v))
+def test_whole_wave_slots_taken_twice(fmt, k, n, m, slots):
+    """64, 128 and 256 lanes per row (k = 4096, 8192, 16384): row slots that
+    fill 4 waves exactly run 8 waves per workgroup once there are two
+    batches per compute unit; ragged last batch, one and several tokens,
+    every output against the oracle."""
+    rc, g = qb.qmv_gemv_geometry(fmt, k, n, min(m, 2), 256)
+    assert rc == qb.QMV_OK and (g["threads"], g["slots"]) == (512, slots)
+    check_case(fmt, k, n, m, algo="gemv", seed=k + n + m)
+
+
+@pytest.mark.parametrize("fmt,k,n,m,slots", [
+    (Q4_K, 3072, 5125, 1, 10), (Q6_K, 6144, 2561, 2, 5), (Q8_0, 3072, 5125, 2, 10),
+    (Q4_0, 3072, 2000, 3, 10), (Q5_0, 6144, 2600, 1, 5)], ids=lambda v: str(v))
+def test_three_wave_workgroups_padded(fmt, k, n, m, slots):
+    """48 and 96 lanes per row (k = 3072, 6144): the block formats' 3-wave
+    workgroups are padded to 8 waves (10 or 5 row slots + 32 idle lanes),
+    with two or more batches per compute unit, or in one round of workgroups
+    where the unpadded ones needed two (Q4_0 x 2000); every output against
+    the oracle."""
+    rc, g = qb.qmv_gemv_geometry(fmt, k, n, min(m, 2), 256)
+    assert rc == qb.QMV_OK and (g["threads"], g["slots"], g["lanes"]) == (512, slots, k // 64)
+    check_case(fmt, k, n, m, algo="gemv", seed=k + n + m)
+
+
 # ------------------------------------------------------- measured workloads
 
 @pytest.mark.parametrize("name", ["bf16_ffn_up", "f16_ffn_up", "q4_k_ffn_up", "q8_0_ffn_up",

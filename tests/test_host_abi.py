@@ -256,7 +256,8 @@ def test_gemv_geometry(lib):
     """Host-side launch planning of the streaming GEMV family (no device):
     5-wave workgroups of 40-lane rows are padded to 8 waves (two per SIMD, two
     per compute unit) where every compute unit stays busy; the direct kernel's
-    large launches pad to 4 waves instead and take four per compute unit."""
+    large launches pad to 4 waves instead and take four per compute unit; row
+    slots that fill 4 waves exactly take 8 from two batches per compute unit."""
     geo = qb.qmv_gemv_geometry
     rc, g = geo(qb.QMV_FMT_Q6_K, 2560, 262144, 1, 256)  # vocabulary projection
     assert rc == qb.QMV_OK
@@ -267,8 +268,15 @@ def test_gemv_geometry(lib):
     assert (g["threads"], g["slots"], g["lanes"], g["per_cu"]) == (512, 12, 40, 2)
     rc, g = geo(qb.QMV_FMT_BF16, 2560, 262144, 1, 256)  # direct kernel: 4-wave padding
     assert (g["threads"], g["slots"], g["per_cu"], g["staged"]) == (256, 6, 4, 0)
-    rc, g = geo(qb.QMV_FMT_Q4_K, 4096, 14336, 2, 256)  # 64 lanes: already whole waves
-    assert (g["threads"], g["slots"], g["lanes"], g["tokens"], g["per_cu"]) == (256, 4, 64, 2, 2)
+    rc, g = geo(qb.QMV_FMT_Q4_K, 4096, 14336, 2, 256)  # 64 lanes: 4 whole waves taken twice
+    assert (g["threads"], g["slots"], g["lanes"], g["tokens"], g["per_cu"]) == (512, 8, 64, 2, 2)
+    rc, g = geo(qb.QMV_FMT_BF16, 8192, 28672, 1, 256)  # direct kernel too
+    assert (g["threads"], g["slots"], g["lanes"], g["per_cu"], g["staged"]) == (512, 4, 128, 2, 0)
+    # 8 waves of whole-wave slots from two batches per compute unit on
+    assert geo(qb.QMV_FMT_Q4_K, 4096, 8 * 512, 1, 256)[1]["threads"] == 512
+    assert geo(qb.QMV_FMT_Q4_K, 4096, 8 * 511, 1, 256)[1]["threads"] == 256
+    assert geo(qb.QMV_FMT_Q4_K, 16384, 2 * 512, 1, 256)[1]["slots"] == 2
+    assert geo(qb.QMV_FMT_Q4_K, 16384, 2 * 511, 1, 256)[1]["slots"] == 1
     # the direct kernel's 4-wave threshold: at least 4 batches per workgroup at
     # 4 per compute unit
     assert geo(qb.QMV_FMT_BF16, 2560, 6 * 4096, 1, 256)[1]["threads"] == 256
