@@ -210,9 +210,16 @@ bool plan_gemv_t(int fmt, int64_t k, int64_t rows, int num_cu, GemvTPlan *out) {
     g.U = (int)U64;
     g.UPL = g.U <= 512 ? 1 : 2;
     g.L = (g.U + g.UPL - 1) / g.UPL;
-    // P row slots (a power of two), P*L <= 512 threads, aiming at 4+ waves
+    // P row slots (a power of two), P*L <= 512 threads, aiming at 4+ waves;
+    // 8 for the block formats' rows of 64+ lanes (k >= 4096), which halves
+    // the batches and barriers per row. Measured (one token, 4 -> 8 waves):
+    // k=4096 x 14336 Q4_K 23.5 -> 21.9 us, Q6_K 22.1 -> 20.8, Q8_0 27.2 ->
+    // 25.8, Q4_0 23.1 -> 22.0; k=8192 x 8192 Q4_K 29.4 -> 25.4; k=4096 x
+    // 128256 Q6_K 76.9-80.6 -> 76.7-77.1. F16/BF16 mixed (F16 k=8192 x 28672
+    // 80.9 -> 78.3, BF16 k=4096 x 14336 27.5 -> 28.4): 4 waves.
+    const bool wide8 = g.L >= 64 && fmt != FMT_F16 && fmt != FMT_BF16;
     g.P = 1;
-    while (g.P * 2 * g.L <= 512 && g.P * g.L < 256) g.P *= 2;
+    while (g.P * 2 * g.L <= 512 && g.P * g.L < (wide8 ? 512 : 256)) g.P *= 2;
     // small problems: fewer slots, so that more workgroups share the rows
     while (g.P > 1 && (rows + g.P - 1) / g.P < 2 * (int64_t)num_cu) g.P /= 2;
     // A batch of P rows spans P*rb bytes; when rows are not a whole number

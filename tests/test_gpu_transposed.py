@@ -79,6 +79,17 @@ def test_t_formats(fmt, k, n, m, algo):
     check_t(fmt, k, n, m, algo=algo, seed=k * 3 + n + m + fmt)
 
 
+@pytest.mark.parametrize("fmt,k,n,m", [
+    (Q4_K, 4096, 4100, 1), (Q6_K, 4096, 4103, 2), (Q8_0, 4096, 4100, 1), (Q4_0, 4096, 4100, 2),
+    (Q5_0, 4096, 4101, 1), (BF16, 4096, 4100, 1), (Q4_K, 8192, 2100, 2), (Q6_K, 16384, 1030, 1)],
+    ids=lambda v: str(v))
+def test_t_wide_rows(fmt, k, n, m):
+    """Rows of 64, 128 and 256 lanes (k = 4096, 8192, 16384) with enough rows
+    that the block formats run 8 row slots of 64 lanes (4 of 128, 2 of 256)
+    per workgroup; ragged last batch; every dx column against the oracle."""
+    check_t(fmt, k, n, m, algo="gemv", seed=k + n + m + fmt)
+
+
 @pytest.mark.parametrize("fmt", ALL_FORMATS, ids=lambda f: synth.FORMAT_NAMES[f])
 def test_t_range_and_accumulate(fmt):
     k, n, m = 1280 if fmt not in (Q4_K, Q6_K) else 1536, 900, 2
