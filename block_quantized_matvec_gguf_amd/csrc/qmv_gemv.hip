@@ -611,15 +611,15 @@ static bool staged_format(int fmt) {
 
 static constexpr size_t LDS_BUDGET = 80 * 1024; // weight buffers + reductions
 
-bool plan_gemv(int fmt, int64_t k, int64_t rows, int mt_max, int num_cu, GemvPlan *p,
-               int pair_lanes) {
+static bool plan_gemv_upl(int fmt, int64_t k, int64_t rows, int mt_max, int num_cu, GemvPlan *p,
+                          int pair_lanes, int upl) {
     if (k <= 0 || k % 64 != 0) return false;
     const int64_t U64 = k / 64;
     if (U64 > 1024) return false;
     GemvPlan g = {};
     g.fmt = fmt;
     g.U = (int)U64;
-    g.UPL = g.U <= 512 ? 1 : 2;
+    g.UPL = upl ? upl : g.U <= 512 ? 1 : 2;
     g.L = (g.U + g.UPL - 1) / g.UPL;
     g.G = g.L & -g.L;
     if (g.G > 16) g.G = 16;
@@ -770,6 +770,28 @@ bool plan_gemv(int fmt, int64_t k, int64_t rows, int mt_max, int num_cu, GemvPla
     if (g.lds_bytes > 160 * 1024) return false;
     *p = g;
     return true;
+}
+
+// Rows of 192+ units (k >= 12288) and many of them, one token, block formats:
+// two units per lane, which gives the 8-wave workgroup about 512/(U/2) row
+// slots, where that leaves at least 8 batches per workgroup at two per
+// compute unit and two workgroups' staging buffers fit a compute unit's LDS
+// (else one unit per lane). Measured (Q4_K, one token, same process): k=28672 x 8192 42.5 ->
+// 39.3 us, k=16384 x 53248 112.5 -> 92.9; with fewer batches it loses
+// (k=14336 x 4096 15.2 -> 22.0, k=12288 x 4096 21.2 -> 22.1, k=16384 x 4096
+// 15.5 -> 22.8).
+bool plan_gemv(int fmt, int64_t k, int64_t rows, int mt_max, int num_cu, GemvPlan *p,
+               int pair_lanes) {
+    const int64_t U = k / 64;
+    GemvPlan two;
+    if (k > 0 && k % 64 == 0 && U >= 192 && U <= 512 && mt_max == 1 && staged_format(fmt) &&
+        rows >= 16 * (int64_t)num_cu * (512 / ((U + 1) / 2)) &&
+        plan_gemv_upl(fmt, k, rows, mt_max, num_cu, &two, pair_lanes, 2) &&
+        two.lds_bytes <= LDS_BUDGET) {
+        *p = two;
+        return true;
+    }
+    return plan_gemv_upl(fmt, k, rows, mt_max, num_cu, p, pair_lanes, 0);
 }
 
 template <typename K>

@@ -346,6 +346,23 @@ def test_whole_wave_slots_taken_twice(fmt, k, n, m, slots):
 
 
 @pytest.mark.parametrize("fmt,k,n,m,slots", [
+    (Q4_K, 28672, 8200, 1, 2), (Q4_0, 28736, 8200, 1, 2), (Q4_K, 16384, 16400, 1, 4)],
+    ids=lambda v: str(v))
+def test_two_units_per_lane_wide_rows(fmt, k, n, m, slots):
+    """Rows of 192+ units with at least 8 batches per workgroup, one token:
+    every lane owns two units (Q4_0 k=28736: 449 units, so the last lane's
+    second unit is past the row and only re-read); every output against the
+    oracle, and the two-token launch of the same shape (one unit per lane)
+    within the same bound."""
+    rc, g = qb.qmv_gemv_geometry(fmt, k, n, 1, 256)
+    assert rc == qb.QMV_OK
+    assert (g["threads"], g["slots"], g["units_per_lane"]) == (512, slots, 2)
+    assert qb.qmv_gemv_geometry(fmt, k, n, 2, 256)[1]["units_per_lane"] == 1
+    check_case(fmt, k, n, m, algo="gemv", seed=k + n + m)
+    check_case(fmt, k, n, 2, algo="gemv", seed=k + n + 2)
+
+
+@pytest.mark.parametrize("fmt,k,n,m,slots", [
     (Q4_K, 3072, 5125, 1, 10), (Q6_K, 6144, 2561, 2, 5), (Q8_0, 3072, 5125, 2, 10),
     (Q4_0, 3072, 2000, 3, 10), (Q5_0, 6144, 2600, 1, 5)], ids=lambda v: str(v))
 def test_three_wave_workgroups_padded(fmt, k, n, m, slots):

@@ -277,6 +277,15 @@ def test_gemv_geometry(lib):
     assert geo(qb.QMV_FMT_Q4_K, 4096, 8 * 511, 1, 256)[1]["threads"] == 256
     assert geo(qb.QMV_FMT_Q4_K, 16384, 2 * 512, 1, 256)[1]["slots"] == 2
     assert geo(qb.QMV_FMT_Q4_K, 16384, 2 * 511, 1, 256)[1]["slots"] == 1
+    # two units per lane: rows of 192+ units, one token, 8+ batches per workgroup
+    assert geo(qb.QMV_FMT_Q4_K, 28672, 8192, 1, 256)[1]["units_per_lane"] == 2
+    assert geo(qb.QMV_FMT_Q4_K, 28672, 8191, 1, 256)[1]["units_per_lane"] == 1
+    assert geo(qb.QMV_FMT_Q4_K, 28672, 8192, 2, 256)[1]["units_per_lane"] == 1
+    assert geo(qb.QMV_FMT_BF16, 28672, 8192, 1, 256)[1]["units_per_lane"] == 1
+    assert geo(qb.QMV_FMT_Q4_K, 14336, 4096, 1, 256)[1]["units_per_lane"] == 1
+    # ... and only where two workgroups' staging buffers fit a compute unit
+    assert geo(qb.QMV_FMT_Q6_K, 16384, 262144, 1, 256)[1]["units_per_lane"] == 1
+    assert geo(qb.QMV_FMT_Q4_K, 16384, 262144, 1, 256)[1]["units_per_lane"] == 2
     # the direct kernel's 4-wave threshold: at least 4 batches per workgroup at
     # 4 per compute unit
     assert geo(qb.QMV_FMT_BF16, 2560, 6 * 4096, 1, 256)[1]["threads"] == 256
