@@ -669,7 +669,11 @@ static bool plan_gemv_upl(int fmt, int64_t k, int64_t rows, int mt_max, int num_
     // rows, Q4_K 8.8 -> 8.1 us, Q6_K 9.3 -> 8.9; x 128256 (from 4 waves, four
     // per compute unit) Q4_K 43.5 -> 40.0, Q6_K 55.0 -> 52.4; k=6144 (96
     // lanes) x 16384, Q4_K 23.9 -> 16.0; BF16 k=3072 x 8192 10.0 -> 11.1,
-    // hence the block formats only. Measured,
+    // hence the block formats only. There up to a quarter of the lanes may
+    // idle: k=12288 (192 lanes, one slot of 3 waves -> two slots in 8 waves)
+    // x 4096 rows Q4_K 21.5 -> 14.8 us, Q6_K 22.1 -> 15.6, Q8_0 22.8 -> 14.9,
+    // Q4_0 21.1 -> 14.5; x 16384 Q4_K 49.9 -> 32.1, Q6_K 53.2 -> 43.4; x 1024
+    // Q4_K 13.0 -> 10.1 (4 waves, 64 idle lanes, instead: 5-16% faster). Measured,
     // k=2560 (40 lanes): the vocabulary products (262144 rows) Q6_K 120 us
     // unpadded, 113 with 256, 89.7-90.0 against 92.3-92.5 us with 512 rather
     // than 256 (Q4_K 70.1 against 73.3-74.6; BF16 with 512: 8 tiles 3%
@@ -680,8 +684,10 @@ static bool plan_gemv_upl(int fmt, int64_t k, int64_t rows, int mt_max, int num_
         const int P4 = 256 / g.L, P8 = 512 / g.L;
         const bool many = P4 >= 1 && (256 - P4 * g.L) * 8 <= 256 &&
                           (rows + P4 - 1) / P4 >= 16 * (int64_t)num_cu;
-        bool pad8 = (g.T > 256 || (g.T > 128 && staged_format(fmt))) && P8 >= 1 &&
-                    (512 - P8 * g.L) * 8 <= 512;
+        // block formats' 3-wave workgroups: up to a quarter of the lanes idle
+        const bool three = g.T <= 256 && staged_format(fmt);
+        bool pad8 = (g.T > 256 || (g.T > 128 && three)) && P8 >= 1 &&
+                    (512 - P8 * g.L) * (three ? 4 : 8) <= 512;
         if (pad8) {
             const int64_t b8 = (rows + P8 - 1) / P8, bp = (rows + g.P - 1) / g.P;
             pad8 = b8 >= 2 * (int64_t)num_cu || (b8 <= num_cu && bp > num_cu);

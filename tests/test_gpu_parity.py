@@ -364,10 +364,12 @@ def test_two_units_per_lane_wide_rows(fmt, k, n, m, slots):
 
 @pytest.mark.parametrize("fmt,k,n,m,slots", [
     (Q4_K, 3072, 5125, 1, 10), (Q6_K, 6144, 2561, 2, 5), (Q8_0, 3072, 5125, 2, 10),
-    (Q4_0, 3072, 2000, 3, 10), (Q5_0, 6144, 2600, 1, 5)], ids=lambda v: str(v))
+    (Q4_0, 3072, 2000, 3, 10), (Q5_0, 6144, 2600, 1, 5), (Q4_K, 12288, 1030, 2, 2),
+    (Q8_0, 12288, 4100, 1, 2), (Q6_K, 12288, 1031, 3, 2)], ids=lambda v: str(v))
 def test_three_wave_workgroups_padded(fmt, k, n, m, slots):
-    """48 and 96 lanes per row (k = 3072, 6144): the block formats' 3-wave
-    workgroups are padded to 8 waves (10 or 5 row slots + 32 idle lanes),
+    """48, 96 and 192 lanes per row (k = 3072, 6144, 12288): the block
+    formats' 3-wave workgroups are padded to 8 waves (10, 5 or 2 row slots +
+    32, 32 or 128 idle lanes),
     with two or more batches per compute unit, or in one round of workgroups
     where the unpadded ones needed two (Q4_0 x 2000); every output against
     the oracle."""

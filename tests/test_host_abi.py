@@ -277,6 +277,10 @@ def test_gemv_geometry(lib):
     assert geo(qb.QMV_FMT_Q4_K, 4096, 8 * 511, 1, 256)[1]["threads"] == 256
     assert geo(qb.QMV_FMT_Q4_K, 16384, 2 * 512, 1, 256)[1]["slots"] == 2
     assert geo(qb.QMV_FMT_Q4_K, 16384, 2 * 511, 1, 256)[1]["slots"] == 1
+    # 3-wave workgroups of 192-lane rows: two slots in 8 waves (a quarter idle)
+    rc, g = geo(qb.QMV_FMT_Q4_K, 12288, 4096, 1, 256)
+    assert (g["threads"], g["slots"], g["lanes"], g["units_per_lane"]) == (512, 2, 192, 1)
+    assert geo(qb.QMV_FMT_BF16, 12288, 4096, 1, 256)[1]["threads"] == 192
     # two units per lane: rows of 192+ units, one token, 8+ batches per workgroup
     assert geo(qb.QMV_FMT_Q4_K, 28672, 8192, 1, 256)[1]["units_per_lane"] == 2
     assert geo(qb.QMV_FMT_Q4_K, 28672, 8191, 1, 256)[1]["units_per_lane"] == 1
@@ -298,7 +302,7 @@ def test_gemv_geometry(lib):
     # invariants over shapes
     for fmt in (qb.QMV_FMT_Q4_0, qb.QMV_FMT_Q4_K, qb.QMV_FMT_Q6_K, qb.QMV_FMT_BF16,
                 qb.QMV_FMT_Q8_0, qb.QMV_FMT_Q5_0):
-        for k in (256, 1024, 2304, 2560, 4096, 8192, 16384):
+        for k in (256, 1024, 2304, 2560, 3072, 4096, 6144, 8192, 12288, 16384, 28672):
             for rows in (1, 7, 300, 10240, 262144):
                 for m in (1, 2):
                     rc, g = geo(fmt, k, rows, m, 256)
@@ -309,12 +313,17 @@ def test_gemv_geometry(lib):
                     if g["per_cu"] == 4:
                         assert g["threads"] == 256 and (256 - busy) * 8 <= 256
                     elif g["threads"] == 512 and busy < 512:
-                        # 5-7 waves of row slots padded to 8 whole waves
-                        assert g["per_cu"] == 2 and (512 - busy) * 8 <= 512 and busy > 256
+                        # 5-7 waves of row slots padded to 8 whole waves (block
+                        # formats: also 3 waves, up to a quarter of the lanes idle)
+                        idle_cap = 4 if g["staged"] else 8
+                        assert g["per_cu"] == 2 and (512 - busy) * idle_cap <= 512 and busy > 256
                     else:
                         assert g["per_cu"] == 2 and g["threads"] == busy
-                    # whole waves, or one partial wave of a workgroup below 256 threads
-                    assert g["threads"] % 256 == 0 or g["threads"] <= 256
+                    # whole groups of 4 waves, or a workgroup below 256 threads, or
+                    # one row slot of more than 256 lanes (k=28672 with one unit
+                    # per lane: 448 threads)
+                    assert (g["threads"] % 256 == 0 or g["threads"] <= 256 or
+                            (g["slots"] == 1 and g["lanes"] > 256))
     # shapes the streaming kernels do not take, and bad arguments
     assert geo(qb.QMV_FMT_F16, 96, 10, 1, 256)[0] == qb.QMV_ERR_UNSUPPORTED
     assert geo(qb.QMV_FMT_Q4_K, 2560, 0, 1, 256)[0] == qb.QMV_ERR_INVALID_ARGUMENT
