@@ -673,7 +673,11 @@ static bool plan_gemv_upl(int fmt, int64_t k, int64_t rows, int mt_max, int num_
     // idle: k=12288 (192 lanes, one slot of 3 waves -> two slots in 8 waves)
     // x 4096 rows Q4_K 21.5 -> 14.8 us, Q6_K 22.1 -> 15.6, Q8_0 22.8 -> 14.9,
     // Q4_0 21.1 -> 14.5; x 16384 Q4_K 49.9 -> 32.1, Q6_K 53.2 -> 43.4; x 1024
-    // Q4_K 13.0 -> 10.1 (4 waves, 64 idle lanes, instead: 5-16% faster). Measured,
+    // Q4_K 13.0 -> 10.1 (4 waves, 64 idle lanes, instead: 5-16% faster); and
+    // 5-7-wave ones with more than an eighth idle: k=13824 (216 lanes, 2 slots)
+    // x 5120 Q4_K 20.6 -> 19.3-20.0, Q4_0 19.8 -> 18.9, Q6_K 22.2 -> 21.7, Q8_0
+    // 24.6 -> 25.2; x 1024 Q4_K 12.2 -> 11.3; k=9216 x 4096 12.0 -> 11.2;
+    // k=13312 x 4096 16.5 -> 15.0. Measured,
     // k=2560 (40 lanes): the vocabulary products (262144 rows) Q6_K 120 us
     // unpadded, 113 with 256, 89.7-90.0 against 92.3-92.5 us with 512 rather
     // than 256 (Q4_K 70.1 against 73.3-74.6; BF16 with 512: 8 tiles 3%
@@ -684,10 +688,10 @@ static bool plan_gemv_upl(int fmt, int64_t k, int64_t rows, int mt_max, int num_
         const int P4 = 256 / g.L, P8 = 512 / g.L;
         const bool many = P4 >= 1 && (256 - P4 * g.L) * 8 <= 256 &&
                           (rows + P4 - 1) / P4 >= 16 * (int64_t)num_cu;
-        // block formats' 3-wave workgroups: up to a quarter of the lanes idle
-        const bool three = g.T <= 256 && staged_format(fmt);
-        bool pad8 = (g.T > 256 || (g.T > 128 && three)) && P8 >= 1 &&
-                    (512 - P8 * g.L) * (three ? 4 : 8) <= 512;
+        // block formats: up to a quarter of the lanes idle
+        const bool blk = staged_format(fmt);
+        bool pad8 = (g.T > 256 || (g.T > 128 && blk)) && P8 >= 1 &&
+                    (512 - P8 * g.L) * (blk ? 4 : 8) <= 512;
         if (pad8) {
             const int64_t b8 = (rows + P8 - 1) / P8, bp = (rows + g.P - 1) / g.P;
             pad8 = b8 >= 2 * (int64_t)num_cu || (b8 <= num_cu && bp > num_cu);

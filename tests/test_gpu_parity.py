@@ -378,6 +378,18 @@ def test_three_wave_workgroups_padded(fmt, k, n, m, slots):
     check_case(fmt, k, n, m, algo="gemv", seed=k + n + m)
 
 
+
+@pytest.mark.parametrize("fmt,k,n,m,slots", [
+    (Q4_K, 13824, 1030, 2, 2), (Q4_0, 9216, 1540, 1, 3), (Q6_K, 13312, 1031, 3, 2),
+    (Q8_0, 13824, 1030, 1, 2)], ids=lambda v: str(v))
+def test_wide_slots_padded_quarter_idle(fmt, k, n, m, slots):
+    """5-7-wave workgroups of wide rows (216, 144, 208 lanes: k = 13824, 9216,
+    13312) padded to 8 waves with up to a quarter of the lanes idle (block
+    formats); every output against the oracle."""
+    rc, g = qb.qmv_gemv_geometry(fmt, k, n, min(m, 2), 256)
+    assert rc == qb.QMV_OK and (g["threads"], g["slots"], g["lanes"]) == (512, slots, k // 64)
+    check_case(fmt, k, n, m, algo="gemv", seed=k + n + m)
+
 # ------------------------------------------------------- measured workloads
 
 @pytest.mark.parametrize("name", ["bf16_ffn_up", "f16_ffn_up", "q4_k_ffn_up", "q8_0_ffn_up",
